@@ -1,0 +1,59 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins
+catch every one (no GPU).  Each mutant is a textual edit of oracle.c built
+into a temporary library; the original is never modified."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "scale dropped from the scores": ("z[i] = scale * dot;", "z[i] = dot;"),
+    "GQA head mapped round-robin": ("int32_t kvh = h / group;", "int32_t kvh = h % num_kv_heads;"),
+    "offset in block taken from the block index": (
+        "block_size + i % block_size;\n    double sk", "block_size + i / block_size;\n    double sk"),
+    "softmax not normalised": ("double w = z[i] / total;", "double w = z[i];"),
+    "binary16 exponent bias off by one": ("expo - 25);", "expo - 24);"),
+    "binary16 subnormal scale wrong": ("ldexp((double)frac, -24);", "ldexp((double)frac, -23);"),
+    "bfloat16 shifted wrong": ("(uint32_t)b << 16;", "(uint32_t)b << 15;"),
+    "int8 key scale dropped": ("row * head_dim + d) * sk;", "row * head_dim + d);"),
+    "newest token excluded from attention": (
+        "oracle_attention_dense(qv, K, V, ctx,", "oracle_attention_dense(qv, K, V, ctx - 1,"),
+    "decode slot offset from block index": (
+        "slots[s] = (int64_t)block * block_size + pos % block_size;",
+        "slots[s] = (int64_t)block * block_size + pos / block_size;"),
+    "append block/offset swapped": (
+        "int64_t block = slots[t] / block_size, off = slots[t] % block_size;\n    for (int32_t h = 0; h < num_kv_heads; ++h) {\n      size_t src = ((size_t)t * num_kv_heads + h) * row;",
+        "int64_t block = slots[t] % block_size, off = slots[t] / block_size;\n    for (int32_t h = 0; h < num_kv_heads; ++h) {\n      size_t src = ((size_t)t * num_kv_heads + h) * row;"),
+    "quantizer truncates": ("float c = rintf(r);", "float c = truncf(r);"),
+    "quantizer range 128": ("volatile float ratio = a / 127.0f;", "volatile float ratio = a / 128.0f;"),
+    "values mixed from keys": ("out[d] += w * V[i * head_dim + d];", "out[d] += w * K[i * head_dim + d];"),
+    "running minimum instead of maximum": ("if (z[i] > m) m = z[i];", "if (z[i] < m) m = z[i];"),
+    "gather offset from block index": (
+        "block_size + i % block_size;\n        size_t dst_row", "block_size + i / block_size;\n        size_t dst_row"),
+    "binary16 rounding truncates": ("double n = nearbyint(a / quantum);", "double n = floor(a / quantum);"),
+    "dot product over half the head": (
+        "for (int32_t d = 0; d < head_dim; ++d) dot += q[d] * K[i * head_dim + d];",
+        "for (int32_t d = 0; d < head_dim / 2; ++d) dot += q[d] * K[i * head_dim + d];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation site not found exactly once: {old!r}"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.build(output=lib_path, source=str(path))
+    lib = oracle.load(lib_path)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, oracle.OracleError, ValueError, IndexError) as e:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant '{name}'"
