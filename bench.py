@@ -1,0 +1,268 @@
+"""Benchmark: decode steps of paged KV-cache attention on one MI355X.
+
+Default workload (the headline): Llama-2-7B layer shape, fp16, multi-head
+(32 query / 32 KV heads, head_dim 128), 16 sequences x 4096 cached
+positions, block size 16, all 32 layers' pools resident (32 GiB).  One step
+= the decode slots of the batch, then for every layer in order: append the
+new token's K/V rows, partitioned paged attention and the log-sum-exp merge.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.  value = logical KV bytes read per step / step time
+(GB/s); the roofline block times the dominant kernel (the partitioned
+attention) with HIP events around each of its launches inside the timed
+region; cpu_baseline times the CPU oracle on the host cores over a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import decode_attention_paged_append_amd as pa  # noqa: E402
+import workloads as W  # noqa: E402
+
+METRIC = ("decode-attention KV-read GB/s (% of HBM peak) + seq-steps/s, "
+          "Llama-2-7B 16×4096")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+KERNEL_SOURCES = ["decode_attention_paged_append_amd/csrc/decode_kernel.h",
+                  "decode_attention_paged_append_amd/csrc/device.h",
+                  "decode_attention_paged_append_amd/csrc/decode_dispatch.h",
+                  "decode_attention_paged_append_amd/csrc/api.cpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+class Bench:
+    """All layers' inputs resident on the GPU, and the step that runs them."""
+
+    def __init__(self, shape: W.Shape, layers: int, dev):
+        self.shape, self.layers, self.dev = shape, layers, dev
+        self.layout = W.layout_for(shape)
+        lay = self.layout
+        self.bt = lay.block_tables.to(dev)
+        self.ctx = lay.context_lens.to(dev)
+        self.int8 = shape.cache_dtype == "i8"
+        self.append = shape.name != W.LLAMA2_70B.name   # shared-prefix blocks are not appended
+        self.cases = []
+        for layer in range(layers):
+            c = W.make_case(shape, lay, device=dev, seed=layer, poison=False)
+            if self.int8:
+                c = self._quantize(c)
+            self.cases.append(c)
+        s, hq, d = shape.num_seqs, shape.num_q_heads, shape.head_dim
+        desc = pa.CacheDesc(lay.num_blocks, shape.num_kv_heads, shape.block_size, d,
+                            pa.DTYPE_CODE[W.TORCH_DTYPE[shape.cache_dtype]])
+        self.part = pa.decode_partition_tokens(desc, s, hq, lay.max_blocks)
+        self.nparts = -(-lay.max_blocks * shape.block_size // self.part)
+        nbytes = pa.decode_workspace_bytes(desc, s, hq, lay.max_blocks, self.part)
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        self.outs = [torch.empty_like(c.q) for c in self.cases]
+        self.slots = torch.empty(s, dtype=torch.int64, device=dev)
+
+    def _quantize(self, c):
+        nb, hkv, bs, d = c.k_cache.shape
+        rows = lambda x: x.permute(0, 2, 1, 3).reshape(nb * bs, hkv, d).contiguous()
+        slots = torch.arange(nb * bs, dtype=torch.int64, device=self.dev)
+        kq = torch.empty((nb, hkv, bs, d), dtype=torch.int8, device=self.dev)
+        vq = torch.empty_like(kq)
+        ks = torch.empty((nb, hkv, bs), dtype=torch.float16, device=self.dev)
+        vs = torch.empty_like(ks)
+        pa.kv_append_int8(rows(c.k_cache), rows(c.v_cache), slots, kq, vq, ks, vs)
+        torch.cuda.synchronize()
+        c.k_cache, c.v_cache = kq, vq
+        c.k_scale, c.v_scale = ks, vs
+        return c
+
+    def step(self, events=None):
+        """One decode step over every layer; events: list of (start, end) pairs
+        recorded around each layer's partitioned-attention launch."""
+        sh = self.shape
+        if self.append:
+            pa.decode_slot_mapping(self.bt, self.ctx, sh.block_size, out=self.slots)
+        for layer, c in enumerate(self.cases):
+            ks = getattr(c, "k_scale", None)
+            vs = getattr(c, "v_scale", None)
+            if self.append:
+                if self.int8:
+                    pa.kv_append_int8(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache, ks, vs)
+                else:
+                    pa.kv_append(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache)
+            if events is not None:
+                events[layer][0].record()
+            pa.decode_partitions(c.q, c.k_cache, c.v_cache, self.bt, self.ctx, sh.scale,
+                                 self.outs[layer], self.part, self.ws, ks, vs)
+            if events is not None:
+                events[layer][1].record()
+            if self.nparts > 1:
+                pa.lse_merge(self.ws, self.ctx, sh.num_q_heads, sh.head_dim,
+                             self.layout.max_blocks, sh.block_size, self.part, self.outs[layer])
+
+    def kv_bytes_per_layer(self) -> int:
+        return W.kv_bytes_per_layer_step(self.shape, self.layout.context_lens.tolist())
+
+    def io_bytes_per_layer(self) -> int:
+        """Algorithmic bytes of one layer's attention: cached K/V (+ scales),
+        q and out, and the block-table entries read."""
+        sh = self.shape
+        qo = 2 * sh.num_seqs * sh.num_q_heads * sh.head_dim * W.ELEM_BYTES[sh.q_dtype]
+        tables = sum(W.blocks_needed(int(c), sh.block_size) for c in self.layout.context_lens) * 4
+        return self.kv_bytes_per_layer() + qo + tables
+
+
+def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
+    """The CPU oracle, as it stands, over layer 0 of the same workload."""
+    import oracle
+
+    c = b.cases[0]
+    lay = b.layout
+    host = W.to_numpy_bits
+    args = dict(k_scale=host(c.k_scale) if b.int8 else None,
+                v_scale=host(c.v_scale) if b.int8 else None,
+                bf16=b.shape.cache_dtype == "bf16")
+    q, kc, vc = host(c.q), host(c.k_cache), host(c.v_cache)
+    bt, ctx = host(lay.block_tables), host(lay.context_lens)
+    threads = oracle.max_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.paged_decode_attention(q, kc, vc, bt, ctx, b.shape.scale, num_threads=threads, **args)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(b.kv_bytes_per_layer() * reps / dt / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"layer 0 of {b.layers}: all {b.shape.num_seqs} seqs x "
+                      f"{b.shape.num_q_heads} heads, fp64 oracle run {reps} time(s) in "
+                      f"{dt:.1f} s on {threads} threads"}
+
+
+def traffic_block(io_bytes: int):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
+    on the current kernel sources (else null)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=W.LLAMA2_7B.name, choices=sorted(W.SHAPES))
+    ap.add_argument("--layers", type=int, default=0, help="0: the workload's own layer count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-kernel", type=int, default=0,
+                    help="only run N copies of a 1 GiB tensor (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+
+    if args.copy_kernel:
+        src = torch.ones(1 << 29, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.copy_kernel):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 2, "copies": args.copy_kernel}))
+        return
+
+    shape = W.SHAPES[args.workload]
+    layers = args.layers or shape.layers
+    b = Bench(shape, layers, dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        b.step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+              for _ in range(layers * args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        b.step(events[k * layers:(k + 1) * layers])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    kernel_ms = sum(e0.elapsed_time(e1) for e0, e1 in events) / len(events)
+
+    kv_step = b.kv_bytes_per_layer() * layers
+    value = kv_step / (ms_step / 1e3) / 1e9
+    io = b.io_bytes_per_layer()
+    achieved = io / (kernel_ms / 1e3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.cache_dtype,
+        "data": "synthetic: seeded N(0,1) Q/K/V at the layer shape; block tables a seeded "
+                "permutation of the pool",
+        "config": {
+            "workload": f"{shape.name}: {shape.description}; step = "
+                        + ("slots + per layer (append, paged attention, merge)" if b.append
+                           else "per layer (paged attention, merge)"),
+            "num_seqs": shape.num_seqs, "context_lens_sum": int(b.layout.context_lens.sum()),
+            "layers": layers, "num_q_heads": shape.num_q_heads,
+            "num_kv_heads": shape.num_kv_heads, "head_dim": shape.head_dim,
+            "block_size": shape.block_size, "partition_tokens": b.part,
+            "partitions": b.nparts,
+        },
+        "seq_steps_per_s": round(shape.num_seqs * 1e3 / ms_step, 2),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kv_bytes_per_step": kv_step,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_partition_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_block(io),
+            "bytes_per_launch": io,
+            "avg_launch_ms": round(kernel_ms, 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

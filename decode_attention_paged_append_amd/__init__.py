@@ -1,0 +1,294 @@
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+Python binding of ``libpagedattn.so`` (the C ABI in ``include/pagedattn.h``).
+Each function here carries the C entry point's name without its ``pa_``
+prefix and only marshals arguments: it checks that torch tensors are on the
+GPU, contiguous and of the right type, then passes their device pointers and
+torch's current HIP stream to the library.  Every step of the computation
+runs in the library's HIP kernels; there is no CPU fallback -- importing
+works without the library, but any call raises if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "PagedAttnError", "library", "CacheDesc", "slot_mapping", "decode_slot_mapping",
+    "kv_append", "kv_append_int8", "decode_workspace_bytes", "decode_partition_tokens",
+    "paged_decode_attention", "paged_decode_attention_int8", "decode_partitions", "lse_merge",
+    "gather_kv", "abi_version",
+]
+
+LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int8: 3}
+CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
+
+
+class PagedAttnError(RuntimeError):
+    """A non-OK status from the library."""
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, k_cache: torch.Tensor) -> "CacheDesc":
+        nb, hkv, bs, d = k_cache.shape
+        return cls(nb, hkv, bs, d, DTYPE_CODE[k_cache.dtype])
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY_PATH):
+            raise PagedAttnError(
+                f"{LIBRARY_PATH} is missing: build it with "
+                "`python -m decode_attention_paged_append_amd.build`")
+        _lib = _declare(ctypes.CDLL(LIBRARY_PATH))
+    return _lib
+
+
+def _declare(lib):
+    P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    D = ctypes.POINTER(CacheDesc)
+    sig = {
+        "pa_slot_mapping": [P, i32, i32, P, P, i64, i32, P, P],
+        "pa_decode_slot_mapping": [P, i32, P, i32, i32, P, P],
+        "pa_kv_append": [P, P, P, i64, P, P, D, P],
+        "pa_kv_append_int8": [P, P, P, i64, P, P, P, P, D, P],
+        "pa_paged_decode_attention": [P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
+        "pa_paged_decode_attention_int8": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
+        "pa_decode_partitions": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D, P, sz, P],
+        "pa_lse_merge": [P, sz, P, i32, i32, i32, i32, i32, i32, i32, P, P],
+        "pa_gather_kv": [P, P, P, P, P, i32, P, i32, P, P, P, P, D, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.pa_decode_workspace_bytes.argtypes = [D, i32, i32, i32, i32]
+    lib.pa_decode_workspace_bytes.restype = sz
+    lib.pa_decode_partition_tokens.argtypes = [D, i32, i32, i32]
+    lib.pa_decode_partition_tokens.restype = i32
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_abi_version.restype = i32
+    return lib
+
+
+def _ok(status: int, lib) -> None:
+    if status != 0:
+        raise PagedAttnError(f"{lib.pa_status_string(status).decode()}: "
+                             f"{lib.pa_last_error().decode()}")
+
+
+def _dev(t: torch.Tensor | None, name: str, dtype=None, ndim=None):
+    """Device pointer of a contiguous GPU tensor (None stays NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def abi_version() -> int:
+    return library().pa_abi_version()
+
+
+# ---------------------------------------------------------------- slots
+
+def slot_mapping(block_tables, token_seq, token_pos, block_size, out=None):
+    """int64 slot of each (sequence, position) pair; see pa_slot_mapping."""
+    lib = library()
+    n = token_seq.numel()
+    out = torch.empty(n, dtype=torch.int64, device=block_tables.device) if out is None else out
+    _ok(lib.pa_slot_mapping(_dev(block_tables, "block_tables", torch.int32, 2),
+                            block_tables.shape[1], block_tables.shape[0],
+                            _dev(token_seq, "token_seq", torch.int32),
+                            _dev(token_pos, "token_pos", torch.int32), n, block_size,
+                            _dev(out, "slot_mapping", torch.int64), _stream(block_tables)), lib)
+    return out
+
+
+def decode_slot_mapping(block_tables, context_lens, block_size, out=None):
+    """Slot of each sequence's newest position context_lens[s]-1 (-1 if empty)."""
+    lib = library()
+    s = context_lens.numel()
+    out = torch.empty(s, dtype=torch.int64, device=block_tables.device) if out is None else out
+    _ok(lib.pa_decode_slot_mapping(_dev(block_tables, "block_tables", torch.int32, 2),
+                                   block_tables.shape[1],
+                                   _dev(context_lens, "context_lens", torch.int32), s, block_size,
+                                   _dev(out, "slot_mapping", torch.int64),
+                                   _stream(block_tables)), lib)
+    return out
+
+
+# ---------------------------------------------------------------- append
+
+def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache):
+    """Scatter k_new/v_new [T, Hkv, D] into the [NB, Hkv, BS, D] pools."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    t = slot_mapping.numel()
+    if k_new.shape != (t, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{t}, {desc.num_kv_heads}, {desc.head_dim}]")
+    _ok(lib.pa_kv_append(_dev(k_new, "k_new", k_cache.dtype), _dev(v_new, "v_new", k_cache.dtype),
+                         _dev(slot_mapping, "slot_mapping", torch.int64), t,
+                         _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+                         ctypes.byref(desc), _stream(k_cache)), lib)
+
+
+def kv_append_int8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale):
+    """Quantize fp16 rows [T, Hkv, D] and store codes + fp16 scales."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    t = slot_mapping.numel()
+    if k_new.shape != (t, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{t}, {desc.num_kv_heads}, {desc.head_dim}]")
+    if k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_scale.shape:
+        raise ValueError("scales must be [NB, Hkv, BS]")
+    _ok(lib.pa_kv_append_int8(_dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),
+                              _dev(slot_mapping, "slot_mapping", torch.int64), t,
+                              _dev(k_cache, "k_cache", torch.int8, 4),
+                              _dev(v_cache, "v_cache", torch.int8, 4),
+                              _dev(k_scale, "k_scale", torch.float16),
+                              _dev(v_scale, "v_scale", torch.float16), ctypes.byref(desc),
+                              _stream(k_cache)), lib)
+
+
+# ---------------------------------------------------------------- attention
+
+def decode_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks, partition_tokens=0) -> int:
+    desc = k_cache if isinstance(k_cache, CacheDesc) else CacheDesc.of(k_cache)
+    return int(library().pa_decode_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
+                                                   max_blocks, partition_tokens))
+
+
+def decode_partition_tokens(k_cache, num_seqs, num_q_heads, max_blocks) -> int:
+    desc = k_cache if isinstance(k_cache, CacheDesc) else CacheDesc.of(k_cache)
+    return int(library().pa_decode_partition_tokens(ctypes.byref(desc), num_seqs, num_q_heads,
+                                                    max_blocks))
+
+
+def _workspace(ws, nbytes, device):
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return ws
+
+
+def _shapes(q, k_cache, block_tables, context_lens, out):
+    s, hq, d = q.shape
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.numel() != s:
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    if k_cache.shape[3] != d:
+        raise ValueError("head_dim of q and cache differ")
+    return s, hq, block_tables.shape[1]
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                           workspace=None):
+    """out[s,h] = softmax(q[s,h] . K_s^T * scale) . V_s over the paged cache."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    need = decode_workspace_bytes(desc, s, hq, maxb)
+    ws = _workspace(workspace, need, q.device)
+    _ok(lib.pa_paged_decode_attention(
+        _dev(q, "q", k_cache.dtype, 3), _dev(k_cache, "k_cache", ndim=4),
+        _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(block_tables, "block_tables", torch.int32),
+        maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
+        _dev(out, "out", k_cache.dtype), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _stream(q)), lib)
+    return out
+
+
+def paged_decode_attention_int8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                context_lens, scale, out, workspace=None):
+    """Decode attention over an int8 cache with fp16 per-(token, head) scales."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    need = decode_workspace_bytes(desc, s, hq, maxb)
+    ws = _workspace(workspace, need, q.device)
+    _ok(lib.pa_paged_decode_attention_int8(
+        _dev(q, "q", torch.float16, 3), _dev(k_cache, "k_cache", torch.int8, 4),
+        _dev(v_cache, "v_cache", torch.int8, 4), _dev(k_scale, "k_scale", torch.float16),
+        _dev(v_scale, "v_scale", torch.float16), _dev(block_tables, "block_tables", torch.int32),
+        maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
+        _dev(out, "out", torch.float16), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _stream(q)), lib)
+    return out
+
+
+def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                      partition_tokens, workspace, k_scale=None, v_scale=None):
+    """Phase 1 with an explicit partition length (see pa_decode_partitions)."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    q_dtype = torch.float16 if k_cache.dtype == torch.int8 else k_cache.dtype
+    _ok(lib.pa_decode_partitions(
+        _dev(q, "q", q_dtype, 3), _dev(k_cache, "k_cache", ndim=4),
+        _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(k_scale, "k_scale", torch.float16),
+        _dev(v_scale, "v_scale", torch.float16), _dev(block_tables, "block_tables", torch.int32),
+        maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
+        int(partition_tokens), _dev(out, "out", q_dtype), ctypes.byref(desc),
+        _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel(), _stream(q)),
+        lib)
+    return out
+
+
+def lse_merge(workspace, context_lens, num_q_heads, head_dim, max_blocks, block_size,
+              partition_tokens, out):
+    """Phase 2: merge the partials phase 1 left in the workspace into out."""
+    lib = library()
+    _ok(lib.pa_lse_merge(_dev(workspace, "workspace"), workspace.numel(),
+                         _dev(context_lens, "context_lens", torch.int32), context_lens.numel(),
+                         num_q_heads, head_dim, max_blocks, block_size, int(partition_tokens),
+                         DTYPE_CODE[out.dtype], _dev(out, "out"), _stream(out)), lib)
+    return out
+
+
+# ---------------------------------------------------------------- gather
+
+def gather_kv(k_cache, v_cache, block_tables, context_lens, k_out, v_out, k_scale=None,
+              v_scale=None, k_scale_out=None, v_scale_out=None):
+    """Un-page to dense [S, max_blocks*BS, Hkv, D]; rows past a length untouched."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    s, maxb = block_tables.shape
+    want = (s, maxb * desc.block_size, desc.num_kv_heads, desc.head_dim)
+    if tuple(k_out.shape) != want or tuple(v_out.shape) != want:
+        raise ValueError(f"k_out/v_out must be {want}")
+    _ok(lib.pa_gather_kv(_dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", k_cache.dtype, 4),
+                         _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+                         _dev(block_tables, "block_tables", torch.int32), maxb,
+                         _dev(context_lens, "context_lens", torch.int32), s,
+                         _dev(k_out, "k_out", k_cache.dtype), _dev(v_out, "v_out", k_cache.dtype),
+                         _dev(k_scale_out, "k_scale_out"), _dev(v_scale_out, "v_scale_out"),
+                         ctypes.byref(desc), _stream(k_cache)), lib)

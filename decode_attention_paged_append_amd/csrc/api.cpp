@@ -1,0 +1,404 @@
+// api.cpp -- the C ABI of libpagedattn.so: argument checks, the decode plan
+// and kernel dispatch.  Declarations and their contracts: include/pagedattn.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "pagedattn.h"
+#include "decode_dispatch.h"
+#include "kv_ops.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    case PA_I8: return 1;
+    default: return 0;
+  }
+}
+
+bool supported_block(int32_t bs) { return bs == 4 || bs == 8 || bs == 16 || bs == 32; }
+bool supported_dim(int32_t d) { return d == 64 || d == 128; }
+
+pa_status check_cache(const pa_cache_desc* c) {
+  if (!c) return fail(PA_ERR_INVALID_ARG, "cache descriptor is NULL");
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_dim <= 0)
+    return fail(PA_ERR_INVALID_ARG, "cache sizes must be positive (blocks %d, kv heads %d, block %d, dim %d)",
+                c->num_blocks, c->num_kv_heads, c->block_size, c->head_dim);
+  if (!elem_bytes(c->dtype)) return fail(PA_ERR_UNSUPPORTED, "unknown cache dtype %d", c->dtype);
+  if (!supported_dim(c->head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
+  if (!supported_block(c->block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (4, 8, 16 or 32)", c->block_size);
+  if ((int64_t)c->num_blocks * c->block_size > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "pool of %d blocks x %d slots exceeds 2^31 slots",
+                c->num_blocks, c->block_size);
+  return PA_OK;
+}
+
+// ------------------------------------------------------------------ plan
+
+constexpr int32_t kTargetWorkgroups = 2048;  // ~8 resident per CU on 256 CUs
+constexpr int32_t kMinPartitionTokens = 256;
+
+struct Plan {
+  int32_t gc = 1;         // query heads per workgroup
+  int32_t chunks = 1;     // workgroups per KV head (group / gc)
+  int32_t tile = 0;       // positions per tile
+  int32_t part_tokens = 0;
+  int32_t num_parts = 0;
+  size_t ml_bytes = 0;    // workspace: partial (max, sum)
+  size_t o_offset = 0;    // workspace: offset of the partial outputs
+  size_t ws_bytes = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+void size_workspace(Plan& p, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
+  if (p.num_parts <= 1) {
+    p.ml_bytes = p.o_offset = p.ws_bytes = 0;
+    return;
+  }
+  const size_t rows = (size_t)num_seqs * num_q_heads * p.num_parts;
+  p.ml_bytes = rows * 2 * sizeof(float);
+  p.o_offset = align256(p.ml_bytes);
+  p.ws_bytes = p.o_offset + rows * head_dim * sizeof(float);
+}
+
+pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t max_blocks, int32_t requested, Plan* out) {
+  pa_status st = check_cache(c);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                num_q_heads, c->num_kv_heads);
+  if (max_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d <= 0", max_blocks);
+  if ((int64_t)max_blocks * c->block_size > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "block table width x block size exceeds 2^31 positions");
+  if (requested < 0) return fail(PA_ERR_INVALID_ARG, "partition_tokens %d < 0", requested);
+  Plan p;
+  const int32_t group = num_q_heads / c->num_kv_heads;
+  p.gc = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+  p.chunks = group / p.gc;
+  p.tile = pa::tile_tokens(elem_bytes(c->dtype), c->head_dim, c->block_size);
+  const int64_t max_tok = (int64_t)max_blocks * c->block_size;
+  int64_t part;
+  if (requested > 0) {
+    if (requested % p.tile != 0)
+      return fail(PA_ERR_INVALID_ARG,
+                  "partition_tokens %d must be a multiple of the tile length %d", requested, p.tile);
+    part = requested;
+  } else {
+    // Enough workgroups to fill the chip, each wave owning whole tiles.
+    const int64_t unit = (int64_t)p.tile * pa::kDecodeWaves;
+    const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads * p.chunks;
+    const int64_t want_parts = (kTargetWorkgroups + units - 1) / units;
+    part = (max_tok + want_parts - 1) / want_parts;
+    part = std::max<int64_t>(part, kMinPartitionTokens);
+    part = (part + unit - 1) / unit * unit;
+  }
+  if (part >= max_tok) part = (max_tok + p.tile - 1) / p.tile * p.tile;
+  p.part_tokens = (int32_t)std::min<int64_t>(part, INT32_MAX / 2);
+  p.num_parts = (int32_t)((max_tok + p.part_tokens - 1) / p.part_tokens);
+  if (num_seqs > 65535 || (int64_t)c->num_kv_heads * p.chunks > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "grid too large (%d sequences, %d KV heads x %d chunks)",
+                num_seqs, c->num_kv_heads, p.chunks);
+  size_workspace(p, num_seqs, num_q_heads, c->head_dim);
+  *out = p;
+  return PA_OK;
+}
+
+pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache,
+                         const void* k_scale, const void* v_scale, const int32_t* block_tables,
+                         int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, float scale, void* out, const pa_cache_desc* cache,
+                         const Plan& plan, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(PA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (cache->dtype == PA_I8 && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARG, "int8 cache needs k_scale and v_scale");
+  if (plan.num_parts > 1 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes,
+                plan.ws_bytes);
+  pa::DecodeParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = (const uint16_t*)k_scale;
+  p.v_scale = (const uint16_t*)v_scale;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.part_ml = plan.num_parts > 1 ? (float*)workspace : nullptr;
+  p.part_o = plan.num_parts > 1 ? (float*)((char*)workspace + plan.o_offset) : nullptr;
+  p.max_blocks = max_blocks;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_blocks = cache->num_blocks;
+  p.group = num_q_heads / cache->num_kv_heads;
+  p.head_chunks = plan.chunks;
+  p.part_tokens = plan.part_tokens;
+  p.num_parts = plan.num_parts;
+  p.scale_log2 = scale * pa::kLog2e;
+  hipError_t e;
+  switch (cache->dtype) {
+    case PA_F32: e = pa::launch_decode_f32(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
+    case PA_F16: e = pa::launch_decode_f16(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
+    case PA_BF16: e = pa::launch_decode_bf16(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
+    case PA_I8: e = pa::launch_decode_i8(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
+    default: return fail(PA_ERR_UNSUPPORTED, "dtype %d", cache->dtype);
+  }
+  return hip_status(e, "decode partitions launch");
+}
+
+pa_status run_merge(const Plan& plan, const void* workspace, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_tokens,
+                    int32_t out_dtype, void* out, hipStream_t stream) {
+  const hipError_t e = pa::launch_lse_merge(
+      (const float*)workspace, (const float*)((const char*)workspace + plan.o_offset),
+      context_lens, num_seqs, num_q_heads, head_dim, max_tokens, plan.part_tokens,
+      plan.num_parts, out_dtype, out, stream);
+  return hip_status(e, "lse merge launch");
+}
+
+pa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
+                        const void* k_scale, const void* v_scale, const int32_t* block_tables,
+                        int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t num_q_heads, float scale, void* out, const pa_cache_desc* cache,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        bool want_int8) {
+  Plan plan;
+  pa_status st = make_plan(cache, num_seqs, num_q_heads, max_blocks, 0, &plan);
+  if (st != PA_OK) return st;
+  if ((cache->dtype == PA_I8) != want_int8)
+    return fail(PA_ERR_UNSUPPORTED, want_int8 ? "int8 entry point needs an int8 cache"
+                                              : "int8 cache: use pa_paged_decode_attention_int8");
+  if (num_seqs == 0) return PA_OK;
+  st = run_partitions(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks,
+                      context_lens, num_seqs, num_q_heads, scale, out, cache, plan, workspace,
+                      workspace_bytes, stream);
+  if (st != PA_OK || plan.num_parts == 1) return st;
+  const int32_t out_dtype = cache->dtype == PA_I8 ? PA_F16 : cache->dtype;
+  return run_merge(plan, workspace, context_lens, num_seqs, num_q_heads, cache->head_dim,
+                   max_blocks * cache->block_size, out_dtype, out, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t num_seqs, const int32_t* token_seq, const int32_t* token_pos,
+                          int64_t num_tokens, int32_t block_size, int64_t* slot_mapping,
+                          pa_stream_t stream) {
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative sizes or empty table");
+  if (!supported_block(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported", block_size);
+  if (num_tokens == 0) return PA_OK;
+  if (!block_tables || !token_seq || !token_pos || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  return hip_status(pa::launch_slot_mapping(block_tables, max_blocks_per_seq, num_seqs, token_seq,
+                                            token_pos, num_tokens, block_size, slot_mapping,
+                                            (hipStream_t)stream),
+                    "slot mapping launch");
+}
+
+pa_status pa_decode_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t block_size, int64_t* slot_mapping, pa_stream_t stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative sizes or empty table");
+  if (!supported_block(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported", block_size);
+  if (num_seqs == 0) return PA_OK;
+  if (!block_tables || !context_lens || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  return hip_status(pa::launch_decode_slot_mapping(block_tables, max_blocks_per_seq, context_lens,
+                                                   num_seqs, block_size, slot_mapping,
+                                                   (hipStream_t)stream),
+                    "decode slot mapping launch");
+}
+
+pa_status pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                       int64_t num_tokens, void* k_cache, void* v_cache,
+                       const pa_cache_desc* cache, pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (cache->dtype == PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "int8 cache: use pa_kv_append_int8");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  const int32_t row_bytes = cache->head_dim * elem_bytes(cache->dtype);
+  return hip_status(pa::launch_kv_append(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache,
+                                         cache->num_kv_heads, cache->block_size, row_bytes,
+                                         (int64_t)cache->num_blocks * cache->block_size,
+                                         (hipStream_t)stream),
+                    "kv_append launch");
+}
+
+pa_status pa_kv_append_int8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                            int64_t num_tokens, int8_t* k_cache, int8_t* v_cache, void* k_scale,
+                            void* v_scale, const pa_cache_desc* cache, pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (cache->dtype != PA_I8) return fail(PA_ERR_UNSUPPORTED, "pa_kv_append_int8 needs an int8 cache");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  return hip_status(pa::launch_kv_append_int8(k_new, v_new, slot_mapping, num_tokens, k_cache,
+                                              v_cache, k_scale, v_scale, cache->num_kv_heads,
+                                              cache->block_size, cache->head_dim,
+                                              (int64_t)cache->num_blocks * cache->block_size,
+                                              (hipStream_t)stream),
+                    "kv_append_int8 launch");
+}
+
+size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                 int32_t partition_tokens) {
+  Plan plan;
+  if (make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan) != PA_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+int32_t pa_decode_partition_tokens(const pa_cache_desc* cache, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_blocks_per_seq) {
+  Plan plan;
+  if (make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, &plan) != PA_OK) return 0;
+  return plan.part_tokens;
+}
+
+pa_status pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, float scale, void* out,
+                                    const pa_cache_desc* cache, void* workspace,
+                                    size_t workspace_bytes, pa_stream_t stream) {
+  return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
+                       workspace_bytes, (hipStream_t)stream, false);
+}
+
+pa_status pa_paged_decode_attention_int8(const void* q, const int8_t* k_cache,
+                                         const int8_t* v_cache, const void* k_scale,
+                                         const void* v_scale, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, float scale, void* out,
+                                         const pa_cache_desc* cache, void* workspace,
+                                         size_t workspace_bytes, pa_stream_t stream) {
+  return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
+                       workspace_bytes, (hipStream_t)stream, true);
+}
+
+pa_status pa_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
+                               const void* k_scale, const void* v_scale,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, float scale, int32_t partition_tokens,
+                               void* out, const pa_cache_desc* cache, void* workspace,
+                               size_t workspace_bytes, pa_stream_t stream) {
+  Plan plan;
+  pa_status st = make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  return run_partitions(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                        context_lens, num_seqs, num_q_heads, scale, out, cache, plan, workspace,
+                        workspace_bytes, (hipStream_t)stream);
+}
+
+pa_status pa_lse_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                       int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_tokens,
+                       int32_t out_dtype, void* out, pa_stream_t stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_tokens <= 0)
+    return fail(PA_ERR_INVALID_ARG, "bad sizes");
+  if (!supported_dim(head_dim)) return fail(PA_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  if (!supported_block(block_size)) return fail(PA_ERR_UNSUPPORTED, "block_size %d", block_size);
+  if (out_dtype != PA_F32 && out_dtype != PA_F16 && out_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "block table width x block size exceeds 2^31 positions");
+  Plan plan;
+  plan.part_tokens = partition_tokens;
+  const int64_t max_tok = (int64_t)max_blocks_per_seq * block_size;
+  plan.num_parts = (int32_t)((max_tok + partition_tokens - 1) / partition_tokens);
+  if (plan.num_parts <= 1)
+    return fail(PA_ERR_INVALID_ARG, "a single partition is final already; nothing to merge");
+  size_workspace(plan, num_seqs, num_q_heads, head_dim);
+  if (num_seqs == 0) return PA_OK;
+  if (!workspace || !context_lens || !out) return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  if (workspace_bytes < plan.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, plan.ws_bytes);
+  return run_merge(plan, workspace, context_lens, num_seqs, num_q_heads, head_dim, (int32_t)max_tok,
+                   out_dtype, out, (hipStream_t)stream);
+}
+
+pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_scale,
+                       const void* v_scale, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                       void* k_out, void* v_out, void* k_scale_out, void* v_scale_out,
+                       const pa_cache_desc* cache, pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "bad sizes");
+  if (num_seqs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !k_out || !v_out)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  const int32_t row_bytes = cache->head_dim * elem_bytes(cache->dtype);
+  const bool i8 = cache->dtype == PA_I8;
+  return hip_status(pa::launch_gather_kv(k_cache, v_cache, i8 ? k_scale : nullptr,
+                                         i8 ? v_scale : nullptr, block_tables, max_blocks_per_seq,
+                                         context_lens, num_seqs, k_out, v_out,
+                                         i8 ? k_scale_out : nullptr, i8 ? v_scale_out : nullptr,
+                                         cache->num_blocks, cache->num_kv_heads,
+                                         cache->block_size, row_bytes, (hipStream_t)stream),
+                    "gather launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// decode_dispatch.h -- runtime (head_dim, block size, head chunk) -> template
+// instance of the decode kernel for one cache format (internal header).
+#pragma once
+
+#include "decode_kernel.h"
+
+namespace pa {
+
+template <Fmt F, int D, int BS, int GC>
+static hipError_t launch_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
+  const dim3 grid((unsigned)p.num_parts, (unsigned)(p.num_kv_heads * p.head_chunks),
+                  (unsigned)num_seqs);
+  hipLaunchKernelGGL((decode_partition_kernel<F, D, BS, GC, kDecodeWaves>), grid,
+                     dim3(kDecodeWaves * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <Fmt F, int D, int BS>
+static hipError_t launch_gc(const DecodeParams& p, int gc, int num_seqs, hipStream_t stream) {
+  switch (gc) {
+    case 1: return launch_one<F, D, BS, 1>(p, num_seqs, stream);
+    case 2: return launch_one<F, D, BS, 2>(p, num_seqs, stream);
+    case 4: return launch_one<F, D, BS, 4>(p, num_seqs, stream);
+    case 8: return launch_one<F, D, BS, 8>(p, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <Fmt F, int D>
+static hipError_t launch_bs(const DecodeParams& p, int bs, int gc, int num_seqs,
+                            hipStream_t stream) {
+  switch (bs) {
+    case 4: return launch_gc<F, D, 4>(p, gc, num_seqs, stream);
+    case 8: return launch_gc<F, D, 8>(p, gc, num_seqs, stream);
+    case 16: return launch_gc<F, D, 16>(p, gc, num_seqs, stream);
+    case 32: return launch_gc<F, D, 32>(p, gc, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <Fmt F>
+static hipError_t launch_fmt(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                             hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_bs<F, 64>(p, bs, gc, num_seqs, stream);
+    case 128: return launch_bs<F, 128>(p, bs, gc, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_f32(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                             hipStream_t stream);
+hipError_t launch_decode_f16(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                             hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                              hipStream_t stream);
+hipError_t launch_decode_i8(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                            hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,403 @@
+// decode_kernel.h -- partitioned paged decode attention (phase 1) for gfx950.
+//
+// Computes, for one sequence s, one KV head and the GC query heads of a
+// grouped-query group that read it, the attention of each head's query over
+// one partition of the sequence's cached rows:
+//   z_i = scale * q . k_i,   p_i = exp(z_i - m),   l = sum p_i,   o = sum p_i v_i
+// ("KV cache: the engine behind fast LLM inference", "Concept" and step 3 of
+// "What happens at each decoding step").  Rows are reached through the
+// sequence's block table ("PagedAttention: the cache in blocks" on the
+// KV-cache visualization page).  The softmax runs online, tile by tile, in
+// registers: the score row never goes to memory (the guide's "Flash
+// attention: don't build the giant matrix").
+//
+// Work decomposition (wave64, one workgroup = NW waves):
+//   grid = (partition, KV head x head chunk, sequence).
+//   A tile is TT consecutive positions: one whole block when the block holds
+//   at least one wave-load of rows, else several blocks.  Wave w of the
+//   workgroup takes tiles w, w+NW, ... of the partition.
+//   Each lane loads 16 contiguous bytes per fragment, so one wave-load is
+//   1 KiB of consecutive bytes: LR lanes cover one row (head_dim values) and
+//   the wave covers RPI = 64/LR rows.  K and V tiles of a block are
+//   contiguous (BS x D elements per KV head), so every load is fully
+//   coalesced and the whole tile is in flight at once.
+//   The K row read by a lane is dotted with all GC queries from registers,
+//   so a GQA group reads its KV head once; partial dots are summed across
+//   the LR lanes of a row with DPP moves.
+//   Every lane keeps its own running (max, sum, output slice) for the rows
+//   it sees -- no cross-row traffic inside the loop.  Row groups are merged
+//   at the end with shuffles, waves through LDS, and the workgroup writes
+//   either the final normalized output (single partition) or its partial
+//   (max, sum, unnormalized output) for the log-sum-exp merge.
+#pragma once
+
+#include <type_traits>
+
+#include "device.h"
+
+namespace pa {
+
+struct DecodeParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const uint16_t* k_scale;  // int8 cache only: fp16 [NB][Hkv][BS]
+  const uint16_t* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;                // final output (single partition)
+  float* part_ml;           // [S][Hq][P][2]: running max (log2 units), sum
+  float* part_o;            // [S][Hq][P][D]: unnormalized output
+  int32_t max_blocks;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t group;            // Hq / Hkv
+  int32_t head_chunks;      // group / GC
+  int32_t part_tokens;      // multiple of the tile length
+  int32_t num_parts;
+  float scale_log2;         // scale * log2(e): scores are kept in log2 units
+};
+
+// Per-format fragment arithmetic.  A fragment is 16 bytes of cache data.
+template <Fmt F> struct Frag;
+
+template <> struct Frag<Fmt::F32> {
+  static constexpr int VE = 4;  // elements per fragment
+  static constexpr int QW = 4;  // 32-bit words of query per fragment
+  __device__ static __forceinline__ float dot(const uint32_t* q, u32x4 k) {
+    float s = bits_to_float(q[0]) * bits_to_float(k[0]);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) s = fmaf(bits_to_float(q[i]), bits_to_float(k[i]), s);
+    return s;
+  }
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = bits_to_float(v[i]);
+  }
+};
+
+template <> struct Frag<Fmt::F16> {
+  static constexpr int VE = 8;
+  static constexpr int QW = 4;
+  __device__ static __forceinline__ float dot(const uint32_t* q, u32x4 k) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_fdot2(as_h2(q[i]), as_h2(k[i]), s, false);
+    return s;
+  }
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = f16_lo(v[i]);
+      f[2 * i + 1] = f16_hi(v[i]);
+    }
+  }
+};
+
+template <> struct Frag<Fmt::BF16> {
+  static constexpr int VE = 8;
+  static constexpr int QW = 4;
+  __device__ static __forceinline__ float dot(const uint32_t* q, u32x4 k) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(q[i]), as_bf2(k[i]), s, false);
+    return s;
+  }
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(v[i]);
+      f[2 * i + 1] = bf16_hi(v[i]);
+    }
+  }
+};
+
+// int8 codes: 16 per fragment, dotted with 16 fp16 query values.  Codes are
+// turned into binary16 exactly: byte b = code + 128 placed under the exponent
+// pattern 0x64 is the half 1024 + b; subtracting 1152 leaves the code.
+template <> struct Frag<Fmt::I8> {
+  static constexpr int VE = 16;
+  static constexpr int QW = 8;
+  __device__ static __forceinline__ void codes_to_half2(uint32_t w, h16x2& lo, h16x2& hi) {
+    const uint32_t u = w ^ 0x80808080u;
+    const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+    const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+    const h16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    lo = as_h2(a) - bias;
+    hi = as_h2(b) - bias;
+  }
+  __device__ static __forceinline__ float dot(const uint32_t* q, u32x4 k) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h16x2 lo, hi;
+      codes_to_half2(k[i], lo, hi);
+      s = __builtin_amdgcn_fdot2(as_h2(q[2 * i]), lo, s, false);
+      s = __builtin_amdgcn_fdot2(as_h2(q[2 * i + 1]), hi, s, false);
+    }
+    return s;
+  }
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * i + b] = (float)(int8_t)(v[i] >> (8 * b));
+    }
+  }
+};
+
+template <Fmt F>
+__device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
+  if constexpr (F == Fmt::F32) {
+    ((float*)out)[idx] = x;
+  } else if constexpr (F == Fmt::BF16) {
+    ((uint16_t*)out)[idx] = float_to_bf16_rne(x);
+  } else {  // fp16 output (also for the int8 cache)
+    ((uint16_t*)out)[idx] = float_to_f16_rne(x);
+  }
+}
+
+template <Fmt F, int D, int BS, int GC, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(const DecodeParams p) {
+  using FR = Frag<F>;
+  constexpr int CB = FmtInfo<F>::bytes;       // bytes per cache element
+  constexpr int QB = FmtInfo<F>::q_bytes;     // bytes per query element
+  constexpr int VE = FR::VE;                  // elements per 16-byte fragment
+  constexpr int LR = D / VE;                  // lanes per row
+  constexpr int RPI = kWave / LR;             // rows per wave-load
+  constexpr int TT = BS > RPI ? BS : RPI;     // positions per tile
+  constexpr int NJ = TT / RPI;                // fragments per lane per tile (K, and V)
+  constexpr int BPT = TT / BS;                // blocks per tile
+  constexpr int ROWB = D * CB;                // bytes per cached row
+  constexpr bool kInt8 = F == Fmt::I8;
+  static_assert(LR >= 1 && LR <= kWave && (kWave % LR) == 0, "row must split over lanes");
+  static_assert(TT % RPI == 0 && TT % BS == 0, "tile must be whole loads and blocks");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y / p.head_chunks;
+  const int chunk = blockIdx.y - kvh * p.head_chunks;
+  const int s = blockIdx.z;
+  const int h0 = kvh * p.group + chunk * GC;
+  const size_t out_row0 = (size_t)s * p.num_q_heads + h0;
+
+  const int ctx = p.context_lens[s];
+  const bool single = p.num_parts == 1;
+  const int tok0 = part * p.part_tokens;
+  const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
+  if (bad_ctx || tok0 >= ctx) {
+    // Nothing to attend in this partition.  The merge skips it; a single
+    // pass writes the final rows: NaN for a broken length, zeros for ctx 0.
+    if (single) {
+      const float fill = bad_ctx ? __builtin_nanf("") : 0.0f;
+      for (int i = threadIdx.x; i < GC * D; i += NW * kWave)
+        store_out<F>(p.out, out_row0 * D + i, fill);
+    }
+    return;
+  }
+  const int tok_end = min(ctx, tok0 + p.part_tokens);
+  const int ntiles = (tok_end - tok0 + TT - 1) / TT;
+  const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
+
+  const int lrow = lane / LR;  // row of this lane inside a wave-load
+  const int lcol = lane % LR;  // 16-byte column of this lane inside a row
+
+  // Query slices this lane multiplies: elements [lcol*VE, lcol*VE+VE).
+  uint32_t qf[GC][FR::QW];
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    const uint32_t* qp = (const uint32_t*)((const char*)p.q +
+                                           ((out_row0 + g) * D + (size_t)lcol * VE) * QB);
+#pragma unroll
+    for (int w = 0; w < FR::QW; ++w) qf[g][w] = qp[w];
+  }
+
+  float m[GC], l[GC], acc[GC][VE];
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    m[g] = kMaxInit;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
+  }
+  bool bad_block = false;
+
+  const char* __restrict__ kbase = (const char*)p.k_cache;
+  const char* __restrict__ vbase = (const char*)p.v_cache;
+  // Block ids of the partition, 64 at a time in one coalesced load: lane i
+  // holds the id of block ids_base + i (counted from the partition's first
+  // block); a tile then reads its ids with v_readlane, without a memory trip.
+  const int blk0 = tok0 / BS;
+  const int nblk = (tok_end + BS - 1) / BS - blk0;
+  int ids = 0;
+  int ids_base = -kWave;
+  auto tile = [&](const int t, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    const int ttok = tok0 + t * TT;
+    const int nvalid = tok_end - ttok;  // rows of the tile inside the partition
+    const int lb = t * BPT;             // first block of the tile
+    if (lb >= ids_base + kWave) {       // a wave's tiles come in increasing order
+      ids_base = lb & ~(kWave - 1);
+      const int bi = ids_base + lane;
+      ids = bi < nblk ? table[blk0 + bi] : 0;
+    }
+    int phys[BPT];
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      const int id = __builtin_amdgcn_readlane(ids, lb - ids_base + b);
+      const bool ok = (unsigned)id < (unsigned)p.num_blocks;
+      bad_block |= !ok;
+      phys[b] = ok ? id : 0;
+    }
+    u32x4 kf[NJ], vf[NJ];
+    float ks[NJ], vs[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = j * RPI + lrow;  // row inside the tile
+      int pid = phys[0];
+#pragma unroll
+      for (int b = 1; b < BPT; ++b) pid = (r / BS == b) ? phys[b] : pid;
+      const size_t row = ((size_t)pid * p.num_kv_heads + kvh) * BS + (BPT == 1 ? r : r % BS);
+      const size_t off = row * ROWB + (size_t)lcol * 16;
+      const bool valid = !PARTIAL || r < nvalid;
+      if (valid) {
+        kf[j] = load16(kbase + off);
+        vf[j] = load16(vbase + off);
+      } else {
+        kf[j] = u32x4{0, 0, 0, 0};
+        vf[j] = u32x4{0, 0, 0, 0};
+      }
+      if constexpr (kInt8) {
+        ks[j] = valid ? (float)__builtin_bit_cast(_Float16, p.k_scale[row]) : 0.0f;
+        vs[j] = valid ? (float)__builtin_bit_cast(_Float16, p.v_scale[row]) : 0.0f;
+      } else {
+        ks[j] = 1.0f;
+        vs[j] = 1.0f;
+      }
+    }
+    // Keep every K and V load of the tile ahead of the arithmetic, so that
+    // the whole tile is in flight at once (one memory round trip per tile).
+    __builtin_amdgcn_sched_barrier(0);
+    // Scores of every (head, fragment row), summed across the row's lanes.
+    float z[GC][NJ];
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const float d = group_sum<LR>(FR::dot(qf[g], kf[j]));
+        z[g][j] = kInt8 ? d * (ks[j] * p.scale_log2) : d * p.scale_log2;
+        if (PARTIAL && j * RPI + lrow >= nvalid) z[g][j] = -__builtin_inff();
+      }
+    }
+    float vv[NJ][VE];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) FR::unpack(vf[j], vv[j]);
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      float mt = z[g][0];
+#pragma unroll
+      for (int j = 1; j < NJ; ++j) mt = fmaxf(mt, z[g][j]);
+      const float mn = fmaxf(m[g], mt);
+      const float alpha = fast_exp2(m[g] - mn);
+      m[g] = mn;
+      float lsum = l[g] * alpha;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const float pj = fast_exp2(z[g][j] - mn);
+        lsum += pj;
+        const float pv = kInt8 ? pj * vs[j] : pj;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pv, vv[j][e], acc[g][e]);
+      }
+      l[g] = lsum;
+    }
+  };
+
+  const int nfull = (tok_end - tok0) / TT;  // tiles with every row valid
+  for (int t = wave; t < ntiles; t += NW) {
+    if (t < nfull) tile(t, std::false_type{});
+    else tile(t, std::true_type{});
+  }
+
+  // Merge the row groups of the wave (lanes lcol, lcol+LR, ...).
+#pragma unroll
+  for (int off = LR; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      const float mo = __shfl_xor(m[g], off);
+      const float lo = __shfl_xor(l[g], off);
+      const float mn = fmaxf(m[g], mo);
+      const float a = fast_exp2(m[g] - mn);
+      const float b = fast_exp2(mo - mn);
+      l[g] = l[g] * a + lo * b;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const float ao = __shfl_xor(acc[g][e], off);
+        acc[g][e] = acc[g][e] * a + ao * b;
+      }
+      m[g] = mn;
+    }
+  }
+
+  // Merge the waves through LDS and write the result.
+  __shared__ float s_ml[NW][GC][2];
+  __shared__ float s_acc[NW][GC][D];
+  if (lane < LR) {
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s_acc[wave][g][lcol * VE + e] = acc[g][e];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      s_ml[wave][g][0] = m[g];
+      s_ml[wave][g][1] = l[g];
+    }
+  }
+  const bool bad = __syncthreads_or(bad_block ? 1 : 0) != 0;
+  for (int i = threadIdx.x; i < GC * D; i += NW * kWave) {
+    const int g = i / D;
+    const int d = i - g * D;
+    float M = s_ml[0][g][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][g][0]);
+    float L = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float a = fast_exp2(s_ml[w][g][0] - M);
+      L = fmaf(a, s_ml[w][g][1], L);
+      o = fmaf(a, s_acc[w][g][d], o);
+    }
+    if (bad) {
+      M = L = o = __builtin_nanf("");
+    }
+    if (single) {
+      store_out<F>(p.out, (out_row0 + g) * D + d, o / L);
+    } else {
+      const size_t slot = (out_row0 + g) * p.num_parts + part;
+      p.part_o[slot * D + d] = o;
+      if (d == 0) {
+        p.part_ml[2 * slot] = M;
+        p.part_ml[2 * slot + 1] = L;
+      }
+    }
+  }
+}
+
+// Waves per workgroup of the decode kernel.
+constexpr int kDecodeWaves = 4;
+
+// Positions per tile for a format / head_dim / block size (host and device).
+__host__ __device__ constexpr int tile_tokens(int elem_bytes, int head_dim, int block_size) {
+  // 16-byte fragments: head_dim*elem_bytes/16 lanes per row, 64/that rows per load.
+  return block_size > (64 * 16) / (head_dim * elem_bytes) ? block_size
+                                                           : (64 * 16) / (head_dim * elem_bytes);
+}
+
+}  // namespace pa

@@ -1,0 +1,98 @@
+// device.h -- small device-side helpers shared by the library's kernels
+// (internal header, not part of the ABI).  gfx950 / CDNA4, wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+// Running-max start value: finite, so that exp2(m_old - m_new) stays 1 while
+// nothing has been seen and becomes 0 at the first real score.
+constexpr float kMaxInit = -1.0e30f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+enum class Fmt : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3 };
+
+template <Fmt F> struct FmtInfo;
+template <> struct FmtInfo<Fmt::F32> { static constexpr int bytes = 4; static constexpr int q_bytes = 4; };
+template <> struct FmtInfo<Fmt::F16> { static constexpr int bytes = 2; static constexpr int q_bytes = 2; };
+template <> struct FmtInfo<Fmt::BF16> { static constexpr int bytes = 2; static constexpr int q_bytes = 2; };
+// int8 cache: fp16 queries and outputs.
+template <> struct FmtInfo<Fmt::I8> { static constexpr int bytes = 1; static constexpr int q_bytes = 2; };
+
+__device__ __forceinline__ float bits_to_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t float_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Reinterpret a 32-bit word as two packed 16-bit floats.  The word is taken
+// by value: __builtin_bit_cast applied directly to an ext-vector swizzle such
+// as v.y has been seen to read the wrong element, so callers pass v[i].
+__device__ __forceinline__ h16x2 as_h2(uint32_t w) { return __builtin_bit_cast(h16x2, w); }
+__device__ __forceinline__ bf16x2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// bfloat16 halves of a 32-bit word, as fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return bits_to_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return bits_to_float(w & 0xffff0000u); }
+// binary16 halves of a 32-bit word, as fp32 (exact).
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)as_h2(w)[0]; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)as_h2(w)[1]; }
+
+// fp32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+  uint32_t u = float_to_bits(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t float_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Cross-lane moves inside a row of 16 lanes through DPP (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return bits_to_float((uint32_t)__builtin_amdgcn_update_dpp(
+      0, (int)float_to_bits(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
+
+// Sum over aligned groups of N consecutive lanes; every lane of a group ends
+// with the same bits (each step adds two equal partial sums in either order).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "");
+  if constexpr (N >= 2) x += dpp_mov<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp_mov<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp_mov<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_mov<kDppMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp_mov<kDppXor1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp_mov<kDppXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp_mov<kDppMirror>(x));
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
+
+}  // namespace pa

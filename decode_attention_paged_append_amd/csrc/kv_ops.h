@@ -1,0 +1,37 @@
+// kv_ops.h -- launchers of the slot, append and gather kernels (internal).
+#pragma once
+
+#include "device.h"
+
+namespace pa {
+
+hipError_t launch_slot_mapping(const int32_t* tables, int32_t max_blocks, int32_t num_seqs,
+                               const int32_t* token_seq, const int32_t* token_pos,
+                               int64_t num_tokens, int32_t block_size, int64_t* slots,
+                               hipStream_t stream);
+hipError_t launch_decode_slot_mapping(const int32_t* tables, int32_t max_blocks,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t block_size, int64_t* slots, hipStream_t stream);
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
+                            int64_t num_tokens, void* k_cache, void* v_cache,
+                            int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,
+                            int64_t pool_slots, hipStream_t stream);
+hipError_t launch_kv_append_int8(const void* k_new, const void* v_new, const int64_t* slots,
+                                 int64_t num_tokens, int8_t* k_cache, int8_t* v_cache,
+                                 void* k_scale, void* v_scale, int32_t num_kv_heads,
+                                 int32_t block_size, int32_t head_dim, int64_t pool_slots,
+                                 hipStream_t stream);
+hipError_t launch_gather_kv(const void* k_cache, const void* v_cache, const void* k_scale,
+                            const void* v_scale, const int32_t* tables, int32_t max_blocks,
+                            const int32_t* context_lens, int32_t num_seqs, void* k_out,
+                            void* v_out, void* k_scale_out, void* v_scale_out,
+                            int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                            int32_t row_bytes, hipStream_t stream);
+
+// Log-sum-exp merge of partition partials (lse_merge.hip).
+hipError_t launch_lse_merge(const float* part_ml, const float* part_o,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t head_dim, int32_t max_tokens, int32_t part_tokens,
+                            int32_t num_parts, int32_t out_fmt, void* out, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,243 @@
+// kv_ops.hip -- slot mapping, append (plain and int8-quantizing) and the
+// un-paging gather, for gfx950.
+//
+// A sequence's positions live in fixed-size blocks of one shared pool, listed
+// in order by its block table; the slot of position pos is
+// table[pos / BS] * BS + pos % BS ("PagedAttention: the cache in blocks",
+// KV-cache visualization page).  A decode step appends the new token's K and
+// V rows at its slot ("KV cache: the engine behind fast LLM inference",
+// "What happens at each decoding step", step 4).
+#include "kv_ops.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------- slots
+
+__global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int32_t max_blocks,
+                                    int32_t num_seqs, const int32_t* __restrict__ token_seq,
+                                    const int32_t* __restrict__ token_pos, int64_t num_tokens,
+                                    int32_t block_size, int64_t* __restrict__ slots) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= num_tokens) return;
+  const int32_t s = token_seq[t];
+  const int32_t pos = token_pos[t];
+  int64_t slot = -1;
+  if (s >= 0 && s < num_seqs && pos >= 0 && pos < max_blocks * block_size) {
+    const int32_t block = tables[(int64_t)s * max_blocks + pos / block_size];
+    slot = (int64_t)block * block_size + pos % block_size;
+  }
+  slots[t] = slot;
+}
+
+__global__ void decode_slot_mapping_kernel(const int32_t* __restrict__ tables,
+                                           int32_t max_blocks,
+                                           const int32_t* __restrict__ context_lens,
+                                           int32_t num_seqs, int32_t block_size,
+                                           int64_t* __restrict__ slots) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= num_seqs) return;
+  const int32_t ctx = context_lens[s];
+  int64_t slot = -1;
+  if (ctx > 0 && ctx <= max_blocks * block_size) {
+    const int32_t pos = ctx - 1;
+    const int32_t block = tables[(int64_t)s * max_blocks + pos / block_size];
+    slot = (int64_t)block * block_size + pos % block_size;
+  }
+  slots[s] = slot;
+}
+
+// ---------------------------------------------------------------- append
+
+// One thread per 16-byte piece of a (token, head) row; K and V together.
+__global__ void kv_append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
+                                 const int64_t* __restrict__ slots, int64_t num_tokens,
+                                 u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
+                                 int32_t num_kv_heads, int32_t block_size, int32_t pieces,
+                                 int64_t pool_slots) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)num_kv_heads * pieces;
+  if (i >= num_tokens * per_token) return;
+  const int64_t t = i / per_token;
+  const int64_t rest = i - t * per_token;  // = h * pieces + c
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= pool_slots) return;
+  const int64_t block = slot / block_size;
+  const int64_t off = slot - block * block_size;
+  const int64_t h = rest / pieces;
+  const int64_t c = rest - h * pieces;
+  const int64_t dst = ((block * num_kv_heads + h) * block_size + off) * pieces + c;
+  k_cache[dst] = k_new[i];
+  v_cache[dst] = v_new[i];
+}
+
+// int8: LQ = D/8 lanes hold one (token, head) row of fp16 values, 8 each.
+//   a = max |x| over the row (exact);  s = fp16(a / 127)  (IEEE fp32 divide,
+//   round to nearest even);  code = clamp(rint(x / s), -127, 127), 0 if s == 0
+//   (and 0 for a NaN input).
+template <int D>
+__global__ __launch_bounds__(256) void kv_append_int8_kernel(
+    const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
+    const int64_t* __restrict__ slots, int64_t num_tokens, u32x2* __restrict__ k_cache,
+    u32x2* __restrict__ v_cache, uint16_t* __restrict__ k_scale, uint16_t* __restrict__ v_scale,
+    int32_t num_kv_heads, int32_t block_size, int64_t pool_slots) {
+  constexpr int LQ = D / 8;  // lanes per row
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / LQ;        // (token, head) row
+  const int c = (int)(gid % LQ);       // 8-value piece of the row
+  const bool live = row < num_tokens * num_kv_heads;
+  const int64_t t = live ? row / num_kv_heads : 0;
+  const int64_t h = live ? row - t * num_kv_heads : 0;
+  const int64_t slot = live ? slots[t] : -1;
+  const bool store = live && slot >= 0 && slot < pool_slots;
+  // Rows are whole lane groups, so a group shares 'store'; every lane still
+  // takes part in the reductions below.
+  u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+  if (store) {
+    kx = k_new[row * LQ + c];
+    vx = v_new[row * LQ + c];
+  }
+  auto quantize = [&](u32x4 x, u32x2* cache, uint16_t* scales) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = f16_lo(x[i]);
+      f[2 * i + 1] = f16_hi(x[i]);
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+    a = group_max<LQ>(a);
+    const _Float16 s16 = (_Float16)(a / 127.0f);
+    const float s = (float)s16;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float code = 0.0f;
+      if (s != 0.0f) {
+        const float r = rintf(f[i] / s);
+        code = r != r ? 0.0f : fminf(fmaxf(r, -127.0f), 127.0f);
+      }
+      packed[i / 4] |= ((uint32_t)(int32_t)code & 0xffu) << (8 * (i % 4));
+    }
+    if (store) {
+      const int64_t block = slot / block_size;
+      const int64_t off = slot - block * block_size;
+      const int64_t dst_row = (block * num_kv_heads + h) * block_size + off;
+      cache[dst_row * LQ + c] = u32x2{packed[0], packed[1]};
+      if (c == 0) scales[dst_row] = __builtin_bit_cast(uint16_t, s16);
+    }
+  };
+  quantize(kx, k_cache, k_scale);
+  quantize(vx, v_cache, v_scale);
+}
+
+// ---------------------------------------------------------------- gather
+
+// Grid-stride over (sequence, position, head, 16-byte piece) of the dense
+// output; positions at or past the context length are not written.
+__global__ void gather_kv_kernel(const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+                                 const uint16_t* __restrict__ k_scale,
+                                 const uint16_t* __restrict__ v_scale,
+                                 const int32_t* __restrict__ tables, int32_t max_blocks,
+                                 const int32_t* __restrict__ context_lens, int32_t num_seqs,
+                                 char* __restrict__ k_out, char* __restrict__ v_out,
+                                 uint16_t* __restrict__ k_scale_out,
+                                 uint16_t* __restrict__ v_scale_out, int32_t num_blocks,
+                                 int32_t num_kv_heads, int32_t block_size, int32_t row_bytes) {
+  const int32_t pieces = row_bytes / 16;
+  const int64_t cap = (int64_t)max_blocks * block_size;
+  const int64_t total = (int64_t)num_seqs * cap * num_kv_heads * pieces;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = i;
+    const int32_t c = (int32_t)(r % pieces); r /= pieces;
+    const int32_t h = (int32_t)(r % num_kv_heads); r /= num_kv_heads;
+    const int32_t pos = (int32_t)(r % cap);
+    const int32_t s = (int32_t)(r / cap);
+    const int32_t ctx = context_lens[s];
+    if (ctx < 0 || ctx > cap || pos >= ctx) continue;
+    const int32_t block = tables[(int64_t)s * max_blocks + pos / block_size];
+    if (block < 0 || block >= num_blocks) continue;
+    const int64_t src_row = ((int64_t)block * num_kv_heads + h) * block_size + pos % block_size;
+    const int64_t dst_row = ((int64_t)s * cap + pos) * num_kv_heads + h;
+    *(u32x4*)(k_out + dst_row * row_bytes + c * 16) =
+        *(const u32x4*)(k_cache + src_row * row_bytes + c * 16);
+    *(u32x4*)(v_out + dst_row * row_bytes + c * 16) =
+        *(const u32x4*)(v_cache + src_row * row_bytes + c * 16);
+    if (c == 0 && k_scale && k_scale_out) k_scale_out[dst_row] = k_scale[src_row];
+    if (c == 0 && v_scale && v_scale_out) v_scale_out[dst_row] = v_scale[src_row];
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+hipError_t launch_slot_mapping(const int32_t* tables, int32_t max_blocks, int32_t num_seqs,
+                               const int32_t* token_seq, const int32_t* token_pos,
+                               int64_t num_tokens, int32_t block_size, int64_t* slots,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks_for(num_tokens, 256)), dim3(256), 0, stream,
+                     tables, max_blocks, num_seqs, token_seq, token_pos, num_tokens, block_size,
+                     slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_slot_mapping(const int32_t* tables, int32_t max_blocks,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t block_size, int64_t* slots, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_slot_mapping_kernel, dim3(blocks_for(num_seqs, 256)), dim3(256), 0,
+                     stream, tables, max_blocks, context_lens, num_seqs, block_size, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
+                            int64_t num_tokens, void* k_cache, void* v_cache,
+                            int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,
+                            int64_t pool_slots, hipStream_t stream) {
+  const int32_t pieces = row_bytes / 16;
+  const int64_t n = num_tokens * num_kv_heads * pieces;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, stream,
+                     (const u32x4*)k_new, (const u32x4*)v_new, slots, num_tokens,
+                     (u32x4*)k_cache, (u32x4*)v_cache, num_kv_heads, block_size, pieces,
+                     pool_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_int8(const void* k_new, const void* v_new, const int64_t* slots,
+                                 int64_t num_tokens, int8_t* k_cache, int8_t* v_cache,
+                                 void* k_scale, void* v_scale, int32_t num_kv_heads,
+                                 int32_t block_size, int32_t head_dim, int64_t pool_slots,
+                                 hipStream_t stream) {
+  const int64_t lanes = num_tokens * num_kv_heads * (head_dim / 8);
+  const dim3 grid(blocks_for(lanes, 256));
+#define PA_APPEND_I8(D)                                                                        \
+  hipLaunchKernelGGL(kv_append_int8_kernel<D>, grid, dim3(256), 0, stream,                      \
+                     (const u32x4*)k_new, (const u32x4*)v_new, slots, num_tokens,               \
+                     (u32x2*)k_cache, (u32x2*)v_cache, (uint16_t*)k_scale, (uint16_t*)v_scale, \
+                     num_kv_heads, block_size, pool_slots)
+  if (head_dim == 64) PA_APPEND_I8(64);
+  else if (head_dim == 128) PA_APPEND_I8(128);
+  else return hipErrorInvalidValue;
+#undef PA_APPEND_I8
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_kv(const void* k_cache, const void* v_cache, const void* k_scale,
+                            const void* v_scale, const int32_t* tables, int32_t max_blocks,
+                            const int32_t* context_lens, int32_t num_seqs, void* k_out,
+                            void* v_out, void* k_scale_out, void* v_scale_out,
+                            int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                            int32_t row_bytes, hipStream_t stream) {
+  const int64_t total = (int64_t)num_seqs * max_blocks * block_size * num_kv_heads * (row_bytes / 16);
+  const int64_t want = (total + 255) / 256;
+  const unsigned grid = (unsigned)(want < 65536 ? (want > 0 ? want : 1) : 65536);
+  hipLaunchKernelGGL(gather_kv_kernel, dim3(grid), dim3(256), 0, stream, (const char*)k_cache,
+                     (const char*)v_cache, (const uint16_t*)k_scale, (const uint16_t*)v_scale,
+                     tables, max_blocks, context_lens, num_seqs, (char*)k_out, (char*)v_out,
+                     (uint16_t*)k_scale_out, (uint16_t*)v_scale_out, num_blocks, num_kv_heads,
+                     block_size, row_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace pa

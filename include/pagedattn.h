@@ -1,0 +1,242 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: single-token decode attention over
+ * a paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The operations come from three pages on the KV cache:
+ *   [guide] jovanaeducation.com/guides/l-is-2
+ *   [notes] "KV cache: the engine behind fast LLM inference"
+ *           (curiosity-9m6.pages.dev/notes/0043)
+ *   [viz]   the KV-cache visualization page
+ *           (cuuduongthancong.com/~galles/visualization/KVCache.html)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers named as device pointers must point to GPU memory on the current
+ * HIP device; "host" pointers point to CPU memory.  Every device buffer is
+ * owned by the caller: the library never allocates or frees memory, never
+ * synchronizes, and keeps no state between calls except a thread-local error
+ * message.  All GPU work is enqueued on `stream` (a hipStream_t; NULL is the
+ * default stream) and calls return before it completes.
+ *
+ * Layouts (row-major, C order):
+ *   k_cache, v_cache : [num_blocks][num_kv_heads][block_size][head_dim]
+ *                      one contiguous block_size x head_dim tile per
+ *                      (block, KV head)
+ *   k_scale, v_scale : [num_blocks][num_kv_heads][block_size] fp16, int8 only
+ *   block_tables     : int32 [num_seqs][max_blocks_per_seq]; entry j of row s
+ *                      is the pool block holding positions [j*BS, (j+1)*BS)
+ *                      of sequence s.  Entries past ceil(ctx/BS) are never read.
+ *   context_lens     : int32 [num_seqs]; the number of cached positions of
+ *                      each sequence, counting the token appended this step
+ *   q, out           : [num_seqs][num_q_heads][head_dim]
+ *   k_new, v_new     : [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping     : int64 [num_tokens]; slot = block * block_size + offset
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads) (grouped-query
+ * attention: consecutive query heads share a KV head, [viz] "How much
+ * memory").
+ *
+ * Supported: head_dim in {64, 128}; block_size in {4, 8, 16, 32}; element
+ * formats fp32, fp16, bf16 (q, caches and out share one format), and int8
+ * caches with fp16 q/out and per-(token, head) fp16 scales.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued.
+ * A non-PA_OK status means nothing was enqueued (except PA_ERR_HIP, which
+ * reports a launch failure); pa_last_error() then describes the problem.
+ * Device data that breaks the contract cannot be checked on the host without
+ * a synchronization; the kernels never read or write outside the buffers the
+ * descriptor describes, and mark the affected output instead:
+ *   - a context length < 0 or > max_blocks_per_seq * block_size, or a block
+ *     id outside [0, num_blocks) among a sequence's first ceil(ctx/BS)
+ *     entries, makes that sequence's output rows NaN;
+ *   - a slot outside [0, num_blocks * block_size) is skipped by the appends
+ *     (negative slots are padding by contract);
+ *   - two tokens with the same slot in one append race: which row lands
+ *     there is unspecified.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_I8 = 3
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, negative size, Hq % Hkv != 0 ... */
+  PA_ERR_UNSUPPORTED = 2, /* head_dim, block_size or dtype outside the list */
+  PA_ERR_WORKSPACE = 3,   /* workspace smaller than pa_decode_workspace_bytes */
+  PA_ERR_HIP = 4          /* a HIP launch reported an error */
+} pa_status;
+
+/* Shape and element format of one layer's block pool (K and V alike). */
+typedef struct {
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t dtype; /* pa_dtype of the cache elements */
+} pa_cache_desc;
+
+typedef void* pa_stream_t; /* a hipStream_t */
+
+/* ---------------------------------------------------------------- slots */
+
+/* Slot of each appended token: slot = block_tables[seq][pos / BS] * BS +
+ * pos % BS, i.e. the position's block from the sequence's ordered block
+ * table and the offset inside it ([viz] "PagedAttention: the cache in
+ * blocks").  token_seq, token_pos: device int32 [num_tokens]; slot_mapping:
+ * device int64 [num_tokens] (written).  A token whose seq or position falls
+ * outside the table gets slot -1. */
+pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t num_seqs, const int32_t* token_seq,
+                          const int32_t* token_pos, int64_t num_tokens,
+                          int32_t block_size, int64_t* slot_mapping,
+                          pa_stream_t stream);
+
+/* Decode-step slots: each sequence appends one token at position
+ * context_lens[s] - 1 (the length already counts it; [notes] "What happens at
+ * each decoding step", steps 2 and 4).  slot_mapping: device int64
+ * [num_seqs].  Sequences with length 0 or a length past the table get -1. */
+pa_status pa_decode_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t block_size, int64_t* slot_mapping,
+                                 pa_stream_t stream);
+
+/* ---------------------------------------------------------------- append */
+
+/* Store each new token's K and V rows into the pool at its slot, for every
+ * KV head ([notes] step 4 "Append and repeat"; [guide] "How the cache turns
+ * the loop cheap").  k_new, v_new: device [num_tokens][Hkv][D] in the cache's
+ * format (fp32/fp16/bf16); k_cache, v_cache: device pools, updated in place.
+ * Bit-exact copy.  Negative slots are skipped. */
+pa_status pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                       int64_t num_tokens, void* k_cache, void* v_cache,
+                       const pa_cache_desc* cache, pa_stream_t stream);
+
+/* int8 cache ([notes] "How serving systems tame the cost", quantized KV
+ * cache; the quantizer is this library's reading): for every (token, head)
+ * row of fp16 values x,
+ *   a = max |x|,  s = fp16_rne(fp32(a / 127)),
+ *   code = clamp(rint_half_even(fp32(x / s)), -127, 127)   (0 when s == 0),
+ * with IEEE binary32 divisions.  Codes go to k_cache/v_cache (device int8
+ * pools, cache->dtype == PA_I8), s to k_scale/v_scale (device fp16
+ * [NB][Hkv][BS]).  k_new, v_new: device fp16 [num_tokens][Hkv][D]. */
+pa_status pa_kv_append_int8(const void* k_new, const void* v_new,
+                            const int64_t* slot_mapping, int64_t num_tokens,
+                            int8_t* k_cache, int8_t* v_cache, void* k_scale,
+                            void* v_scale, const pa_cache_desc* cache,
+                            pa_stream_t stream);
+
+/* ---------------------------------------------------------------- attention */
+
+/* Workspace the decode entry points need for this shape: fp32 partial
+ * results (running max, sum and unnormalized output) of every context
+ * partition.  partition_tokens = 0 picks the library's own plan, the one
+ * pa_paged_decode_attention uses; pass the same value to the phase entry
+ * points below.  Pure host arithmetic; returns 0 for an invalid shape. */
+size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                 int32_t partition_tokens);
+
+/* The partition length (tokens) the library's plan picks for this shape,
+ * a multiple of the tile length.  Pure host arithmetic; 0 if invalid. */
+int32_t pa_decode_partition_tokens(const pa_cache_desc* cache, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_blocks_per_seq);
+
+/* Decode attention for one new token per sequence: for every query head h,
+ *   out[s][h] = softmax(q[s][h] . K_s^T * scale) . V_s
+ * over the context_lens[s] cached rows of KV head h / G, reached through the
+ * block table ([notes] "Concept" and step 3 "Attend against the cache";
+ * [viz] "PagedAttention: the cache in blocks").  The softmax runs online
+ * over the cache, tile by tile, never forming the score row in memory
+ * ([guide] "Flash attention: don't build the giant matrix"); long contexts
+ * are split into partitions whose partial results a log-sum-exp merge
+ * combines.  q, out: device [S][Hq][D] in the cache's format; fp32
+ * accumulation; out rounded to nearest-even.  A sequence with length 0
+ * gets zeros.  workspace: device, >= pa_decode_workspace_bytes(cache, S, Hq,
+ * max_blocks_per_seq, 0) bytes, contents clobbered. */
+pa_status pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, float scale, void* out,
+                                    const pa_cache_desc* cache, void* workspace,
+                                    size_t workspace_bytes, pa_stream_t stream);
+
+/* The same over an int8 cache: keys and values are code * scale, with the
+ * scales folded into the scores and the weights.  q, out: device fp16. */
+pa_status pa_paged_decode_attention_int8(const void* q, const int8_t* k_cache,
+                                         const int8_t* v_cache, const void* k_scale,
+                                         const void* v_scale, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, float scale, void* out,
+                                         const pa_cache_desc* cache, void* workspace,
+                                         size_t workspace_bytes, pa_stream_t stream);
+
+/* Phase 1 of the above with an explicit partition length, or 0 for the
+ * plan's.  The length must be a positive multiple of the tile, which is
+ * max(block_size, 1024 / (head_dim * bytes per cache element)) positions
+ * (PA_ERR_INVALID_ARG otherwise).  Each workgroup attends
+ * over one partition of one sequence's context for one KV head's query
+ * heads and writes its partial (max, sum, unnormalized output) into the
+ * workspace.  When the partition covers the whole table width
+ * (partition_tokens >= max_blocks_per_seq * BS) the result is final and is
+ * written to out directly; otherwise pa_lse_merge must follow.  k_scale and
+ * v_scale are used only for an int8 cache (NULL otherwise). */
+pa_status pa_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
+                               const void* k_scale, const void* v_scale,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, float scale, int32_t partition_tokens,
+                               void* out, const pa_cache_desc* cache, void* workspace,
+                               size_t workspace_bytes, pa_stream_t stream);
+
+/* Phase 2: log-sum-exp merge of the partitions' partials into out
+ * (max M = max_p m_p; out = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p),
+ * which is the same softmax-weighted sum a single pass gives ([guide]
+ * "Flash attention": tiling leaves the math unchanged).  Arguments as for
+ * pa_decode_partitions with the same partition_tokens; out_dtype is the
+ * format of out (PA_F32, PA_F16 or PA_BF16). */
+pa_status pa_lse_merge(const void* workspace, size_t workspace_bytes,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t partition_tokens, int32_t out_dtype, void* out,
+                       pa_stream_t stream);
+
+/* ---------------------------------------------------------------- gather */
+
+/* Un-page every sequence to dense rows (for checking the block-table
+ * gather): k_out[s][i][h][:] = row of position i, for i < context_lens[s];
+ * rows at or past the length are left untouched.  k_out, v_out: device
+ * [num_seqs][max_blocks_per_seq * BS][Hkv][D] in the cache's format (int8
+ * codes for an int8 cache).  k_scale/v_scale and k_scale_out/v_scale_out
+ * ([S][maxB*BS][Hkv] fp16) are used for an int8 cache only (may be NULL). */
+pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_scale,
+                       const void* v_scale, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t num_seqs, void* k_out, void* v_out, void* k_scale_out,
+                       void* v_scale_out, const pa_cache_desc* cache, pa_stream_t stream);
+
+/* ---------------------------------------------------------------- misc */
+
+const char* pa_status_string(pa_status status); /* static string */
+const char* pa_last_error(void);  /* thread-local detail of the last failure */
+int32_t pa_abi_version(void);     /* PA_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

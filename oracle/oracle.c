@@ -230,6 +230,7 @@ int oracle_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
  *   a = max |x|                         (exact)
  *   s = binary16 nearest to fp32(a / 127)   (fp32 IEEE division, then RNE)
  *   q = clamp(round_half_even(fp32(x / s)), -127, 127), q = 0 when s == 0
+ *   (and for a NaN input),
  * so that q * s reproduces x to within half a step.  All divisions are IEEE
  * binary32, which the GPU reproduces exactly.                               */
 void oracle_quantize_row_int8(const uint16_t* x_f16, int32_t n, int8_t* q,
@@ -252,6 +253,7 @@ void oracle_quantize_row_int8(const uint16_t* x_f16, int32_t n, int8_t* q,
     float x = (float)oracle_f16_to_double(x_f16[d]);
     volatile float r = x / s; /* binary32 quotient */
     float c = rintf(r);       /* default rounding mode: half to even */
+    if (c != c) c = 0.0f;     /* a NaN input encodes as 0 */
     if (c > 127.0f) c = 127.0f;
     if (c < -127.0f) c = -127.0f;
     q[d] = (int8_t)c;

@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_paged_append_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIBRARY_PATH):
+        pytest.fail("libpagedattn.so not built (python -m decode_attention_paged_append_amd.build)")
+    return pa.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pa_abi_version() == int(re.search(r"PA_ABI_VERSION (\d+)", open(HEADER).read())[1])
+    assert lib.pa_status_string(WORKSPACE) == b"workspace too small"
+
+
+def desc(nb=64, hkv=2, bs=16, d=128, dtype=1):
+    return pa.CacheDesc(nb, hkv, bs, d, dtype)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+def test_append_argument_checks(lib):
+    d = desc()
+    assert lib.pa_kv_append(FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, None) == INVALID
+    assert lib.pa_kv_append(FAKE, FAKE, FAKE, -1, FAKE, FAKE, ctypes.byref(d), None) == INVALID
+    assert lib.pa_kv_append(FAKE, None, FAKE, 4, FAKE, FAKE, ctypes.byref(d), None) == INVALID
+    assert lib.pa_kv_append(None, None, None, 0, None, None, ctypes.byref(d), None) == OK
+    bad = desc(d=96)
+    assert lib.pa_kv_append(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(bad), None) == UNSUPPORTED
+    assert b"head_dim 96" in lib.pa_last_error()
+    bad = desc(bs=12)
+    assert lib.pa_kv_append(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(bad), None) == UNSUPPORTED
+    i8 = desc(dtype=3)
+    assert lib.pa_kv_append(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(i8), None) == UNSUPPORTED
+    assert lib.pa_kv_append_int8(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d),
+                                 None) == UNSUPPORTED
+    assert lib.pa_kv_append_int8(FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, FAKE, ctypes.byref(i8),
+                                 None) == INVALID
+
+
+def test_decode_argument_checks(lib):
+    d = desc()
+    call = lambda hq, ws, wsb, desc_=d, s=4, maxb=16: lib.pa_paged_decode_attention(
+        FAKE, FAKE, FAKE, FAKE, maxb, FAKE, s, hq, 0.1, FAKE, ctypes.byref(desc_), ws, wsb, None)
+    assert call(3, FAKE, 1 << 30) == INVALID            # 3 query heads over 2 KV heads
+    assert call(0, FAKE, 1 << 30) == INVALID
+    assert call(4, FAKE, 1 << 30, s=-1) == INVALID
+    assert call(4, FAKE, 1 << 30, maxb=0) == INVALID
+    assert call(4, FAKE, 1 << 30, desc_=desc(dtype=3)) == UNSUPPORTED  # int8 needs its entry
+    assert call(4, FAKE, 1 << 30, desc_=desc(dtype=7)) == UNSUPPORTED
+    need = lib.pa_decode_workspace_bytes(ctypes.byref(d), 4, 4, 16, 64)
+    assert need > 0
+    assert lib.pa_decode_partitions(FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, 4, 4, 0.1, 64,
+                                    FAKE, ctypes.byref(d), FAKE, need - 1, None) == WORKSPACE
+    assert lib.pa_decode_partitions(FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, 4, 4, 0.1, 24,
+                                    FAKE, ctypes.byref(d), FAKE, need, None) == INVALID
+    assert b"multiple of the tile" in lib.pa_last_error()
+    assert call(4, None, 0, s=0) == OK                  # nothing to do
+    assert lib.pa_lse_merge(FAKE, 0, FAKE, 4, 4, 128, 16, 16, 64, 1, FAKE, None) == WORKSPACE
+    assert lib.pa_lse_merge(FAKE, 1 << 30, FAKE, 4, 4, 128, 16, 16, 256, 1, FAKE, None) == INVALID
+    assert lib.pa_lse_merge(FAKE, 1 << 30, FAKE, 4, 4, 128, 16, 16, 64, 3, FAKE, None) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype,d,bs,tile", [(0, 64, 4, 4), (1, 128, 16, 16), (1, 64, 4, 8),
+                                              (3, 64, 4, 16), (3, 128, 32, 32), (0, 128, 8, 8)])
+def test_workspace_and_plan(lib, dtype, d, bs, tile):
+    dd = desc(nb=4096, hkv=8, bs=bs, d=d, dtype=dtype)
+    s, hq, maxb = 16, 32, 4096 // bs
+    part = lib.pa_decode_partition_tokens(ctypes.byref(dd), s, hq, maxb)
+    assert part > 0 and part % tile == 0 and part % bs == 0
+    nparts = -(-maxb * bs // part)
+    ws = lib.pa_decode_workspace_bytes(ctypes.byref(dd), s, hq, maxb, 0)
+    if nparts == 1:
+        assert ws == 0
+    else:
+        ml = s * hq * nparts * 2 * 4
+        assert ws == ((ml + 255) // 256) * 256 + s * hq * nparts * d * 4
+    # an explicit partition covering the whole table needs no workspace
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(dd), s, hq, maxb, maxb * bs) == 0

@@ -1,0 +1,307 @@
+"""Parity of the HIP kernels with the CPU oracle on small seeded inputs that
+span several tiles, ragged tails and the edge cases (needs an MI355X)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_paged_append_amd as pa
+import oracle
+import workloads as W
+from gpu_cases import (TOL, decode_gpu, decode_oracle, dev, host, max_abs_err,
+                       quantize_blocks_oracle, quantize_pool_gpu, tile_tokens)
+
+pytestmark = pytest.mark.gpu
+
+TORCH = W.TORCH_DTYPE
+
+
+def make(dtype, hq, hkv, d, bs, ctx, spare_blocks=5, seed=0, poison_new=False):
+    shape = W.Shape(f"t-{dtype}", dtype, len(ctx), hq, hkv, d, bs)
+    need = sum(W.blocks_needed(c, bs) for c in ctx)
+    lay = W.carve_layout(ctx, bs, num_blocks=need + spare_blocks, seed=seed + 1)
+    case = W.make_case(shape, lay, seed=seed, poison=True, poison_new_slot=poison_new)
+    return shape, lay, case
+
+
+def to_dev(*ts):
+    return [t.to(dev()).contiguous() for t in ts]
+
+
+# ---------------------------------------------------------------- slots / append / gather
+
+@pytest.mark.parametrize("bs", [4, 16, 32])
+def test_slot_mapping_bit_exact(bs):
+    ctx = [0, 1, bs, bs + 1, 5 * bs - 1, 77]
+    lay = W.carve_layout(ctx, bs, num_blocks=64, seed=3)
+    bt, ctx_t = to_dev(lay.block_tables, lay.context_lens)
+    got = pa.decode_slot_mapping(bt, ctx_t, bs)
+    ref = oracle.decode_slot_mapping(host(lay.block_tables), host(lay.context_lens), bs)
+    assert (got.cpu().numpy() == ref).all()
+    seq = torch.tensor([1, 3, 3, 5, 5, 5], dtype=torch.int32)
+    pos = torch.tensor([0, 0, bs, 0, 40, 76], dtype=torch.int32)
+    got = pa.slot_mapping(bt, *to_dev(seq, pos), bs)
+    ref = oracle.slot_mapping(host(lay.block_tables), seq.numpy(), pos.numpy(), bs)
+    assert (got.cpu().numpy() == ref).all()
+    # outside the table: -1
+    bad = pa.slot_mapping(bt, *to_dev(torch.tensor([9, 0], dtype=torch.int32),
+                                      torch.tensor([0, lay.max_blocks * bs], dtype=torch.int32)), bs)
+    assert bad.cpu().tolist() == [-1, -1]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_kv_append_bit_exact(dtype, d):
+    nb, hkv, bs = 12, 3, 8
+    src = W.randn((nb, hkv, bs, d), dtype, 5)
+    kc, vc = src.clone(), W.randn((nb, hkv, bs, d), dtype, 6)
+    k_new, v_new = W.randn((7, hkv, d), dtype, 7), W.randn((7, hkv, d), dtype, 8)
+    slots = torch.tensor([3, -1, 50, 0, nb * bs - 1, nb * bs, 17], dtype=torch.int64)
+    kd, vd, knd, vnd, sd = to_dev(kc, vc, k_new, v_new, slots)
+    pa.kv_append(knd, vnd, sd, kd, vd)
+    torch.cuda.synchronize()
+    kh, vh = host(kc).copy(), host(vc).copy()
+    ok = slots.clone()
+    ok[ok >= nb * bs] = -1          # the oracle rejects what the kernel skips
+    oracle.kv_append(host(k_new), host(v_new), ok.numpy(), kh, vh, bf16=dtype == "bf16")
+    assert host(kd).tobytes() == kh.tobytes()
+    assert host(vd).tobytes() == vh.tobytes()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kv_append_int8_bit_exact(d):
+    nb, hkv, bs = 10, 2, 16
+    t = 40
+    k_new = (torch.randn((t, hkv, d), generator=W.generator(9)) *
+             torch.logspace(-4, 4, t)[:, None, None]).to(torch.float16)
+    v_new = W.randn((t, hkv, d), "f16", 10)
+    k_new[3] = 0                     # all-zero rows: scale 0, codes 0
+    k_new[4, 0, :5] = torch.tensor([65504, -65504, 1e-7, 6e-8, -3.0])
+    slots = torch.randperm(nb * bs, generator=W.generator(11))[:t].to(torch.int64)
+    slots[5] = -1
+    kq = torch.full((nb, hkv, bs, d), -128, dtype=torch.int8)
+    vq = kq.clone()
+    ks = torch.full((nb, hkv, bs), float("nan"), dtype=torch.float16)
+    vs = ks.clone()
+    dk = to_dev(k_new, v_new, slots, kq, vq, ks, vs)
+    pa.kv_append_int8(*dk)
+    torch.cuda.synchronize()
+    hq_, hv_, hks, hvs = host(kq).copy(), host(vq).copy(), host(ks).copy(), host(vs).copy()
+    oracle.kv_append_int8(host(k_new), host(v_new), host(slots), hq_, hv_, hks, hvs)
+    assert host(dk[3]).tobytes() == hq_.tobytes()
+    assert host(dk[4]).tobytes() == hv_.tobytes()
+    assert host(dk[5]).view(np.uint16).tobytes() == hks.view(np.uint16).tobytes()
+    assert host(dk[6]).view(np.uint16).tobytes() == hvs.view(np.uint16).tobytes()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_gather_bit_exact(dtype):
+    ctx = [0, 5, 16, 33]
+    bs, hkv, d = 4, 2, 64
+    lay = W.carve_layout(ctx, bs, num_blocks=20, seed=2)
+    cdt = dtype if dtype != "i8" else "f16"
+    kc = W.randn((20, hkv, bs, d), cdt, 1)
+    vc = W.randn((20, hkv, bs, d), cdt, 2)
+    ks = vs = None
+    if dtype == "i8":
+        kc = (kc * 40).clamp(-127, 127).to(torch.int8)
+        vc = (vc * 40).clamp(-127, 127).to(torch.int8)
+        ks, vs = W.randn((20, hkv, bs), "f16", 3), W.randn((20, hkv, bs), "f16", 4)
+    cap = lay.max_blocks * bs
+    fill = (lambda shp, t: torch.full(shp, 7, dtype=t))
+    ko, vo = fill((4, cap, hkv, d), kc.dtype), fill((4, cap, hkv, d), kc.dtype)
+    kso = vso = None
+    if dtype == "i8":
+        kso, vso = fill((4, cap, hkv), torch.float16), fill((4, cap, hkv), torch.float16)
+    args = [None if x is None else x.to(dev()).contiguous()
+            for x in (kc, vc, lay.block_tables, lay.context_lens, ko, vo, ks, vs, kso, vso)]
+    pa.gather_kv(*args)
+    torch.cuda.synchronize()
+    refs = [host(x).copy() if x is not None else None for x in (ko, vo, kso, vso)]
+    oracle.gather_kv(host(kc), host(vc), host(lay.block_tables), host(lay.context_lens),
+                     refs[0], refs[1], None if ks is None else host(ks),
+                     None if vs is None else host(vs), refs[2], refs[3], bf16=dtype == "bf16")
+    for g, r in zip((args[4], args[5], args[8], args[9]), refs):
+        if r is not None:
+            assert host(g).tobytes() == r.tobytes()
+
+
+# ---------------------------------------------------------------- attention
+
+SWEEP_HEADS = [(4, 4), (8, 4), (8, 2), (8, 1), (6, 2), (16, 1)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bs", [4, 8, 16, 32])
+@pytest.mark.parametrize("hq,hkv", SWEEP_HEADS)
+def test_decode_matches_oracle(dtype, d, bs, hq, hkv):
+    ctx = [0, 1, bs - 1, bs, bs + 1, 3 * bs + 5, 257, 600]
+    shape, lay, case = make(dtype, hq, hkv, d, bs, ctx, seed=hq * 7 + bs)
+    q, kc, vc, bt, ctx_t = to_dev(case.q, case.k_cache, case.v_cache, lay.block_tables,
+                                  lay.context_lens)
+    ref = decode_oracle(case.q, case.k_cache, case.v_cache, lay.block_tables, lay.context_lens,
+                        shape.scale)
+    tile = tile_tokens(dtype, d, bs)
+    whole = -(-lay.max_blocks * bs // tile) * tile      # one partition covers the table
+    for part in (None, tile, 3 * tile, whole):
+        out = decode_gpu(q, kc, vc, bt, ctx_t, shape.scale, part)
+        err = max_abs_err(out, ref)
+        assert err <= TOL[dtype], (part, err)
+        assert (out[0] == 0).all()   # empty sequence
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bs", [4, 16, 32])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (16, 2)])
+def test_int8_decode_matches_oracle(d, bs, hq, hkv):
+    ctx = [1, bs + 3, 200, 513]
+    shape, lay, case = make("i8", hq, hkv, d, bs, ctx, seed=3, spare_blocks=2)
+    src_k = case.k_cache.nan_to_num(0.0).to(dev())
+    src_v = case.v_cache.nan_to_num(0.0).to(dev())
+    kq, vq, ks, vs = quantize_pool_gpu(src_k, src_v, None)
+    okq, ovq, oks, ovs, blocks = quantize_blocks_oracle(src_k, src_v, range(lay.num_blocks))
+    assert host(kq).tobytes() == okq.tobytes() and host(vs).tobytes() == ovs.tobytes()
+    q, bt, ctx_t = to_dev(case.q, lay.block_tables, lay.context_lens)
+    ref = oracle.paged_decode_attention(host(case.q), okq, ovq, host(lay.block_tables),
+                                        host(lay.context_lens), shape.scale, k_scale=oks,
+                                        v_scale=ovs)
+    tile = tile_tokens("i8", d, bs)
+    for part in (None, tile, -(-lay.max_blocks * bs // tile) * tile):
+        out = decode_gpu(q, kq, vq, bt, ctx_t, shape.scale, part, ks, vs)
+        assert max_abs_err(out, ref) <= TOL["i8"], part
+
+
+def test_tiny_config_decode_step():
+    """The tiny fp32 workload: slots, append and attention of one decode step."""
+    shape = W.TINY
+    lay = W.layout_for(shape)
+    case = W.make_case(shape, lay, poison=True, poison_new_slot=True)
+    q, kc, vc, kn, vn, bt, ctx = to_dev(case.q, case.k_cache, case.v_cache, case.k_new,
+                                        case.v_new, lay.block_tables, lay.context_lens)
+    slots = pa.decode_slot_mapping(bt, ctx, shape.block_size)
+    pa.kv_append(kn, vn, slots, kc, vc)
+    out = decode_gpu(q, kc, vc, bt, ctx, shape.scale)
+    oslots = oracle.decode_slot_mapping(host(lay.block_tables), host(lay.context_lens),
+                                        shape.block_size)
+    assert (slots.cpu().numpy() == oslots).all()
+    kh, vh = host(case.k_cache).copy(), host(case.v_cache).copy()
+    oracle.kv_append(host(case.k_new), host(case.v_new), oslots, kh, vh)
+    assert host(kc).tobytes() == kh.tobytes() and host(vc).tobytes() == vh.tobytes()
+    ref = oracle.paged_decode_attention(host(case.q), kh, vh, host(lay.block_tables),
+                                        host(lay.context_lens), shape.scale)
+    assert max_abs_err(out, ref) <= TOL["f32"]
+
+
+def test_tiny_prefill_then_decode_loop():
+    """3-token prompt + 4 decode steps on the GPU (append only the new rows)
+    against the oracle's cached and recomputing lanes."""
+    from oracle import decode_loop
+    rng = np.random.default_rng(21)
+    hq, hkv, d, dm, bs = 4, 2, 64, 64, 4
+    x = rng.standard_normal((7, dm))
+    Wq, Wk, Wv = (rng.standard_normal((dm, n * d)) / 8 for n in (hq, hkv, hkv))
+    table = [11, 3, 40]
+    ref = decode_loop.run(x, Wq, Wk, Wv, 3, hq, hkv, d, bs, table, 64, 0.125)
+    qr = (x @ Wq).astype(np.float32).reshape(7, hq, d)
+    kr = (x @ Wk).astype(np.float32).reshape(7, hkv, d)
+    vr = (x @ Wv).astype(np.float32).reshape(7, hkv, d)
+    kc = torch.full((64, hkv, bs, d), float("nan"), device=dev())
+    vc = torch.full_like(kc, float("nan"))
+    bt = torch.tensor([table], dtype=torch.int32, device=dev())
+    done = 0
+    for i, n in enumerate(ref["prefix_lengths"]):
+        new = torch.arange(done, n, dtype=torch.int32, device=dev())
+        slots = pa.slot_mapping(bt, torch.zeros_like(new), new, bs)
+        pa.kv_append(torch.from_numpy(kr[done:n]).to(dev()), torch.from_numpy(vr[done:n]).to(dev()),
+                     slots, kc, vc)
+        done = n
+        out = decode_gpu(torch.from_numpy(qr[n - 1:n]).to(dev()), kc, vc, bt,
+                         torch.tensor([n], dtype=torch.int32, device=dev()), 0.125)
+        assert max_abs_err(out[0], ref["out_cache"][i]) <= TOL["f32"]
+        assert max_abs_err(out[0], ref["out_no_cache"][i]) <= TOL["f32"]
+
+
+def test_permutation_invariance_bit_exact():
+    """Renumbering the pool's blocks leaves the GPU result bit-identical."""
+    shape, lay, case = make("f16", 8, 2, 128, 16, [5, 100, 300, 1000], spare_blocks=9)
+    perm = torch.randperm(lay.num_blocks, generator=W.generator(5))
+    k2, v2 = torch.empty_like(case.k_cache), torch.empty_like(case.v_cache)
+    k2[perm], v2[perm] = case.k_cache, case.v_cache
+    bt2 = torch.where(lay.block_tables >= 0, perm[lay.block_tables.clamp(min=0).long()].int(),
+                      lay.block_tables)
+    a = decode_gpu(*to_dev(case.q, case.k_cache, case.v_cache, lay.block_tables, lay.context_lens),
+                   shape.scale)
+    b = decode_gpu(*to_dev(case.q, k2, v2, bt2, lay.context_lens), shape.scale)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_shared_prefix_and_determinism():
+    """Sequences naming the same blocks with the same query give the same bits;
+    repeated runs give the same bits."""
+    bs, d = 16, 128
+    ctx = [700, 700, 1500]
+    shape, lay, case = make("bf16", 8, 1, d, bs, ctx, seed=4)
+    bt = lay.block_tables.clone()
+    bt[1] = bt[0]
+    q = case.q.clone()
+    q[1] = q[0]
+    args = to_dev(q, case.k_cache, case.v_cache, bt, lay.context_lens)
+    a = decode_gpu(*args, shape.scale)
+    assert torch.equal(a[0].view(torch.int16), a[1].view(torch.int16))
+    for _ in range(3):
+        assert torch.equal(decode_gpu(*args, shape.scale).view(torch.int16), a.view(torch.int16))
+
+
+def test_value_rows_of_ones_and_one_hot():
+    """V = 1 gives 1; one-hot V rows expose the softmax weights."""
+    ctx = [33, 64]
+    shape, lay, case = make("f32", 2, 2, 64, 4, ctx, seed=8)
+    vc = torch.ones_like(case.v_cache)
+    out = decode_gpu(*to_dev(case.q, case.k_cache, vc, lay.block_tables, lay.context_lens), 0.125)
+    assert (out - 1).abs().max().item() <= 1e-6
+    # one-hot: V row of position i is e_i (positions < 64 = head_dim)
+    vc = torch.zeros_like(case.v_cache)
+    for s in range(2):
+        for i in range(ctx[s]):
+            vc[lay.block_tables[s, i // 4], :, i % 4, i] = 1.0
+    out = decode_gpu(*to_dev(case.q, case.k_cache, vc, lay.block_tables, lay.context_lens), 0.125)
+    for s in range(2):
+        for h in range(2):
+            K = np.stack([host(case.k_cache)[lay.block_tables[s, i // 4], h, i % 4]
+                          for i in range(ctx[s])]).astype(np.float64)
+            z = 0.125 * K @ host(case.q)[s, h].astype(np.float64)
+            w = np.exp(z - z.max()) / np.exp(z - z.max()).sum()
+            got = out[s, h].double().cpu().numpy()
+            assert np.abs(got[:ctx[s]] - w).max() <= 1e-6 and (got[ctx[s]:] == 0).all()
+
+
+def test_broken_device_data_gives_nan_not_faults():
+    """A context length past the table, or a block id outside the pool, makes
+    that sequence's rows NaN; other sequences are unaffected."""
+    shape, lay, case = make("f16", 4, 2, 128, 16, [40, 40, 40, 40], seed=6)
+    ctx = lay.context_lens.clone()
+    ctx[1] = lay.max_blocks * 16 + 1
+    ctx[2] = -3
+    bt = lay.block_tables.clone()
+    bt[3, 1] = lay.num_blocks + 1000
+    ref = decode_oracle(case.q, case.k_cache, case.v_cache, lay.block_tables, lay.context_lens,
+                        shape.scale)
+    for part in (None, 16, 64):
+        out = decode_gpu(*to_dev(case.q, case.k_cache, case.v_cache, bt, ctx), shape.scale, part)
+        assert torch.isnan(out[1:]).all()
+        assert max_abs_err(out[:1], ref[:1]) <= TOL["f16"]
+
+
+def test_large_scores_stay_finite():
+    """A scale that makes exp overflow in a naive softmax still gives the row
+    with the largest score (online max subtraction)."""
+    shape, lay, case = make("f32", 2, 1, 64, 16, [300, 1000], seed=12)
+    out = decode_gpu(*to_dev(case.q, case.k_cache, case.v_cache, lay.block_tables,
+                             lay.context_lens), 1e3)
+    ref = decode_oracle(case.q, case.k_cache, case.v_cache, lay.block_tables, lay.context_lens,
+                        1e3)
+    # near-ties between the top scores amplify fp32 score rounding; the check is
+    # that nothing overflows and the result tracks the oracle loosely
+    assert torch.isfinite(out).all() and max_abs_err(out, ref) <= 1e-2
