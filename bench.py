@@ -10,9 +10,9 @@ new token's K/V rows, partitioned paged attention and the log-sum-exp merge.
 
 Prints one JSON line.  value = logical KV bytes read per step / step time
 (GB/s); the roofline block times the dominant kernel (the partitioned
-attention) with HIP events around each of its launches inside the timed
-region; cpu_baseline times the CPU oracle on the host cores over a bounded
-sample of the same workload.
+attention) with HIP events around a back-to-back batch of its launches;
+cpu_baseline times the CPU oracle on the host cores over a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -52,7 +52,7 @@ def kernel_source_hash() -> str:
 class Bench:
     """All layers' inputs resident on the GPU, and the step that runs them."""
 
-    def __init__(self, shape: W.Shape, layers: int, dev):
+    def __init__(self, shape: W.Shape, layers: int, dev, partition_tokens: int = 0):
         self.shape, self.layers, self.dev = shape, layers, dev
         self.layout = W.layout_for(shape)
         lay = self.layout
@@ -69,7 +69,7 @@ class Bench:
         s, hq, d = shape.num_seqs, shape.num_q_heads, shape.head_dim
         desc = pa.CacheDesc(lay.num_blocks, shape.num_kv_heads, shape.block_size, d,
                             pa.DTYPE_CODE[W.TORCH_DTYPE[shape.cache_dtype]])
-        self.part = pa.decode_partition_tokens(desc, s, hq, lay.max_blocks)
+        self.part = partition_tokens or pa.decode_partition_tokens(desc, s, hq, lay.max_blocks)
         self.nparts = -(-lay.max_blocks * shape.block_size // self.part)
         nbytes = pa.decode_workspace_bytes(desc, s, hq, lay.max_blocks, self.part)
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -90,9 +90,8 @@ class Bench:
         c.k_scale, c.v_scale = ks, vs
         return c
 
-    def step(self, events=None):
-        """One decode step over every layer; events: list of (start, end) pairs
-        recorded around each layer's partitioned-attention launch."""
+    def step(self):
+        """One decode step over every layer."""
         sh = self.shape
         if self.append:
             pa.decode_slot_mapping(self.bt, self.ctx, sh.block_size, out=self.slots)
@@ -104,15 +103,17 @@ class Bench:
                     pa.kv_append_int8(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache, ks, vs)
                 else:
                     pa.kv_append(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache)
-            if events is not None:
-                events[layer][0].record()
-            pa.decode_partitions(c.q, c.k_cache, c.v_cache, self.bt, self.ctx, sh.scale,
-                                 self.outs[layer], self.part, self.ws, ks, vs)
-            if events is not None:
-                events[layer][1].record()
+            self.attend(layer)
             if self.nparts > 1:
                 pa.lse_merge(self.ws, self.ctx, sh.num_q_heads, sh.head_dim,
                              self.layout.max_blocks, sh.block_size, self.part, self.outs[layer])
+
+    def attend(self, layer):
+        """The dominant kernel: partitioned attention of one layer."""
+        c, sh = self.cases[layer], self.shape
+        pa.decode_partitions(c.q, c.k_cache, c.v_cache, self.bt, self.ctx, sh.scale,
+                             self.outs[layer], self.part, self.ws, getattr(c, "k_scale", None),
+                             getattr(c, "v_scale", None))
 
     def kv_bytes_per_layer(self) -> int:
         return W.kv_bytes_per_layer_step(self.shape, self.layout.context_lens.tolist())
@@ -173,6 +174,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=W.LLAMA2_7B.name, choices=sorted(W.SHAPES))
     ap.add_argument("--layers", type=int, default=0, help="0: the workload's own layer count")
+    ap.add_argument("--partition-tokens", type=int, default=0,
+                    help="0: the library's own plan (what pa_paged_decode_attention runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-kernel", type=int, default=0,
@@ -196,24 +199,35 @@ def main():
 
     shape = W.SHAPES[args.workload]
     layers = args.layers or shape.layers
-    b = Bench(shape, layers, dev)
+    b = Bench(shape, layers, dev, args.partition_tokens)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         b.step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-              for _ in range(layers * args.steps)]
+    # Timed region: K whole steps, bracketed by events on torch's current
+    # stream, which is the stream the binding hands to every launch.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for k in range(args.steps):
-        b.step(events[k * layers:(k + 1) * layers])
+    for _ in range(args.steps):
+        b.step()
     end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    kernel_ms = sum(e0.elapsed_time(e1) for e0, e1 in events) / len(events)
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # The dominant kernel's average launch duration: the same launches (every
+    # layer, K times) back to back between two events, so that per-launch
+    # event overhead does not inflate it.
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    k0.record()
+    for _ in range(args.steps):
+        for layer in range(layers):
+            b.attend(layer)
+    k1.record()
+    torch.cuda.synchronize()
+    kernel_ms = k0.elapsed_time(k1) / (args.steps * layers)
 
     kv_step = b.kv_bytes_per_layer() * layers
     value = kv_step / (ms_step / 1e3) / 1e9

@@ -22,7 +22,11 @@ __all__ = [
     "gather_kv", "abi_version",
 ]
 
-LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+# PA_LIBRARY_PATH may name another build of the same library (e.g. a variant
+# under test); by default the in-tree build next to this file is loaded.
+LIBRARY_PATH = os.environ.get(
+    "PA_LIBRARY_PATH",
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so"))
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int8: 3}
 CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 

@@ -263,8 +263,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(const Deco
       const size_t off = row * ROWB + (size_t)lcol * 16;
       const bool valid = !PARTIAL || r < nvalid;
       if (valid) {
-        kf[j] = load16(kbase + off);
-        vf[j] = load16(vbase + off);
+        kf[j] = load16_stream(kbase + off);
+        vf[j] = load16_stream(vbase + off);
       } else {
         kf[j] = u32x4{0, 0, 0, 0};
         vf[j] = u32x4{0, 0, 0, 0};
