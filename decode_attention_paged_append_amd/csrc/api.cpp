@@ -64,6 +64,7 @@ constexpr int32_t kTargetWorkgroups = 2048;  // ~8 resident per CU on 256 CUs
 constexpr int32_t kMinPartitionTokens = 256;
 
 struct Plan {
+  bool mfma = false;      // matrix-core kernel (grouped-query heads)
   int32_t gc = 1;         // query heads per workgroup
   int32_t chunks = 1;     // workgroups per KV head (group / gc)
   int32_t tile = 0;       // positions per tile
@@ -101,7 +102,16 @@ pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_head
   if (requested < 0) return fail(PA_ERR_INVALID_ARG, "partition_tokens %d < 0", requested);
   Plan p;
   const int32_t group = num_q_heads / c->num_kv_heads;
-  p.gc = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+  // Four or more query heads per KV head: the score and value products are
+  // dense enough for the matrix cores (fp16 / bf16 / int8 caches, blocks of
+  // 16 or 32).  Otherwise the vector-ALU kernel, up to 8 heads per workgroup.
+  const int32_t gc_mfma = group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : 0;
+  if (c->dtype != PA_F32 && (c->block_size == 16 || c->block_size == 32) && gc_mfma >= 4) {
+    p.mfma = true;
+    p.gc = gc_mfma;
+  } else {
+    p.gc = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+  }
   p.chunks = group / p.gc;
   p.tile = pa::tile_tokens(elem_bytes(c->dtype), c->head_dim, c->block_size);
   const int64_t max_tok = (int64_t)max_blocks * c->block_size;
@@ -165,6 +175,16 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
   p.num_parts = plan.num_parts;
   p.scale_log2 = scale * pa::kLog2e;
   hipError_t e;
+  const int D = cache->head_dim, BS = cache->block_size;
+  if (plan.mfma) {
+    switch (cache->dtype) {
+      case PA_F16: e = pa::launch_mfma_f16(p, D, BS, plan.gc, num_seqs, stream); break;
+      case PA_BF16: e = pa::launch_mfma_bf16(p, D, BS, plan.gc, num_seqs, stream); break;
+      case PA_I8: e = pa::launch_mfma_i8(p, D, BS, plan.gc, num_seqs, stream); break;
+      default: return fail(PA_ERR_UNSUPPORTED, "dtype %d", cache->dtype);
+    }
+    return hip_status(e, "decode partitions launch");
+  }
   switch (cache->dtype) {
     case PA_F32: e = pa::launch_decode_f32(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
     case PA_F16: e = pa::launch_decode_f16(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;

@@ -8,4 +8,9 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int head_dim, int bs, int g
   return launch_fmt<Fmt::BF16>(p, head_dim, bs, gc, num_seqs, stream);
 }
 
+hipError_t launch_mfma_bf16(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                           hipStream_t stream) {
+  return launch_mfma_fmt<Fmt::BF16>(p, head_dim, bs, gc, num_seqs, stream);
+}
+
 }  // namespace pa

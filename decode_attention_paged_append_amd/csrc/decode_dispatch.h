@@ -2,7 +2,7 @@
 // instance of the decode kernel for one cache format (internal header).
 #pragma once
 
-#include "decode_kernel.h"
+#include "decode_mfma.h"
 
 namespace pa {
 
@@ -47,6 +47,44 @@ static hipError_t launch_fmt(const DecodeParams& p, int head_dim, int bs, int gc
     default: return hipErrorInvalidValue;
   }
 }
+
+// ---- matrix-core kernel for grouped-query heads (fp16 / bf16 / int8 caches,
+// block size 16 or 32, 4..16 query heads per workgroup)
+template <Fmt F, int D, int BS, int GC>
+static hipError_t launch_mfma_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
+  const dim3 grid((unsigned)p.num_parts, (unsigned)(p.num_kv_heads * p.head_chunks),
+                  (unsigned)num_seqs);
+  hipLaunchKernelGGL((decode_mfma_kernel<F, D, BS, GC, kDecodeWaves>), grid,
+                     dim3(kDecodeWaves * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <Fmt F, int D, int BS>
+static hipError_t launch_mfma_gc(const DecodeParams& p, int gc, int num_seqs, hipStream_t stream) {
+  switch (gc) {
+    case 4: return launch_mfma_one<F, D, BS, 4>(p, num_seqs, stream);
+    case 8: return launch_mfma_one<F, D, BS, 8>(p, num_seqs, stream);
+    case 16: return launch_mfma_one<F, D, BS, 16>(p, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <Fmt F>
+static hipError_t launch_mfma_fmt(const DecodeParams& p, int head_dim, int bs, int gc,
+                                  int num_seqs, hipStream_t stream) {
+  if (head_dim == 128 && bs == 16) return launch_mfma_gc<F, 128, 16>(p, gc, num_seqs, stream);
+  if (head_dim == 128 && bs == 32) return launch_mfma_gc<F, 128, 32>(p, gc, num_seqs, stream);
+  if (head_dim == 64 && bs == 16) return launch_mfma_gc<F, 64, 16>(p, gc, num_seqs, stream);
+  if (head_dim == 64 && bs == 32) return launch_mfma_gc<F, 64, 32>(p, gc, num_seqs, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma_f16(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                           hipStream_t stream);
+hipError_t launch_mfma_bf16(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                            hipStream_t stream);
+hipError_t launch_mfma_i8(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                          hipStream_t stream);
 
 hipError_t launch_decode_f32(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                              hipStream_t stream);

@@ -1,0 +1,358 @@
+// decode_mfma.h -- grouped-query paged decode attention on the matrix cores.
+//
+// Same computation and same partials as decode_partition_kernel (phase 1 of
+// the decode: "KV cache: the engine behind fast LLM inference", "Concept" and
+// step 3; online softmax per the guide's "Flash attention: don't build the
+// giant matrix"), for GQA groups of 4..16 query heads per KV head ("How much
+// memory" on the KV-cache visualization page).  With several query heads per
+// key row the vector-ALU path spends ~4G VALU instructions per cached element,
+// more than the HBM time; here both products are dense contractions and run
+// as MFMA:
+//
+//   S^T[tok][head] = K[tok][:] . Q[head][:]      v_mfma_f32_16x16x32_{f16,bf16}
+//   O^T[dim][head] += V^T[dim][tok] . P^T[tok][head]  v_mfma_f32_16x16x16_{f16,bf16}
+//
+// A tile is 16 consecutive positions of one block; each wave of the
+// workgroup takes every NW-th tile of the partition.  Lane l = 16g + n.
+//
+//  * K arrives through fully coalesced 16-byte loads (rows of the block are
+//    contiguous), goes to a per-wave LDS tile whose 16-byte chunks are XOR-
+//    swizzled by row, and is read back in the MFMA A layout (lane l: row n,
+//    8 consecutive dims of k-group g) without bank conflicts.
+//  * S^T comes out with lane l holding tokens 4g..4g+3 of head n: exactly the
+//    B operand P^T of the value product, so the softmax weights never move.
+//  * V needs no LDS: lane l loads tokens 4g..4g+3 of its own dims n*D/16..;
+//    packing one dim of those 4 tokens gives the A operand of MFMA e directly
+//    when MFMA e's row r stands for dim r*D/16 + e.  Every load is still one
+//    whole row per 16 lanes (coalesced).
+//  * The online max is per head = per lane column, so the output rescale is
+//    a per-lane multiply; it is skipped when no running max moved.
+//  * P is rounded to the operand format (fp16 / bf16) for the value product;
+//    the running sum uses the fp32 weights.
+//  * int8 caches: codes become fp16 exactly (byte + 1024 under the exponent
+//    0x64, minus 1152); the key scale multiplies the score and the value
+//    scale the weight of its token.
+#pragma once
+
+#include "decode_kernel.h"
+
+namespace pa {
+
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Matrix-core operations in the operand format of a cache format.
+template <Fmt F> struct Mfma;
+template <> struct Mfma<Fmt::F16> {
+  __device__ static __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, a),
+                                                   __builtin_bit_cast(h16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h16x4, a),
+                                                  __builtin_bit_cast(h16x4, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
+    const f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, h16x2));
+  }
+};
+template <> struct Mfma<Fmt::BF16> {
+  __device__ static __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
+    const f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  }
+};
+
+// Four int8 codes -> four exact fp16 values (two words, element order kept).
+__device__ __forceinline__ u32x2 codes4_to_f16(uint32_t w) {
+  h16x2 lo, hi;
+  Frag<Fmt::I8>::codes_to_half2(w, lo, hi);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+// Heads per workgroup (GC, padded to 16 in the MFMA) x NW waves.
+template <Fmt F, int D, int BS, int GC, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void decode_mfma_kernel(const DecodeParams p) {
+  constexpr bool kInt8 = F == Fmt::I8;
+  constexpr Fmt OF = kInt8 ? Fmt::F16 : F;      // MFMA operand format
+  using MM = Mfma<OF>;
+  constexpr int EB = FmtInfo<F>::bytes;         // cache element bytes
+  constexpr int TT = 16;                        // positions per tile
+  constexpr int ROWB = D * EB;                  // cache bytes per row
+  constexpr int K_LOADS = TT * ROWB / 1024;     // 1 KiB wave-loads per K tile
+  constexpr int K_LPR = ROWB / 16;              // lanes per row in a K load
+  constexpr int K_RPL = kWave / K_LPR;          // rows per K load
+  constexpr int CHUNKS = D / 8;                 // 16-byte chunks per fp16 row in LDS
+  constexpr int VW = ROWB / 16;                 // V bytes per lane per row (16, 8 or 4)
+  constexpr int VE = D / 16;                    // dims per lane = value MFMAs per tile
+  constexpr int QKS = D / 32;                   // 16x16x32 MFMAs per score tile
+  static_assert(BS % TT == 0, "a tile lies inside one block");
+  static_assert(GC >= 1 && GC <= 16, "at most 16 heads per workgroup");
+  static_assert(K_LOADS >= 1 && K_RPL * K_LOADS == TT, "K tile = whole wave-loads");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y / p.head_chunks;
+  const int chunk = blockIdx.y - kvh * p.head_chunks;
+  const int s = blockIdx.z;
+  const int h0 = kvh * p.group + chunk * GC;
+  const size_t out_row0 = (size_t)s * p.num_q_heads + h0;
+
+  const int ctx = p.context_lens[s];
+  const bool single = p.num_parts == 1;
+  const int tok0 = part * p.part_tokens;
+  const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
+  if (bad_ctx || tok0 >= ctx) {
+    if (single) {
+      const float fill = bad_ctx ? __builtin_nanf("") : 0.0f;
+      for (int i = threadIdx.x; i < GC * D; i += NW * kWave)
+        store_out<F>(p.out, out_row0 * D + i, fill);
+    }
+    return;
+  }
+  const int tok_end = min(ctx, tok0 + p.part_tokens);
+  const int ntiles = (tok_end - tok0 + TT - 1) / TT;
+  const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
+
+  // B operand of the score product: Q^T, lane (g, n) holds head n's dims
+  // 32c + 8g .. +8 (zero for padding heads).
+  u32x4 qb[QKS];
+#pragma unroll
+  for (int c = 0; c < QKS; ++c) {
+    qb[c] = u32x4{0, 0, 0, 0};
+    if (n < GC)
+      qb[c] = *(const u32x4*)((const char*)p.q + ((out_row0 + n) * D + 32 * c + 8 * g) * 2);
+  }
+
+  float m = kMaxInit;  // running max of head n (log2 units), same in all g
+  float lsum = 0.0f;   // this lane's share of head n's running sum
+  f32x4 o[VE];         // O^T: rows dim (D/16)*(4g+i) + e, column head n
+#pragma unroll
+  for (int e = 0; e < VE; ++e) o[e] = f32x4{0, 0, 0, 0};
+  bool bad_block = false;
+
+  // LDS: the per-wave K tiles during the loop, the wave partials after it.
+  constexpr int KTILE_BYTES = TT * D * 2;
+  constexpr int ACC_BYTES = GC * D * 4;
+  constexpr int REGION = KTILE_BYTES > ACC_BYTES ? KTILE_BYTES : ACC_BYTES;
+  __shared__ __attribute__((aligned(16))) char s_mem[NW * REGION];
+  __shared__ float s_ml[NW][GC][2];
+  u32x4* const ktile = (u32x4*)(s_mem + wave * REGION);
+
+  const char* __restrict__ kbase = (const char*)p.k_cache;
+  const char* __restrict__ vbase = (const char*)p.v_cache;
+  const int blk0 = tok0 / BS;
+  const int nblk = (tok_end + BS - 1) / BS - blk0;
+  int ids = 0;
+  int ids_base = -kWave;
+
+  auto tile = [&](const int t, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    const int ttok = tok0 + t * TT;
+    const int nvalid = tok_end - ttok;
+    const int rel = ttok / BS - blk0;  // block of the tile, from the partition's first
+    if (rel >= ids_base + kWave) {
+      ids_base = rel & ~(kWave - 1);
+      const int bi = ids_base + lane;
+      ids = bi < nblk ? table[blk0 + bi] : 0;
+    }
+    int phys = __builtin_amdgcn_readlane(ids, rel - ids_base);
+    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    bad_block |= !ok;
+    phys = ok ? phys : 0;
+    const size_t row0 = ((size_t)phys * p.num_kv_heads + kvh) * BS + ttok % BS;
+    const char* kt = kbase + row0 * ROWB;
+    const char* vt = vbase + row0 * ROWB;
+
+    // ---- loads: K (coalesced), V (token 4g+j, dims of lane n), int8 scales
+    u32x4 kraw[K_LOADS];
+#pragma unroll
+    for (int j = 0; j < K_LOADS; ++j) {
+      const int r = j * K_RPL + lane / K_LPR;
+      kraw[j] = u32x4{0, 0, 0, 0};
+      if (!PARTIAL || r < nvalid) kraw[j] = load16_stream(kt + j * 1024 + lane * 16);
+    }
+    uint32_t vraw[4][VW / 4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * g + j;
+      const char* src = vt + (size_t)r * ROWB + n * VW;
+      const bool valid = !PARTIAL || r < nvalid;
+      if constexpr (VW == 16) {
+        u32x4 v = valid ? load16_stream(src) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vraw[j][w] = v[w];
+      } else if constexpr (VW == 8) {
+        u32x2 v = valid ? __builtin_nontemporal_load((const u32x2*)src) : u32x2{0, 0};
+        vraw[j][0] = v[0];
+        vraw[j][1] = v[1];
+      } else {
+        vraw[j][0] = valid ? __builtin_nontemporal_load((const uint32_t*)src) : 0u;
+      }
+    }
+    float ksc[4], vsc[4];
+    if constexpr (kInt8) {
+      // scales of tokens 4g..4g+3: 8 contiguous bytes
+      const size_t srow = row0 + 4 * g;
+      const bool any = !PARTIAL || 4 * g < nvalid;
+      const u32x2 kw = any ? *(const u32x2*)(p.k_scale + srow) : u32x2{0, 0};
+      const u32x2 vw = any ? *(const u32x2*)(p.v_scale + srow) : u32x2{0, 0};
+      ksc[0] = f16_lo(kw[0]); ksc[1] = f16_hi(kw[0]); ksc[2] = f16_lo(kw[1]); ksc[3] = f16_hi(kw[1]);
+      vsc[0] = f16_lo(vw[0]); vsc[1] = f16_hi(vw[0]); vsc[2] = f16_lo(vw[1]); vsc[3] = f16_hi(vw[1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (PARTIAL && 4 * g + i >= nvalid) ksc[i] = vsc[i] = 0.0f;  // never read past the context
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- K tile -> LDS (fp16/bf16 halves), chunk c of row r at c ^ (r % CHUNKS)
+#pragma unroll
+    for (int j = 0; j < K_LOADS; ++j) {
+      const int r = j * K_RPL + lane / K_LPR;
+      if constexpr (kInt8) {
+        const int c0 = 2 * (lane % K_LPR);
+        const u32x2 a = codes4_to_f16(kraw[j][0]), b = codes4_to_f16(kraw[j][1]);
+        const u32x2 c = codes4_to_f16(kraw[j][2]), d = codes4_to_f16(kraw[j][3]);
+        ktile[r * CHUNKS + (c0 ^ (r % CHUNKS))] = u32x4{a[0], a[1], b[0], b[1]};
+        ktile[r * CHUNKS + ((c0 + 1) ^ (r % CHUNKS))] = u32x4{c[0], c[1], d[0], d[1]};
+      } else {
+        const int c0 = lane % K_LPR;
+        ktile[r * CHUNKS + (c0 ^ (r % CHUNKS))] = kraw[j];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- scores: S^T = K . Q^T, lane (g, n): tokens 4g+i of head n
+    f32x4 sacc = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < QKS; ++c) {
+      const u32x4 a = ktile[n * CHUNKS + ((4 * c + g) ^ (n % CHUNKS))];
+      sacc = MM::qk(a, qb[c], sacc);
+    }
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = kInt8 ? sacc[i] * (ksc[i] * p.scale_log2) : sacc[i] * p.scale_log2;
+      if (PARTIAL && 4 * g + i >= nvalid) z[i] = -__builtin_inff();
+    }
+    float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const bool moved = mn > m;
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    float pw[4];
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] = fast_exp2(z[i] - mn);
+      ps += pw[i];
+    }
+    lsum = fmaf(lsum, alpha, ps);
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[e] *= alpha;
+    }
+    if constexpr (kInt8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[i] *= vsc[i];
+    }
+    const u32x2 pb = {MM::pack(pw[0], pw[1]), MM::pack(pw[2], pw[3])};
+
+    // ---- values: O^T += V^T . P^T, MFMA e uses dim (D/16)*row + e
+    uint32_t vh[4][VE / 2];  // fp16/bf16 words of tokens 4g+j, dims of lane n
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (kInt8) {
+#pragma unroll
+        for (int w = 0; w < VW / 4; ++w) {
+          const u32x2 h = codes4_to_f16(vraw[j][w]);
+          vh[j][2 * w] = h[0];
+          vh[j][2 * w + 1] = h[1];
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < VE / 2; ++w) vh[j][w] = vraw[j][w];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const int w = e >> 1;
+      const u32x2 a = {__builtin_amdgcn_perm(vh[1][w], vh[0][w], sel),
+                       __builtin_amdgcn_perm(vh[3][w], vh[2][w], sel)};
+      o[e] = MM::pv(a, pb, o[e]);
+    }
+  };
+
+  for (int t = wave; t < ntiles; t += NW) {
+    if ((t + 1) * TT <= tok_end - tok0) tile(t, std::false_type{});
+    else tile(t, std::true_type{});
+  }
+
+  // ---- merge: sum the lanes' shares of l, then the waves through LDS
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  __syncthreads();  // every wave is done with its K tile region
+  float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][D]
+  if (n < GC) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_acc[n * D + (D / 16) * (4 * g + i) + e] = o[e][i];
+    }
+    if (g == 0) {
+      s_ml[wave][n][0] = m;
+      s_ml[wave][n][1] = lsum;
+    }
+  }
+  const bool bad = __syncthreads_or(bad_block ? 1 : 0) != 0;
+  for (int i = threadIdx.x; i < GC * D; i += NW * kWave) {
+    const int h = i / D;
+    const int d = i - h * D;
+    float M = s_ml[0][h][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h][0]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float a = fast_exp2(s_ml[w][h][0] - M);
+      L = fmaf(a, s_ml[w][h][1], L);
+      acc = fmaf(a, ((const float*)(s_mem + w * REGION))[h * D + d], acc);
+    }
+    if (bad) M = L = acc = __builtin_nanf("");
+    if (single) {
+      store_out<F>(p.out, (out_row0 + h) * D + d, acc / L);
+    } else {
+      const size_t slot = (out_row0 + h) * p.num_parts + part;
+      p.part_o[slot * D + d] = acc;
+      if (d == 0) {
+        p.part_ml[2 * slot] = M;
+        p.part_ml[2 * slot + 1] = L;
+      }
+    }
+  }
+}
+
+}  // namespace pa
