@@ -60,7 +60,15 @@ pa_status check_cache(const pa_cache_desc* c) {
 
 // ------------------------------------------------------------------ plan
 
-constexpr int32_t kTargetWorkgroups = 2048;  // ~8 resident per CU on 256 CUs
+// Partition plan, measured on MI355X (256 CUs):
+//  * vector-ALU kernel (64 VGPRs, 8 waves/SIMD): ~2048 workgroups (8 per CU),
+//    partitions of at least 256 positions;
+//  * matrix-core kernel (3 waves/SIMD): as few partitions as keep >= 512
+//    workgroups (2 per CU) -- its per-workgroup prologue and merge cost more
+//    than the imbalance of long partitions (Llama-2-70B's ragged batch runs
+//    fastest as one partition per sequence).
+constexpr int32_t kTargetWorkgroups = 2048;
+constexpr int32_t kTargetWorkgroupsMfma = 512;
 constexpr int32_t kMinPartitionTokens = 256;
 
 struct Plan {
@@ -125,7 +133,8 @@ pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_head
     // Enough workgroups to fill the chip, each wave owning whole tiles.
     const int64_t unit = (int64_t)p.tile * pa::kDecodeWaves;
     const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads * p.chunks;
-    const int64_t want_parts = (kTargetWorkgroups + units - 1) / units;
+    const int64_t target = p.mfma ? kTargetWorkgroupsMfma : kTargetWorkgroups;
+    const int64_t want_parts = (target + units - 1) / units;
     part = (max_tok + want_parts - 1) / want_parts;
     part = std::max<int64_t>(part, kMinPartitionTokens);
     part = (part + unit - 1) / unit * unit;
