@@ -63,12 +63,14 @@ pa_status check_cache(const pa_cache_desc* c) {
 // Partition plan, measured on MI355X (256 CUs):
 //  * vector-ALU kernel (64 VGPRs, 8 waves/SIMD): ~2048 workgroups (8 per CU),
 //    partitions of at least 256 positions;
-//  * matrix-core kernel (3 waves/SIMD): as few partitions as keep >= 512
-//    workgroups (2 per CU) -- its per-workgroup prologue and merge cost more
-//    than the imbalance of long partitions (Llama-2-70B's ragged batch runs
-//    fastest as one partition per sequence).
+//  * matrix-core kernel (3 waves/SIMD, two tiles in flight per wave): as few
+//    partitions as keep >= 256 workgroups (one per CU) for 16-bit caches -- its per-workgroup prologue and
+//    merge cost more than the imbalance of long partitions (Llama-2-70B's
+//    ragged batch runs fastest as one partition per sequence); int8 tiles
+//    carry half the bytes and do best with ~2048 workgroups.
 constexpr int32_t kTargetWorkgroups = 2048;
-constexpr int32_t kTargetWorkgroupsMfma = 512;
+constexpr int32_t kTargetWorkgroupsMfma = 256;
+constexpr int32_t kTargetWorkgroupsMfmaInt8 = 2048;
 constexpr int32_t kMinPartitionTokens = 256;
 
 struct Plan {
@@ -133,7 +135,8 @@ pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_head
     // Enough workgroups to fill the chip, each wave owning whole tiles.
     const int64_t unit = (int64_t)p.tile * pa::kDecodeWaves;
     const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads * p.chunks;
-    const int64_t target = p.mfma ? kTargetWorkgroupsMfma : kTargetWorkgroups;
+    const int64_t target = !p.mfma ? kTargetWorkgroups
+                           : c->dtype == PA_I8 ? kTargetWorkgroupsMfmaInt8 : kTargetWorkgroupsMfma;
     const int64_t want_parts = (target + units - 1) / units;
     part = (max_tok + want_parts - 1) / want_parts;
     part = std::max<int64_t>(part, kMinPartitionTokens);

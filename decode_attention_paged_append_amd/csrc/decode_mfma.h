@@ -100,6 +100,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   constexpr int VW = ROWB / 16;                 // V bytes per lane per row (16, 8 or 4)
   constexpr int VE = D / 16;                    // dims per lane = value MFMAs per tile
   constexpr int QKS = D / 32;                   // 16x16x32 MFMAs per score tile
+  constexpr int TPI = 2;                        // tiles fetched per loop iteration
   static_assert(BS % TT == 0, "a tile lies inside one block");
   static_assert(GC >= 1 && GC <= 16, "at most 16 heads per workgroup");
   static_assert(K_LOADS >= 1 && K_RPL * K_LOADS == TT, "K tile = whole wave-loads");
@@ -163,10 +164,20 @@ void decode_mfma_kernel(const DecodeParams p) {
   int ids = 0;
   int ids_base = -kWave;
 
-  auto tile = [&](const int t, auto partial_tag) {
+  // Raw data of one tile, as loaded.
+  struct Raw {
+    u32x4 k[K_LOADS];
+    uint32_t v[4][VW / 4];
+    float ks[4], vs[4];
+    int nvalid;  // rows of the tile inside the partition
+  };
+
+  auto fetch = [&](const int t, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
+    Raw raw;
     const int ttok = tok0 + t * TT;
     const int nvalid = tok_end - ttok;
+    raw.nvalid = nvalid;
     const int rel = ttok / BS - blk0;  // block of the tile, from the partition's first
     if (rel >= ids_base + kWave) {
       ids_base = rel & ~(kWave - 1);
@@ -182,14 +193,14 @@ void decode_mfma_kernel(const DecodeParams p) {
     const char* vt = vbase + row0 * ROWB;
 
     // ---- loads: K (coalesced), V (token 4g+j, dims of lane n), int8 scales
-    u32x4 kraw[K_LOADS];
+    u32x4* const kraw = raw.k;
 #pragma unroll
     for (int j = 0; j < K_LOADS; ++j) {
       const int r = j * K_RPL + lane / K_LPR;
       kraw[j] = u32x4{0, 0, 0, 0};
       if (!PARTIAL || r < nvalid) kraw[j] = load16_stream(kt + j * 1024 + lane * 16);
     }
-    uint32_t vraw[4][VW / 4];
+    uint32_t (*const vraw)[VW / 4] = raw.v;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * g + j;
@@ -207,7 +218,8 @@ void decode_mfma_kernel(const DecodeParams p) {
         vraw[j][0] = valid ? __builtin_nontemporal_load((const uint32_t*)src) : 0u;
       }
     }
-    float ksc[4], vsc[4];
+    float* const ksc = raw.ks;
+    float* const vsc = raw.vs;
     if constexpr (kInt8) {
       // scales of tokens 4g..4g+3: 8 contiguous bytes
       const size_t srow = row0 + 4 * g;
@@ -221,7 +233,16 @@ void decode_mfma_kernel(const DecodeParams p) {
         if (PARTIAL && 4 * g + i >= nvalid) ksc[i] = vsc[i] = 0.0f;  // never read past the context
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    return raw;
+  };
+
+  auto consume = [&](const Raw& raw, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    const int nvalid = raw.nvalid;
+    const u32x4* const kraw = raw.k;
+    const uint32_t (*const vraw)[VW / 4] = raw.v;
+    const float* const ksc = raw.ks;
+    const float* const vsc = raw.vs;
 
     // ---- K tile -> LDS (fp16/bf16 halves), chunk c of row r at c ^ (r % CHUNKS)
 #pragma unroll
@@ -306,9 +327,29 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   };
 
-  for (int t = wave; t < ntiles; t += NW) {
-    if ((t + 1) * TT <= tok_end - tok0) tile(t, std::false_type{});
-    else tile(t, std::true_type{});
+  // Every load of TPI tiles is issued before the first of them is used, so a
+  // wave keeps TPI tiles in flight (int8 tiles are half the bytes).
+  const int nfull = (tok_end - tok0) / TT;  // tiles with every row valid
+  int t = wave;
+  if constexpr (TPI == 2) {
+    for (; t + NW < nfull; t += 2 * NW) {
+      const Raw a = fetch(t, std::false_type{});
+      const Raw b = fetch(t + NW, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      consume(a, std::false_type{});
+      consume(b, std::false_type{});
+    }
+  }
+  for (; t < ntiles; t += NW) {
+    if (t < nfull) {
+      const Raw a = fetch(t, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      consume(a, std::false_type{});
+    } else {
+      const Raw a = fetch(t, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      consume(a, std::true_type{});
+    }
   }
 
   // ---- merge: sum the lanes' shares of l, then the waves through LDS
