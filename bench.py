@@ -3,8 +3,10 @@
 Default workload (the headline): Llama-2-7B layer shape, fp16, multi-head
 (32 query / 32 KV heads, head_dim 128), 16 sequences x 4096 cached
 positions, block size 16, all 32 layers' pools resident (32 GiB).  One step
-= the decode slots of the batch, then for every layer in order: append the
-new token's K/V rows, partitioned paged attention and the log-sum-exp merge.
+= for every layer in order: store the new token's K/V rows at its slot and
+attend over the paged cache (pa_decode_step: slots, append and partitioned
+attention in one launch, then the log-sum-exp merge).  --separate runs the
+same step as separate launches (slots, append, partitions, merge).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
@@ -52,8 +54,10 @@ def kernel_source_hash() -> str:
 class Bench:
     """All layers' inputs resident on the GPU, and the step that runs them."""
 
-    def __init__(self, shape: W.Shape, layers: int, dev, partition_tokens: int = 0):
+    def __init__(self, shape: W.Shape, layers: int, dev, partition_tokens: int = 0,
+                 separate: bool = False):
         self.shape, self.layers, self.dev = shape, layers, dev
+        self.separate = separate
         self.layout = W.layout_for(shape)
         lay = self.layout
         self.bt = lay.block_tables.to(dev)
@@ -70,9 +74,12 @@ class Bench:
         desc = pa.CacheDesc(lay.num_blocks, shape.num_kv_heads, shape.block_size, d,
                             pa.DTYPE_CODE[W.TORCH_DTYPE[shape.cache_dtype]])
         self.part = partition_tokens or pa.decode_partition_tokens(desc, s, hq, lay.max_blocks)
+        # the library routes >= 4 query heads per KV head with 16/32 blocks to matrix cores
+        self.mfma = (shape.cache_dtype != "f32" and shape.block_size in (16, 32)
+                     and shape.group % 4 == 0)
         self.nparts = -(-lay.max_blocks * shape.block_size // self.part)
         nbytes = pa.decode_workspace_bytes(desc, s, hq, lay.max_blocks, self.part)
-        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         self.outs = [torch.empty_like(c.q) for c in self.cases]
         self.slots = torch.empty(s, dtype=torch.int64, device=dev)
 
@@ -93,14 +100,14 @@ class Bench:
     def step(self):
         """One decode step over every layer."""
         sh = self.shape
-        if self.append:
+        fused_append = self.append and not self.int8 and not self.separate
+        if self.append and not fused_append:
             pa.decode_slot_mapping(self.bt, self.ctx, sh.block_size, out=self.slots)
         for layer, c in enumerate(self.cases):
-            ks = getattr(c, "k_scale", None)
-            vs = getattr(c, "v_scale", None)
-            if self.append:
+            if self.append and not fused_append:
                 if self.int8:
-                    pa.kv_append_int8(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache, ks, vs)
+                    pa.kv_append_int8(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache,
+                                      c.k_scale, c.v_scale)
                 else:
                     pa.kv_append(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache)
             self.attend(layer)
@@ -109,22 +116,36 @@ class Bench:
                              self.layout.max_blocks, sh.block_size, self.part, self.outs[layer])
 
     def attend(self, layer):
-        """The dominant kernel: partitioned attention of one layer."""
+        """The dominant kernel: one layer's attention-partition launch (with
+        the append fused into it for 16/32-bit caches)."""
         c, sh = self.cases[layer], self.shape
-        pa.decode_partitions(c.q, c.k_cache, c.v_cache, self.bt, self.ctx, sh.scale,
-                             self.outs[layer], self.part, self.ws, getattr(c, "k_scale", None),
-                             getattr(c, "v_scale", None))
+        out = self.outs[layer]
+        if self.fused_append:
+            pa.decode_step_partitions(c.q, c.k_new, c.v_new, c.k_cache, c.v_cache, self.bt,
+                                      self.ctx, sh.scale, out, self.part, self.ws)
+        else:
+            pa.decode_partitions(c.q, c.k_cache, c.v_cache, self.bt, self.ctx, sh.scale, out,
+                                 self.part, self.ws, getattr(c, "k_scale", None),
+                                 getattr(c, "v_scale", None))
+
+    @property
+    def fused_append(self) -> bool:
+        return self.append and not self.int8 and not self.separate
 
     def kv_bytes_per_layer(self) -> int:
         return W.kv_bytes_per_layer_step(self.shape, self.layout.context_lens.tolist())
 
     def io_bytes_per_layer(self) -> int:
-        """Algorithmic bytes of one layer's attention: cached K/V (+ scales),
-        q and out, and the block-table entries read."""
+        """Algorithmic bytes of one layer's attention launch: cached K/V
+        (+ scales), q and out, the block-table entries read, and with a fused
+        append the new rows read and written."""
         sh = self.shape
         qo = 2 * sh.num_seqs * sh.num_q_heads * sh.head_dim * W.ELEM_BYTES[sh.q_dtype]
         tables = sum(W.blocks_needed(int(c), sh.block_size) for c in self.layout.context_lens) * 4
-        return self.kv_bytes_per_layer() + qo + tables
+        new_rows = 0
+        if self.fused_append:
+            new_rows = 2 * 2 * sh.num_seqs * sh.num_kv_heads * sh.head_dim * W.ELEM_BYTES[sh.cache_dtype]
+        return self.kv_bytes_per_layer() + qo + tables + new_rows
 
 
 def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
@@ -176,6 +197,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="0: the workload's own layer count")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="0: the library's own plan (what pa_paged_decode_attention runs)")
+    ap.add_argument("--separate", action="store_true",
+                    help="separate launches for slots, append, partitions and merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-kernel", type=int, default=0,
@@ -199,7 +222,7 @@ def main():
 
     shape = W.SHAPES[args.workload]
     layers = args.layers or shape.layers
-    b = Bench(shape, layers, dev, args.partition_tokens)
+    b = Bench(shape, layers, dev, args.partition_tokens, args.separate)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         b.step()
@@ -248,9 +271,11 @@ def main():
         "data": "synthetic: seeded N(0,1) Q/K/V at the layer shape; block tables a seeded "
                 "permutation of the pool",
         "config": {
-            "workload": f"{shape.name}: {shape.description}; step = "
-                        + ("slots + per layer (append, paged attention, merge)" if b.append
-                           else "per layer (paged attention, merge)"),
+            "workload": f"{shape.name}: {shape.description}; step = per layer "
+                        + ("attention launch with the slot and append fused in, then merge"
+                           if b.fused_append
+                           else "slots, append, attention partitions, merge launches"
+                           if b.append else "attention partitions, merge launches"),
             "num_seqs": shape.num_seqs, "context_lens_sum": int(b.layout.context_lens.sum()),
             "layers": layers, "num_q_heads": shape.num_q_heads,
             "num_kv_heads": shape.num_kv_heads, "head_dim": shape.head_dim,
@@ -262,7 +287,7 @@ def main():
         "kv_bytes_per_step": kv_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_partition_kernel",
+            "kernel": "decode_mfma_kernel" if b.mfma else "decode_partition_kernel",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -18,8 +18,8 @@ import torch
 __all__ = [
     "PagedAttnError", "library", "CacheDesc", "slot_mapping", "decode_slot_mapping",
     "kv_append", "kv_append_int8", "decode_workspace_bytes", "decode_partition_tokens",
-    "paged_decode_attention", "paged_decode_attention_int8", "decode_partitions", "lse_merge",
-    "gather_kv", "abi_version",
+    "paged_decode_attention", "paged_decode_attention_int8", "decode_step", "decode_partitions",
+    "decode_step_partitions", "lse_merge", "gather_kv", "abi_version",
 ]
 
 # PA_LIBRARY_PATH may name another build of the same library (e.g. a variant
@@ -74,6 +74,9 @@ def _declare(lib):
         "pa_paged_decode_attention_int8": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
         "pa_decode_partitions": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D, P, sz, P],
         "pa_lse_merge": [P, sz, P, i32, i32, i32, i32, i32, i32, i32, P, P],
+        "pa_decode_step": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
+        "pa_decode_step_partitions": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D, P, sz,
+                                      P],
         "pa_gather_kv": [P, P, P, P, P, i32, P, i32, P, P, P, P, D, P],
     }
     for name, args in sig.items():
@@ -198,8 +201,9 @@ def decode_partition_tokens(k_cache, num_seqs, num_q_heads, max_blocks) -> int:
 
 
 def _workspace(ws, nbytes, device):
+    """The caller's workspace, or a new one of the size the plan needs."""
     if ws is None:
-        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
     return ws
 
 
@@ -249,6 +253,28 @@ def paged_decode_attention_int8(q, k_cache, v_cache, k_scale, v_scale, block_tab
     return out
 
 
+def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+                workspace=None):
+    """One decode step: store each sequence's k_new/v_new [S, Hkv, D] rows at
+    position context_lens[s]-1 inside the attention launch and attend over
+    all context_lens[s] rows (see pa_decode_step)."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    if k_new.shape != (s, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{s}, {desc.num_kv_heads}, {desc.head_dim}]")
+    need = decode_workspace_bytes(desc, s, hq, maxb)
+    ws = _workspace(workspace, need, q.device)
+    _ok(lib.pa_decode_step(
+        _dev(q, "q", k_cache.dtype, 3), _dev(k_new, "k_new", k_cache.dtype),
+        _dev(v_new, "v_new", k_cache.dtype), _dev(k_cache, "k_cache", ndim=4),
+        _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(block_tables, "block_tables", torch.int32),
+        maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
+        _dev(out, "out", k_cache.dtype), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _stream(q)), lib)
+    return out
+
+
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, out,
                       partition_tokens, workspace, k_scale=None, v_scale=None):
     """Phase 1 with an explicit partition length (see pa_decode_partitions)."""
@@ -262,6 +288,25 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, ou
         _dev(v_scale, "v_scale", torch.float16), _dev(block_tables, "block_tables", torch.int32),
         maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
         int(partition_tokens), _dev(out, "out", q_dtype), ctypes.byref(desc),
+        _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel(), _stream(q)),
+        lib)
+    return out
+
+
+def decode_step_partitions(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                           out, partition_tokens, workspace):
+    """Phase 1 of decode_step with an explicit partition length."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    if k_new.shape != (s, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{s}, {desc.num_kv_heads}, {desc.head_dim}]")
+    _ok(lib.pa_decode_step_partitions(
+        _dev(q, "q", k_cache.dtype, 3), _dev(k_new, "k_new", k_cache.dtype),
+        _dev(v_new, "v_new", k_cache.dtype), _dev(k_cache, "k_cache", ndim=4),
+        _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(block_tables, "block_tables", torch.int32),
+        maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
+        int(partition_tokens), _dev(out, "out", k_cache.dtype), ctypes.byref(desc),
         _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel(), _stream(q)),
         lib)
     return out

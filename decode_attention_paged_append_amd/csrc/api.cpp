@@ -87,6 +87,8 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace of a multi-partition plan: fp32 (max, sum) [S][Hq][P][2], then
+// fp32 unnormalized outputs [S][Hq][P][D].
 void size_workspace(Plan& p, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
   if (p.num_parts <= 1) {
     p.ml_bytes = p.o_offset = p.ws_bytes = 0;
@@ -158,7 +160,8 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
                          int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
                          int32_t num_q_heads, float scale, void* out, const pa_cache_desc* cache,
                          const Plan& plan, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+                         hipStream_t stream, const void* k_new = nullptr,
+                         const void* v_new = nullptr) {
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (cache->dtype == PA_I8 && (!k_scale || !v_scale))
@@ -186,6 +189,8 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
   p.scale_log2 = scale * pa::kLog2e;
+  p.k_new = k_new;
+  p.v_new = v_new;
   hipError_t e;
   const int D = cache->head_dim, BS = cache->block_size;
   if (plan.mfma) {
@@ -222,7 +227,8 @@ pa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
                         int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
                         int32_t num_q_heads, float scale, void* out, const pa_cache_desc* cache,
                         void* workspace, size_t workspace_bytes, hipStream_t stream,
-                        bool want_int8) {
+                        bool want_int8, const void* k_new = nullptr,
+                        const void* v_new = nullptr) {
   Plan plan;
   pa_status st = make_plan(cache, num_seqs, num_q_heads, max_blocks, 0, &plan);
   if (st != PA_OK) return st;
@@ -232,7 +238,7 @@ pa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   if (num_seqs == 0) return PA_OK;
   st = run_partitions(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks,
                       context_lens, num_seqs, num_q_heads, scale, out, cache, plan, workspace,
-                      workspace_bytes, stream);
+                      workspace_bytes, stream, k_new, v_new);
   if (st != PA_OK || plan.num_parts == 1) return st;
   const int32_t out_dtype = cache->dtype == PA_I8 ? PA_F16 : cache->dtype;
   return run_merge(plan, workspace, context_lens, num_seqs, num_q_heads, cache->head_dim,
@@ -382,6 +388,40 @@ pa_status pa_decode_partitions(const void* q, const void* k_cache, const void* v
   return run_partitions(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
                         context_lens, num_seqs, num_q_heads, scale, out, cache, plan, workspace,
                         workspace_bytes, (hipStream_t)stream);
+}
+
+pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         float scale, void* out, const pa_cache_desc* cache, void* workspace,
+                         size_t workspace_bytes, pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (cache->dtype == PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "int8 cache: use pa_kv_append_int8 + pa_paged_decode_attention_int8");
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
+  return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
+                       workspace_bytes, (hipStream_t)stream, false, k_new, v_new);
+}
+
+pa_status pa_decode_step_partitions(const void* q, const void* k_new, const void* v_new,
+                                    void* k_cache, void* v_cache, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, float scale,
+                                    int32_t partition_tokens, void* out,
+                                    const pa_cache_desc* cache, void* workspace,
+                                    size_t workspace_bytes, pa_stream_t stream) {
+  Plan plan;
+  pa_status st = make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan);
+  if (st != PA_OK) return st;
+  if (cache->dtype == PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "int8 cache: use pa_kv_append_int8 + pa_decode_partitions");
+  if (num_seqs == 0) return PA_OK;
+  if (!k_new || !v_new) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
+  return run_partitions(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                        context_lens, num_seqs, num_q_heads, scale, out, cache, plan, workspace,
+                        workspace_bytes, (hipStream_t)stream, k_new, v_new);
 }
 
 pa_status pa_lse_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

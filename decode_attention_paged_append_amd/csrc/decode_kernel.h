@@ -57,7 +57,45 @@ struct DecodeParams {
   int32_t part_tokens;      // multiple of the tile length
   int32_t num_parts;
   float scale_log2;         // scale * log2(e): scores are kept in log2 units
+  // Fused append (optional): the decoded token's K and V rows [S][Hkv][D] in
+  // the cache format.  The token sits at position context_len - 1; every
+  // workgroup whose partition holds it stores the rows into the pool before
+  // it reads the pool (identical bytes when several head chunks do so).
+  const void* k_new;
+  const void* v_new;
 };
+
+template <Fmt F>
+__device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
+  if constexpr (F == Fmt::F32) {
+    ((float*)out)[idx] = x;
+  } else if constexpr (F == Fmt::BF16) {
+    ((uint16_t*)out)[idx] = float_to_bf16_rne(x);
+  } else {  // fp16 output (also for the int8 cache)
+    ((uint16_t*)out)[idx] = float_to_f16_rne(x);
+  }
+}
+
+// Fused append: store the decoded token's K and V rows (head kvh of sequence
+// s) at its slot, table[pos / BS] * BS + pos % BS, if the block id is valid,
+// then make them visible to the whole workgroup before it reads the pool.
+// Same-CU ordering only: the stores complete (workgroup-scope release) before
+// the barrier, and no lane has read those lines yet in this launch.
+template <int ROWB, int BS, int NT>
+__device__ __forceinline__ void append_new_rows(const DecodeParams& p, const int32_t* table,
+                                                int s, int kvh, int pos) {
+  const int bid = table[pos / BS];
+  if ((unsigned)bid < (unsigned)p.num_blocks) {
+    const size_t dst = (((size_t)bid * p.num_kv_heads + kvh) * BS + pos % BS) * ROWB;
+    const size_t src = ((size_t)s * p.num_kv_heads + kvh) * ROWB;
+    for (int i = threadIdx.x; i < ROWB / 16; i += NT) {
+      *(u32x4*)((char*)p.k_cache + dst + 16 * i) = load16((const char*)p.k_new + src + 16 * i);
+      *(u32x4*)((char*)p.v_cache + dst + 16 * i) = load16((const char*)p.v_new + src + 16 * i);
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+}
 
 // Per-format fragment arithmetic.  A fragment is 16 bytes of cache data.
 template <Fmt F> struct Frag;
@@ -147,19 +185,28 @@ template <> struct Frag<Fmt::I8> {
   }
 };
 
-template <Fmt F>
-__device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
-  if constexpr (F == Fmt::F32) {
-    ((float*)out)[idx] = x;
-  } else if constexpr (F == Fmt::BF16) {
-    ((uint16_t*)out)[idx] = float_to_bf16_rne(x);
-  } else {  // fp16 output (also for the int8 cache)
-    ((uint16_t*)out)[idx] = float_to_f16_rne(x);
+
+// Result of one workgroup for one query head row of one sequence: final when
+// the partition is the sequence's only one, else a partial (running max M in
+// log2 units, sum L, unnormalized output) for the log-sum-exp merge.
+template <Fmt F, int D>
+__device__ __forceinline__ void store_result(const DecodeParams& p, bool direct, size_t row,
+                                             int part, int d, float M, float L, float o) {
+  if (direct) {
+    store_out<F>(p.out, row * D + d, o / L);
+  } else {
+    const size_t slot = row * p.num_parts + part;
+    p.part_o[slot * D + d] = o;
+    if (d == 0) {
+      p.part_ml[2 * slot] = M;
+      p.part_ml[2 * slot + 1] = L;
+    }
   }
 }
 
 template <Fmt F, int D, int BS, int GC, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(GC == 1 ? 8 : GC == 2 ? 4 : 1, 8)))
+void decode_partition_kernel(const DecodeParams p) {
   using FR = Frag<F>;
   constexpr int CB = FmtInfo<F>::bytes;       // bytes per cache element
   constexpr int QB = FmtInfo<F>::q_bytes;     // bytes per query element
@@ -200,6 +247,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(const Deco
   const int tok_end = min(ctx, tok0 + p.part_tokens);
   const int ntiles = (tok_end - tok0 + TT - 1) / TT;
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
+  // Fused append: the decoded token (position ctx-1) is this partition's last
+  // row when tok_end == ctx.
+  if (!kInt8 && p.k_new != nullptr && tok_end == ctx)
+    append_new_rows<ROWB, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
 
   const int lrow = lane / LR;  // row of this lane inside a wave-load
   const int lcol = lane % LR;  // 16-byte column of this lane inside a row
@@ -374,19 +425,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(const Deco
       L = fmaf(a, s_ml[w][g][1], L);
       o = fmaf(a, s_acc[w][g][d], o);
     }
-    if (bad) {
-      M = L = o = __builtin_nanf("");
-    }
-    if (single) {
-      store_out<F>(p.out, (out_row0 + g) * D + d, o / L);
-    } else {
-      const size_t slot = (out_row0 + g) * p.num_parts + part;
-      p.part_o[slot * D + d] = o;
-      if (d == 0) {
-        p.part_ml[2 * slot] = M;
-        p.part_ml[2 * slot + 1] = L;
-      }
-    }
+    if (bad) M = L = o = __builtin_nanf("");
+    store_result<F, D>(p, single, out_row0 + g, part, d, M, L, o);
   }
 }
 

@@ -131,6 +131,10 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int tok_end = min(ctx, tok0 + p.part_tokens);
   const int ntiles = (tok_end - tok0 + TT - 1) / TT;
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
+  // Fused append: the decoded token (position ctx-1) is this partition's last
+  // row when tok_end == ctx.
+  if (!kInt8 && p.k_new != nullptr && tok_end == ctx)
+    append_new_rows<ROWB, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
 
   // B operand of the score product: Q^T, lane (g, n) holds head n's dims
   // 32c + 8g .. +8 (zero for padding heads).
@@ -383,16 +387,7 @@ void decode_mfma_kernel(const DecodeParams p) {
       acc = fmaf(a, ((const float*)(s_mem + w * REGION))[h * D + d], acc);
     }
     if (bad) M = L = acc = __builtin_nanf("");
-    if (single) {
-      store_out<F>(p.out, (out_row0 + h) * D + d, acc / L);
-    } else {
-      const size_t slot = (out_row0 + h) * p.num_parts + part;
-      p.part_o[slot * D + d] = acc;
-      if (d == 0) {
-        p.part_ml[2 * slot] = M;
-        p.part_ml[2 * slot + 1] = L;
-      }
-    }
+    store_result<F, D>(p, single, out_row0 + h, part, d, M, L, acc);
   }
 }
 

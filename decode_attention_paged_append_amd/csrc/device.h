@@ -93,6 +93,8 @@ __device__ __forceinline__ float group_max(float x) {
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
+
 // Cache rows are read once per decode step: non-temporal loads stream them
 // past the caches instead of evicting lines that are reused (measured: the
 // Llama-2-7B attention kernel goes from ~182 us to ~170 us per layer).

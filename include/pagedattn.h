@@ -145,7 +145,9 @@ pa_status pa_kv_append_int8(const void* k_new, const void* v_new,
  * results (running max, sum and unnormalized output) of every context
  * partition.  partition_tokens = 0 picks the library's own plan, the one
  * pa_paged_decode_attention uses; pass the same value to the phase entry
- * points below.  Pure host arithmetic; returns 0 for an invalid shape. */
+ * points below.  Pure host arithmetic; returns 0 for an invalid shape or a
+ * single-partition plan (which needs no workspace).  Contents are scratch;
+ * calls that overlap on one workspace race. */
 size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq,
                                  int32_t partition_tokens);
@@ -161,12 +163,13 @@ int32_t pa_decode_partition_tokens(const pa_cache_desc* cache, int32_t num_seqs,
  * block table ([notes] "Concept" and step 3 "Attend against the cache";
  * [viz] "PagedAttention: the cache in blocks").  The softmax runs online
  * over the cache, tile by tile, never forming the score row in memory
- * ([guide] "Flash attention: don't build the giant matrix"); long contexts
- * are split into partitions whose partial results a log-sum-exp merge
- * combines.  q, out: device [S][Hq][D] in the cache's format; fp32
- * accumulation; out rounded to nearest-even.  A sequence with length 0
- * gets zeros.  workspace: device, >= pa_decode_workspace_bytes(cache, S, Hq,
- * max_blocks_per_seq, 0) bytes, contents clobbered. */
+ * ([guide] "Flash attention: don't build the giant matrix").  Long contexts
+ * are split into partitions whose partials a second launch combines with the
+ * log-sum-exp merge (pa_decode_partitions + pa_lse_merge).  q, out: device
+ * [S][Hq][D] in the cache's format; fp32 accumulation; out rounded to
+ * nearest-even.  A sequence with length 0 gets zeros.  workspace: device,
+ * >= pa_decode_workspace_bytes(cache, S, Hq, max_blocks_per_seq, 0) bytes,
+ * contents clobbered. */
 pa_status pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                                     const int32_t* context_lens, int32_t num_seqs,
@@ -185,6 +188,25 @@ pa_status pa_paged_decode_attention_int8(const void* q, const int8_t* k_cache,
                                          const pa_cache_desc* cache, void* workspace,
                                          size_t workspace_bytes, pa_stream_t stream);
 
+/* One decode step for a fp32 / fp16 / bf16 cache: store each
+ * sequence's new K and V rows (k_new, v_new: device [S][Hkv][D] in the
+ * cache's format) at position context_lens[s] - 1, i.e. at slot
+ * block_tables[s][pos / BS] * BS + pos % BS ([notes] steps 2-4: project the
+ * new token, attend, append; [guide] "How the cache turns the loop cheap"),
+ * and compute the same attention as pa_paged_decode_attention over all
+ * context_lens[s] rows, the new one included.  The append happens inside the
+ * attention launch (each workgroup whose partition holds the new position
+ * stores the rows, then reads them back through the pool); the merge of a
+ * multi-partition plan is the second launch.  Equivalent to
+ * pa_decode_slot_mapping + pa_kv_append + pa_paged_decode_attention.
+ * Sequences of length 0 append nothing.
+ * k_cache, v_cache are updated in place; other arguments as above. */
+pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         float scale, void* out, const pa_cache_desc* cache, void* workspace,
+                         size_t workspace_bytes, pa_stream_t stream);
+
 /* Phase 1 of the above with an explicit partition length, or 0 for the
  * plan's.  The length must be a positive multiple of the tile, which is
  * max(block_size, 1024 / (head_dim * bytes per cache element)) positions
@@ -202,6 +224,17 @@ pa_status pa_decode_partitions(const void* q, const void* k_cache, const void* v
                                int32_t num_q_heads, float scale, int32_t partition_tokens,
                                void* out, const pa_cache_desc* cache, void* workspace,
                                size_t workspace_bytes, pa_stream_t stream);
+
+/* Phase 1 of pa_decode_step with an explicit partition length (as for
+ * pa_decode_partitions): the append at context_lens[s] - 1 and the
+ * partitions' attention, in one launch. */
+pa_status pa_decode_step_partitions(const void* q, const void* k_new, const void* v_new,
+                                    void* k_cache, void* v_cache, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, float scale,
+                                    int32_t partition_tokens, void* out,
+                                    const pa_cache_desc* cache, void* workspace,
+                                    size_t workspace_bytes, pa_stream_t stream);
 
 /* Phase 2: log-sum-exp merge of the partitions' partials into out
  * (max M = max_p m_p; out = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p),

@@ -100,7 +100,8 @@ def test_workspace_and_plan(lib, dtype, d, bs, tile):
     if nparts == 1:
         assert ws == 0
     else:
+        a256 = lambda x: (x + 255) // 256 * 256
         ml = s * hq * nparts * 2 * 4
-        assert ws == ((ml + 255) // 256) * 256 + s * hq * nparts * d * 4
+        assert ws == a256(ml) + s * hq * nparts * d * 4
     # an explicit partition covering the whole table needs no workspace
     assert lib.pa_decode_workspace_bytes(ctypes.byref(dd), s, hq, maxb, maxb * bs) == 0

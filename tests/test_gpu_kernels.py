@@ -305,3 +305,78 @@ def test_large_scores_stay_finite():
     # near-ties between the top scores amplify fp32 score rounding; the check is
     # that nothing overflows and the result tracks the oracle loosely
     assert torch.isfinite(out).all() and max_abs_err(out, ref) <= 1e-2
+
+
+# ---------------------------------------------------------------- fused step / merge
+
+@pytest.mark.parametrize("dtype,d,bs,hq,hkv", [
+    ("f32", 64, 4, 4, 2), ("f16", 128, 16, 32, 32), ("f16", 128, 16, 32, 8),
+    ("bf16", 128, 16, 64, 8), ("bf16", 64, 32, 8, 2), ("f16", 64, 8, 16, 1),
+    ("bf16", 128, 32, 32, 2)])
+def test_decode_step_equals_append_then_attend(dtype, d, bs, hq, hkv):
+    """One launch (append at ctx-1 + attention + in-kernel merge) gives the
+    oracle's cache bit-exactly and the oracle's attention within tolerance,
+    and agrees with the separate slot + append + attention calls (the tile
+    holding the new row takes the partial-tile code path there, so the two
+    may differ in rounding, not beyond the tolerance)."""
+    ctx = [1, bs, bs + 1, 300, 2049, 700]
+    shape, lay, case = make(dtype, hq, hkv, d, bs, ctx, seed=11, poison_new=True)
+    q, kc, vc, kn, vn, bt, ctx_t = to_dev(case.q, case.k_cache, case.v_cache, case.k_new,
+                                          case.v_new, lay.block_tables, lay.context_lens)
+    kc2, vc2 = kc.clone(), vc.clone()
+    out = torch.empty_like(q)
+    pa.decode_step(q, kn, vn, kc, vc, bt, ctx_t, shape.scale, out)
+    torch.cuda.synchronize()
+    slots = oracle.decode_slot_mapping(host(lay.block_tables), host(lay.context_lens), bs)
+    kh, vh = host(case.k_cache).copy(), host(case.v_cache).copy()
+    oracle.kv_append(host(case.k_new), host(case.v_new), slots, kh, vh, bf16=dtype == "bf16")
+    assert host(kc).tobytes() == kh.tobytes() and host(vc).tobytes() == vh.tobytes()
+    ref = oracle.paged_decode_attention(host(case.q), kh, vh, host(lay.block_tables),
+                                        host(lay.context_lens), shape.scale, bf16=dtype == "bf16")
+    assert max_abs_err(out, ref) <= TOL[dtype]
+    # the separate path on the same plan
+    pa.kv_append(kn, vn, pa.decode_slot_mapping(bt, ctx_t, bs), kc2, vc2)
+    out2 = torch.empty_like(q)
+    pa.paged_decode_attention(q, kc2, vc2, bt, ctx_t, shape.scale, out2)
+    torch.cuda.synchronize()
+    assert (out.double() - out2.double()).abs().max().item() <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [("f16", 8, 8), ("bf16", 32, 4), ("i8", 16, 4)])
+def test_library_plan_many_partitions_reused_workspace(dtype, hq, hkv):
+    """The library's own plan on long, ragged contexts (several partitions and
+    the merge launch), twice on one workspace: same bits, oracle tolerance."""
+    d, bs = 128, 16
+    ctx = [4000, 17, 2500, 0, 3999]
+    shape, lay, case = make(dtype, hq, hkv, d, bs, ctx, seed=13)
+    if dtype == "i8":
+        kq, vq, ks, vs = quantize_pool_gpu(case.k_cache.nan_to_num(0.0).to(dev()),
+                                           case.v_cache.nan_to_num(0.0).to(dev()), None)
+        okq, ovq, oks, ovs, _ = quantize_blocks_oracle(case.k_cache.nan_to_num(0.0),
+                                                      case.v_cache.nan_to_num(0.0),
+                                                      range(lay.num_blocks))
+        ref = oracle.paged_decode_attention(host(case.q), okq, ovq, host(lay.block_tables),
+                                            host(lay.context_lens), shape.scale, k_scale=oks,
+                                            v_scale=ovs)
+        kc, vc = kq, vq
+    else:
+        kc, vc = to_dev(case.k_cache, case.v_cache)
+        ks = vs = None
+        ref = decode_oracle(case.q, case.k_cache, case.v_cache, lay.block_tables,
+                            lay.context_lens, shape.scale)
+    q, bt, ctx_t = to_dev(case.q, lay.block_tables, lay.context_lens)
+    nbytes = pa.decode_workspace_bytes(kc, len(ctx), hq, lay.max_blocks)
+    assert nbytes > 0, "expected a multi-partition plan"
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev())  # garbage is fine
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(q)
+        if dtype == "i8":
+            pa.paged_decode_attention_int8(q, kc, vc, ks, vs, bt, ctx_t, shape.scale, out, ws)
+        else:
+            pa.paged_decode_attention(q, kc, vc, bt, ctx_t, shape.scale, out, ws)
+        torch.cuda.synchronize()
+        assert max_abs_err(out, ref) <= TOL[dtype]
+        assert (out[3] == 0).all()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.uint8), outs[1].view(torch.uint8))
