@@ -95,3 +95,25 @@ def test_llama3_8b_int8_quantized_decode():
                                         host(lay.context_lens), shape.scale, k_scale=oks,
                                         v_scale=ovs, pairs=pairs)
     assert max_abs_err(out, ref, pairs) <= TOL["i8"]
+
+
+@pytest.mark.parametrize("shape", [W.LLAMA2_7B, W.LLAMA3_8B], ids=lambda s: s.name)
+def test_decode_step_full_size(shape):
+    """The benchmark's step at full size: append fused into the attention
+    launch (library plan), then the merge launch."""
+    lay = W.layout_for(shape)
+    case = W.make_case(shape, lay, device=dev(), seed=3, poison=True, poison_new_slot=True)
+    kh, vh = host(case.k_cache).copy(), host(case.v_cache).copy()
+    bt, ctx = lay.block_tables.to(dev()), lay.context_lens.to(dev())
+    out = torch.empty_like(case.q)
+    pa.decode_step(case.q, case.k_new, case.v_new, case.k_cache, case.v_cache, bt, ctx,
+                   shape.scale, out)
+    torch.cuda.synchronize()
+    oslots = oracle.decode_slot_mapping(host(lay.block_tables), host(lay.context_lens),
+                                        shape.block_size)
+    oracle.kv_append(host(case.k_new), host(case.v_new), oslots, kh, vh)
+    assert same_bytes(host(case.k_cache), kh) and same_bytes(host(case.v_cache), vh)
+    pairs = sample_pairs(shape.num_seqs, shape.num_q_heads, 3)
+    ref = oracle.paged_decode_attention(host(case.q), kh, vh, host(lay.block_tables),
+                                        host(lay.context_lens), shape.scale, pairs=pairs)
+    assert max_abs_err(out, ref, pairs) <= TOL["f16"]
