@@ -188,12 +188,109 @@ def traffic_block(io_bytes: int):
     return t.get("traffic_bytes_per_launch")
 
 
+def block_pool_bench(dev, steps: int, warmup: int, cpu: bool) -> dict:
+    """The block pool at the Llama-3-8B layer shape (8 KV heads x 128, fp16,
+    block size 16): the copy-on-write kernel's bandwidth over a batch of
+    whole-block copies, and the native manager's host time per decode round
+    of 256 sequences (256 appends of one token, then the table export)."""
+    import numpy as np
+
+    hkv, bs, d, nb = 8, 16, 128, 8192
+    kc = torch.randn((nb, hkv, bs, d), device=dev).to(torch.float16)
+    vc = torch.randn_like(kc)
+    g = torch.Generator().manual_seed(1)
+    perm = torch.randperm(nb, generator=g)
+    results = {}
+    for npairs in (2048, 64):
+        pairs = torch.stack([perm[:npairs], perm[nb // 2:nb // 2 + npairs]], 1).to(
+            torch.int32).to(dev).contiguous()
+        for _ in range(warmup):
+            pa.copy_blocks(kc, vc, pairs)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = steps * 10
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            pa.copy_blocks(kc, vc, pairs)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        moved = 2 * npairs * 2 * hkv * bs * d * 2          # K and V, read + write
+        results[npairs] = (ms, moved)
+
+    # host: 256 sequences prefilled to 4096 tokens, then decode rounds
+    seqs_n, ctx0, rounds = 256, 4096, 2048
+    pool = seqs_n * (ctx0 + rounds) // bs + 64
+    m = pa.BlockManager(pool, bs)
+    seqs = [m.add() for _ in range(seqs_n)]
+    m.append([(s, ctx0) for s in seqs])
+    maxb = (ctx0 + rounds) // bs + 1
+    ids = np.array(seqs, np.int32)
+    ones = np.ones(seqs_n, np.int32)
+    t0 = time.perf_counter()
+    for _ in range(rounds):
+        m.append_arrays(ids, ones)
+        m.block_tables(ids, maxb)
+    host_us = (time.perf_counter() - t0) / rounds * 1e6
+    # forks: 32 prompts of 1000 tokens, 8 requests each sharing the prompt;
+    # the first decode round copies the 32 x 7 shared partial blocks
+    m2 = pa.BlockManager(32 * 8 * 80, bs)
+    roots = [m2.add() for _ in range(32)]
+    m2.append([(r, 1000) for r in roots])
+    kids = [m2.fork(r) for r in roots for _ in range(7)]
+    t0 = time.perf_counter()
+    _, copies = m2.append([(s, 1) for s in roots + kids])
+    fork_round_us = (time.perf_counter() - t0) * 1e6
+
+    cpu_block = None
+    if cpu:
+        from oracle import block_manager as obm
+        om = obm.BlockManager(pool, bs)
+        oseqs = [om.add() for _ in range(seqs_n)]
+        om.append([(s, ctx0) for s in oseqs])
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0 and n < rounds:
+            om.append([(s, 1) for s in oseqs])
+            n += 1
+        dt = time.perf_counter() - t0
+        cpu_block = {"value": round(dt / n * 1e6, 1), "unit": "us per decode round",
+                     "cores": 1, "kind": "oracle",
+                     "sample": f"the plain block-pool model, {n} decode rounds of 256 "
+                               f"sequences at 4096+ tokens, {dt:.1f} s"}
+    ms, moved = results[2048]
+    ms64, moved64 = results[64]
+    gbs = moved / (ms / 1e3) / 1e9
+    return {
+        "metric": "block pool: copy-on-write block copy GB/s (read + write) + host us per "
+                  "decode round",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "block pool at the Llama-3-8B layer shape (8 KV heads x 128, "
+                               "fp16, block 16); step = pa_copy_blocks of 2048 block pairs "
+                               "(K and V, 64 KiB per pair)", "pairs": 2048},
+        "copy_64_pairs": {"us": round(ms64 * 1e3, 2),
+                          "GB/s": round(moved64 / (ms64 / 1e3) / 1e9, 2)},
+        "host_us_per_decode_round": round(host_us, 2),
+        "host_decode_round": "256 sequences at 4096+ tokens: pa_bm_append of one token each, "
+                             "then pa_bm_block_tables of all 256 rows",
+        "host_us_fork_round": round(fork_round_us, 2),
+        "fork_round_copies": int(len(copies)),
+        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": moved,
+                     "avg_launch_ms": round(ms, 5)},
+        "cpu_baseline": cpu_block,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=W.LLAMA2_7B.name, choices=sorted(W.SHAPES))
+    ap.add_argument("--workload", default=W.LLAMA2_7B.name,
+                    choices=sorted(W.SHAPES) + ["block-pool"])
     ap.add_argument("--layers", type=int, default=0, help="0: the workload's own layer count")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="0: the library's own plan (what pa_paged_decode_attention runs)")
@@ -218,6 +315,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": src.numel() * 2, "copies": args.copy_kernel}))
+        return
+
+    if args.workload == "block-pool":
+        print(json.dumps(block_pool_bench(dev, args.steps, args.warmup,
+                                          not args.no_cpu_baseline)))
         return
 
     shape = W.SHAPES[args.workload]

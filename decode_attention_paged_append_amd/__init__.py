@@ -13,13 +13,15 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 __all__ = [
     "PagedAttnError", "library", "CacheDesc", "slot_mapping", "decode_slot_mapping",
     "kv_append", "kv_append_int8", "decode_workspace_bytes", "decode_partition_tokens",
     "paged_decode_attention", "paged_decode_attention_int8", "decode_step", "decode_partitions",
-    "decode_step_partitions", "lse_merge", "gather_kv", "abi_version",
+    "decode_step_partitions", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
+    "BlockManager", "copy_blocks",
 ]
 
 # PA_LIBRARY_PATH may name another build of the same library (e.g. a variant
@@ -33,6 +35,13 @@ CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 
 class PagedAttnError(RuntimeError):
     """A non-OK status from the library."""
+
+
+class OutOfBlocks(PagedAttnError):
+    """The block pool cannot hold the request (PA_ERR_OUT_OF_BLOCKS)."""
+
+
+OUT_OF_BLOCKS = 5
 
 
 class CacheDesc(ctypes.Structure):
@@ -78,6 +87,13 @@ def _declare(lib):
         "pa_decode_step_partitions": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D, P, sz,
                                       P],
         "pa_gather_kv": [P, P, P, P, P, i32, P, i32, P, P, P, P, D, P],
+        "pa_copy_blocks": [P, P, P, P, P, i32, D, P],
+        "pa_bm_create": [i32, i32, ctypes.POINTER(P)],
+        "pa_bm_add_sequence": [P, ctypes.POINTER(i32)],
+        "pa_bm_fork": [P, i32, i32, ctypes.POINTER(i32)],
+        "pa_bm_free_sequence": [P, i32],
+        "pa_bm_append": [P, P, P, i32, P, i64, P, i32, ctypes.POINTER(i32)],
+        "pa_bm_block_tables": [P, P, i32, i32, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -87,6 +103,12 @@ def _declare(lib):
     lib.pa_decode_workspace_bytes.restype = sz
     lib.pa_decode_partition_tokens.argtypes = [D, i32, i32, i32]
     lib.pa_decode_partition_tokens.restype = i32
+    lib.pa_bm_destroy.argtypes = [P]
+    lib.pa_bm_destroy.restype = None
+    for name, args in (("pa_bm_num_free_blocks", [P]), ("pa_bm_ref_count", [P, i32]),
+                       ("pa_bm_sequence_length", [P, i32])):
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = i32
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -96,7 +118,8 @@ def _declare(lib):
 
 def _ok(status: int, lib) -> None:
     if status != 0:
-        raise PagedAttnError(f"{lib.pa_status_string(status).decode()}: "
+        cls = OutOfBlocks if status == OUT_OF_BLOCKS else PagedAttnError
+        raise cls(f"{lib.pa_status_string(status).decode()}: "
                              f"{lib.pa_last_error().decode()}")
 
 
@@ -341,3 +364,106 @@ def gather_kv(k_cache, v_cache, block_tables, context_lens, k_out, v_out, k_scal
                          _dev(k_out, "k_out", k_cache.dtype), _dev(v_out, "v_out", k_cache.dtype),
                          _dev(k_scale_out, "k_scale_out"), _dev(v_scale_out, "v_scale_out"),
                          ctypes.byref(desc), _stream(k_cache)), lib)
+
+
+# ---------------------------------------------------------------- block pool
+
+def _host_i32(a, name):
+    """A contiguous int32 host array and its address (ctypes.cast, which
+    data_as uses, costs ~15 us a call; the plain address does not)."""
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data
+
+
+class BlockManager:
+    """The library's host-side block pool (pa_bm_*): block tables, context
+    lengths and slots for the append and attention calls, with shared
+    prefixes and copy-on-write.  Not thread-safe."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        lib = library()
+        handle = ctypes.c_void_p()
+        _ok(lib.pa_bm_create(num_blocks, block_size, ctypes.byref(handle)), lib)
+        self._lib, self._h = lib, handle
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pa_bm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self) -> int:
+        sid = ctypes.c_int32()
+        _ok(self._lib.pa_bm_add_sequence(self._h, ctypes.byref(sid)), self._lib)
+        return sid.value
+
+    def fork(self, parent: int, prefix: int | None = None) -> int:
+        sid = ctypes.c_int32()
+        _ok(self._lib.pa_bm_fork(self._h, parent, -1 if prefix is None else prefix,
+                                 ctypes.byref(sid)), self._lib)
+        return sid.value
+
+    def free(self, seq: int) -> None:
+        _ok(self._lib.pa_bm_free_sequence(self._h, seq), self._lib)
+
+    def append(self, requests):
+        """requests: [(seq, n_tokens)].  Returns (slots int64 [sum n], copies
+        int32 [k, 2] of (source, destination) blocks to copy first)."""
+        return self.append_arrays([r[0] for r in requests], [r[1] for r in requests])
+
+    def append_arrays(self, seqs, num_tokens):
+        """append() with the requests as two int32 arrays (sequence ids and
+        token counts)."""
+        seqs, sp = _host_i32(seqs, "seqs")
+        ntok, np_ = _host_i32(num_tokens, "num_tokens")
+        total = int(ntok[ntok > 0].sum()) if ntok.size else 0
+        slots = np.empty(max(total, 1), np.int64)
+        copies = np.empty((max(seqs.size, 1), 2), np.int32)
+        n = ctypes.c_int32()
+        _ok(self._lib.pa_bm_append(self._h, sp, np_, seqs.size,
+                                   slots.ctypes.data, slots.size,
+                                   copies.ctypes.data, copies.shape[0],
+                                   ctypes.byref(n)), self._lib)
+        return slots[:total], copies[:n.value]
+
+    def block_tables(self, seqs, max_blocks: int):
+        """(int32 [len(seqs), max_blocks] tables padded with -1, int32 lengths)."""
+        ids, ip = _host_i32(seqs, "seqs")
+        tables = np.empty((max(ids.size, 1), max_blocks), np.int32)
+        lens = np.empty(max(ids.size, 1), np.int32)
+        _ok(self._lib.pa_bm_block_tables(self._h, ip, ids.size, max_blocks,
+                                         tables.ctypes.data,
+                                         lens.ctypes.data), self._lib)
+        return tables[:ids.size], lens[:ids.size]
+
+    def num_free(self) -> int:
+        return self._lib.pa_bm_num_free_blocks(self._h)
+
+    def ref_count(self, block: int) -> int:
+        return self._lib.pa_bm_ref_count(self._h, block)
+
+    def length(self, seq: int) -> int:
+        return self._lib.pa_bm_sequence_length(self._h, seq)
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, k_scale=None, v_scale=None):
+    """Copy whole blocks (every KV head) from source to destination inside one
+    pool; block_pairs is int32 [n, 2] (a host array is moved to the GPU)."""
+    lib = library()
+    if not isinstance(block_pairs, torch.Tensor) or not block_pairs.is_cuda:
+        block_pairs = torch.as_tensor(np.ascontiguousarray(block_pairs, np.int32).reshape(-1, 2),
+                                      device=k_cache.device)
+    n = block_pairs.shape[0]
+    i8 = k_cache.dtype == torch.int8
+    desc = CacheDesc.of(k_cache)
+    _ok(lib.pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(k_scale, "k_scale", torch.float16) if i8 else None,
+                           _dev(v_scale, "v_scale", torch.float16) if i8 else None,
+                           _dev(block_pairs, "block_pairs", torch.int32, 2), n,
+                           ctypes.byref(desc), _stream(k_cache)), lib)

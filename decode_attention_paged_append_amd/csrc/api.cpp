@@ -9,8 +9,9 @@
 #include "pagedattn.h"
 #include "decode_dispatch.h"
 #include "kv_ops.h"
+#include "status.h"
 
-namespace {
+namespace pa {
 
 thread_local std::string g_last_error;
 
@@ -23,6 +24,13 @@ pa_status fail(pa_status st, const char* fmt, ...) {
   g_last_error = buf;
   return st;
 }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+using pa::g_last_error;
 
 pa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PA_OK;
@@ -256,6 +264,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported shape or format";
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP error";
+    case PA_ERR_OUT_OF_BLOCKS: return "out of pool blocks";
     default: return "unknown status";
   }
 }
@@ -471,6 +480,26 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
                                          cache->num_blocks, cache->num_kv_heads,
                                          cache->block_size, row_bytes, (hipStream_t)stream),
                     "gather launch");
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                         const int32_t* block_pairs, int32_t num_pairs,
+                         const pa_cache_desc* cache, pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs %d < 0", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  const bool i8 = cache->dtype == PA_I8;
+  if (!k_cache || !v_cache || !block_pairs || (i8 && (!k_scale || !v_scale)))
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  const int32_t row_bytes = cache->head_dim * elem_bytes(cache->dtype);
+  if ((int64_t)cache->num_kv_heads * cache->block_size * row_bytes > ((int64_t)1 << 29))
+    return fail(PA_ERR_UNSUPPORTED, "blocks above 512 MiB per tensor");
+  return hip_status(pa::launch_copy_blocks(k_cache, v_cache, i8 ? k_scale : nullptr,
+                                           i8 ? v_scale : nullptr, block_pairs, num_pairs,
+                                           cache->num_blocks, cache->num_kv_heads,
+                                           cache->block_size, row_bytes, (hipStream_t)stream),
+                    "copy_blocks launch");
 }
 
 }  // extern "C"

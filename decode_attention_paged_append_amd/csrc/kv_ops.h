@@ -27,6 +27,10 @@ hipError_t launch_gather_kv(const void* k_cache, const void* v_cache, const void
                             void* v_out, void* k_scale_out, void* v_scale_out,
                             int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                             int32_t row_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                              const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
+                              int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,
+                              hipStream_t stream);
 
 // Log-sum-exp merge of partition partials (lse_merge.hip).
 hipError_t launch_lse_merge(const float* part_ml, const float* part_o,

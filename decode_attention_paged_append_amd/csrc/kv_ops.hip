@@ -240,4 +240,53 @@ hipError_t launch_gather_kv(const void* k_cache, const void* v_cache, const void
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- block copy
+
+// Copy-on-write of shared blocks: one workgroup moves one 16 KiB chunk of a
+// (source, destination) pair's K or V rows (every KV head of a block is one
+// contiguous run), plus, in chunk 0, the pair's int8 scales.
+constexpr int64_t kCopyChunkPieces = 1024;  // 16-byte pieces per workgroup
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, uint16_t* __restrict__ k_scale,
+    uint16_t* __restrict__ v_scale, const int32_t* __restrict__ pairs, int32_t num_blocks,
+    int64_t block_pieces, int32_t scale_elems, int32_t chunks) {
+  const int64_t pair = blockIdx.x;
+  const int32_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int which = (int)blockIdx.y / chunks;  // 0: K, 1: V
+  const int64_t chunk = (int64_t)blockIdx.y - (int64_t)which * chunks;
+  u32x4* cache = which ? v_cache : k_cache;
+  const u32x4* from = cache + (int64_t)src * block_pieces;
+  u32x4* to = cache + (int64_t)dst * block_pieces;
+  const int64_t begin = chunk * kCopyChunkPieces;
+  const int64_t end = begin + kCopyChunkPieces < block_pieces ? begin + kCopyChunkPieces : block_pieces;
+  int64_t i = begin + threadIdx.x;
+  for (; i + 3 * 256 < end; i += 4 * 256) {
+    const u32x4 a = from[i], b = from[i + 256], c = from[i + 512], d = from[i + 768];
+    to[i] = a;
+    to[i + 256] = b;
+    to[i + 512] = c;
+    to[i + 768] = d;
+  }
+  for (; i < end; i += 256) to[i] = from[i];
+  uint16_t* scales = which ? v_scale : k_scale;
+  if (chunk == 0 && scales) {
+    for (int32_t j = threadIdx.x; j < scale_elems; j += 256)
+      scales[(int64_t)dst * scale_elems + j] = scales[(int64_t)src * scale_elems + j];
+  }
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                              const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
+                              int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,
+                              hipStream_t stream) {
+  const int64_t block_pieces = (int64_t)num_kv_heads * block_size * (row_bytes / 16);
+  const int32_t chunks = (int32_t)((block_pieces + kCopyChunkPieces - 1) / kCopyChunkPieces);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2 * chunks), dim3(256), 0, stream,
+                     (u32x4*)k_cache, (u32x4*)v_cache, (uint16_t*)k_scale, (uint16_t*)v_scale,
+                     pairs, num_blocks, block_pieces, num_kv_heads * block_size, chunks);
+  return hipGetLastError();
+}
+
 }  // namespace pa

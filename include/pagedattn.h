@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum {
   PA_F32 = 0,
@@ -77,7 +77,8 @@ typedef enum {
   PA_ERR_INVALID_ARG = 1, /* null pointer, negative size, Hq % Hkv != 0 ... */
   PA_ERR_UNSUPPORTED = 2, /* head_dim, block_size or dtype outside the list */
   PA_ERR_WORKSPACE = 3,   /* workspace smaller than pa_decode_workspace_bytes */
-  PA_ERR_HIP = 4          /* a HIP launch reported an error */
+  PA_ERR_HIP = 4,         /* a HIP launch reported an error */
+  PA_ERR_OUT_OF_BLOCKS = 5 /* the block pool cannot hold the request */
 } pa_status;
 
 /* Shape and element format of one layer's block pool (K and V alike). */
@@ -261,6 +262,80 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
                        int32_t num_seqs, void* k_out, void* v_out, void* k_scale_out,
                        void* v_scale_out, const pa_cache_desc* cache, pa_stream_t stream);
+
+/* ---------------------------------------------------------------- block pool */
+
+/* Host-side owner of one block pool: which pool block holds which positions
+ * of which sequence.  It produces the block tables, context lengths and slot
+ * numbers the calls above consume, following the paging rules of [viz]
+ * "PagedAttention: the cache in blocks" and [guide] "Paging":
+ *   - a sequence takes a new block only when its last block is full, so at
+ *     most one of its blocks is partly filled;
+ *   - a freed sequence returns its blocks to the pool at once;
+ *   - a fork shares its parent's blocks for a prefix, by reference count;
+ *   - a block held by more than one sequence is copied only when one of them
+ *     writes into it: the writer moves onto a fresh block, and the append
+ *     reports the (source, destination) pair, which the caller must copy with
+ *     pa_copy_blocks in every layer's pool before appending to the slots.
+ * The manager lives in host memory only and makes no HIP call.  One manager
+ * serves all layers of a model (they share the tables).  It is not
+ * thread-safe: calls on one manager must not overlap.  Sequence ids are small
+ * integers chosen by the manager; the id of a freed sequence may be reused.
+ * Which free block is handed out is unspecified. */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A pool of num_blocks blocks of block_size slots (block_size in {4, 8, 16,
+ * 32}).  *out receives the manager, or NULL on failure. */
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, pa_block_manager** out);
+void pa_bm_destroy(pa_block_manager* bm);  /* NULL is ignored */
+
+/* A new, empty sequence; its id goes to *seq. */
+pa_status pa_bm_add_sequence(pa_block_manager* bm, int32_t* seq);
+
+/* A new sequence holding the first prefix_tokens positions of parent (all of
+ * them when prefix_tokens < 0): it shares the parent's first
+ * ceil(prefix_tokens / block_size) blocks and takes no block of its own. */
+pa_status pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t prefix_tokens,
+                     int32_t* child);
+
+/* Ends a sequence; every block it alone held is free again. */
+pa_status pa_bm_free_sequence(pa_block_manager* bm, int32_t seq);
+
+/* Reserves num_tokens[r] new positions at the end of sequence seqs[r], for
+ * each request r (host arrays; a sequence at most once).  slots (host int64,
+ * capacity max_slots) receives the slot of every new position, request by
+ * request, in position order -- the slot_mapping of the append that follows.
+ * copies (host int32 [max_copies][2]) receives (source, destination) block
+ * pairs to copy before that append, and *num_copies their number (at most one
+ * per request).  All or nothing: PA_ERR_OUT_OF_BLOCKS when the free blocks
+ * do not cover the request, PA_ERR_INVALID_ARG when a buffer is too small;
+ * then nothing changes. */
+pa_status pa_bm_append(pa_block_manager* bm, const int32_t* seqs, const int32_t* num_tokens,
+                       int32_t num_requests, int64_t* slots, int64_t max_slots,
+                       int32_t* copies, int32_t max_copies, int32_t* num_copies);
+
+/* Host int32 block_tables [num_seqs][max_blocks_per_seq] (entries past a
+ * sequence's blocks set to -1) and, if context_lens is not NULL, host int32
+ * context_lens [num_seqs] of the listed sequences. */
+pa_status pa_bm_block_tables(const pa_block_manager* bm, const int32_t* seqs, int32_t num_seqs,
+                             int32_t max_blocks_per_seq, int32_t* block_tables,
+                             int32_t* context_lens);
+
+int32_t pa_bm_num_free_blocks(const pa_block_manager* bm);           /* -1 if bm is NULL */
+int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block);  /* -1 out of range */
+int32_t pa_bm_sequence_length(const pa_block_manager* bm, int32_t seq); /* -1 if not live */
+
+/* Copies whole blocks inside one pool, for the copy-on-write of shared blocks
+ * ([viz] "PagedAttention: the cache in blocks": a shared block is copied when
+ * one holder writes into it).  block_pairs: device int32 [num_pairs][2] of
+ * (source, destination) block ids; every KV head's rows of the source block
+ * are copied to the destination block, in k_cache and v_cache, and for an
+ * int8 cache also in k_scale and v_scale (NULL otherwise).  Pairs with an id
+ * outside [0, num_blocks) are skipped.  A destination must not be the source
+ * or the destination of another pair in the same call. */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                         const int32_t* block_pairs, int32_t num_pairs,
+                         const pa_cache_desc* cache, pa_stream_t stream);
 
 /* ---------------------------------------------------------------- misc */
 
