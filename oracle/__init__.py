@@ -79,6 +79,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_attention_dense.argtypes = [P, P, P, i64, i32, dbl, P, P]
     lib.oracle_paged_decode_attention.argtypes = [
         P, i32, P, P, P, P, i32, P, i32, P, i32, i32, i32, i32, i32, i32, dbl, P, i64, P, i32]
+    lib.oracle_paged_prefill_attention.argtypes = [
+        P, i32, P, P, P, P, i32, P, i32, P, P, i32, i32, i32, i32, i32, i32, dbl, P, i64, P,
+        i32]
     lib.oracle_gather_kv.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
                                      P, P, P, P]
     lib.oracle_project_row.argtypes = [P, P, i32, i32, P]
@@ -88,7 +91,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_max_threads.restype = i32
     for name in ("oracle_slot_mapping", "oracle_decode_slot_mapping", "oracle_kv_append",
                  "oracle_kv_append_int8", "oracle_attention_dense",
-                 "oracle_paged_decode_attention", "oracle_gather_kv"):
+                 "oracle_paged_decode_attention", "oracle_paged_prefill_attention",
+                 "oracle_gather_kv"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -229,6 +233,36 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
         _ptr(q), q_code, _ptr(k_cache), _ptr(v_cache), _ptr(ks), _ptr(vs), cache_code,
         _ptr(bt), bt.shape[1], _ptr(ctx), s_, hq, hkv, nb, bs, d, float(scale), _ptr(pp),
         n_pairs, _ptr(out), int(num_threads)))
+    return out
+
+
+def paged_prefill_attention(q, k_cache, v_cache, block_tables, query_start, context_lens,
+                            scale, k_scale=None, v_scale=None, rows=None, bf16=False,
+                            num_threads=0, lib=None) -> np.ndarray:
+    """fp64 causal attention of every query token (or the listed (token, head)
+    rows) over the paged cache.  q: [total, Hq, D]; query_start: int32 [S+1];
+    sequence s's tokens sit at its last query_start[s+1]-query_start[s]
+    positions.  Returns [total, Hq, D] when rows is None, else [len(rows), D]."""
+    q = np.ascontiguousarray(q)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    nb, hkv, bs, d = k_cache.shape
+    total, hq, dq = q.shape
+    assert dq == d and bt.shape[0] == ctx.shape[0] == qs.shape[0] - 1 and qs[-1] == total
+    ks = None if k_scale is None else np.ascontiguousarray(k_scale).view(np.uint16)
+    vs = None if v_scale is None else np.ascontiguousarray(v_scale).view(np.uint16)
+    if rows is None:
+        out = np.empty((total, hq, d), dtype=np.float64)
+        rp, n_rows = None, total * hq
+    else:
+        rp = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        n_rows = rp.shape[0]
+        out = np.empty((n_rows, d), dtype=np.float64)
+    _check((lib or load()).oracle_paged_prefill_attention(
+        _ptr(q), _dtype_code(q, bf16), _ptr(k_cache), _ptr(v_cache), _ptr(ks), _ptr(vs),
+        _dtype_code(k_cache, bf16), _ptr(bt), bt.shape[1], _ptr(qs), _ptr(ctx), ctx.shape[0],
+        hq, hkv, nb, bs, d, float(scale), _ptr(rp), n_rows, _ptr(out), int(num_threads)))
     return out
 
 

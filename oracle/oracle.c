@@ -20,6 +20,9 @@
  *   - un-paging through a block table: a sequence's rows live in fixed-size
  *     blocks of one shared pool, listed in order by a per-sequence block table
  *     ([viz] "PagedAttention: the cache in blocks").
+ *   - prefill: every prompt token's query attends causally over the cache
+ *     (positions up to its own; [viz] "The idea", "Without vs with the
+ *     cache").
  *   - append: the new token's K and V rows are stored into the cache
  *     ([notes] step 4; [guide] "How the cache turns the loop cheap").
  *   - int8 cache ([notes] "How serving systems tame the cost", "Quantized KV
@@ -409,6 +412,84 @@ int oracle_paged_decode_attention(
         qv[d] = load_elem(q, q_dtype, ((size_t)s * num_q_heads + h) * head_dim + d);
       st = oracle_attention_dense(qv, K, V, ctx, head_dim, scale,
                                   out + (size_t)p * head_dim, NULL);
+    }
+    if (st != OR_OK) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+      status = st;
+    }
+    free(K);
+    free(V);
+    free(qv);
+  }
+  return status;
+}
+
+/* Prefill (and chunked prefill) attention: several query tokens of one
+ * sequence at once ([viz] "Without vs with the cache": the prefill pass takes
+ * all prompt tokens in one go; [viz] "Prefill and decode feel different").
+ * Sequence s brings T_s = query_start[s+1] - query_start[s] query tokens whose
+ * K and V rows are already in the cache as its last T_s positions, so query
+ * token i of s sits at position p = context_lens[s] - T_s + i.  Under the
+ * causal mask a token never looks ahead ([viz] "The idea"): it attends to
+ * positions 0..p, with the dense definition above.
+ * q: [total][num_q_heads][head_dim] with total = query_start[num_seqs].
+ * rows: optional list of n_rows (token, head) pairs; NULL = every pair,
+ * token-major.  out: fp64 [n_rows][head_dim].                              */
+int oracle_paged_prefill_attention(
+    const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+    const uint16_t* k_scale, const uint16_t* v_scale, int32_t cache_dtype,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* query_start,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t num_blocks, int32_t block_size,
+    int32_t head_dim, double scale, const int32_t* rows, int64_t n_rows,
+    double* out, int32_t num_threads) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || block_size <= 0 || head_dim <= 0 ||
+      max_blocks <= 0 || !elem_bytes(cache_dtype) || !elem_bytes(q_dtype) ||
+      !query_start || query_start[0] != 0)
+    return OR_BAD_ARG;
+  if (cache_dtype == OR_I8 && (!k_scale || !v_scale)) return OR_BAD_ARG;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    int32_t t = query_start[s + 1] - query_start[s];
+    if (t < 0) return OR_BAD_ARG;
+    if (context_lens[s] < t || context_lens[s] > max_blocks * block_size) return OR_BAD_CTX;
+  }
+  const int64_t total = query_start[num_seqs];
+  if (!rows) n_rows = total * num_q_heads;
+  for (int64_t r = 0; rows && r < n_rows; ++r)
+    if (rows[2 * r] < 0 || rows[2 * r] >= total || rows[2 * r + 1] < 0 ||
+        rows[2 * r + 1] >= num_q_heads)
+      return OR_BAD_ARG;
+  int32_t group = num_q_heads / num_kv_heads;
+  int status = OR_OK;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int64_t tok = rows ? rows[2 * r] : r / num_q_heads;
+    int32_t h = rows ? rows[2 * r + 1] : (int32_t)(r % num_q_heads);
+    int32_t s = 0;
+    while (query_start[s + 1] <= tok) ++s;  /* the sequence holding token tok */
+    int32_t t_s = query_start[s + 1] - query_start[s];
+    int32_t pos = context_lens[s] - t_s + (int32_t)(tok - query_start[s]);
+    int32_t n = pos + 1;                    /* positions 0..pos */
+    int32_t kvh = h / group;
+    double* K = (double*)malloc(sizeof(double) * (size_t)n * head_dim);
+    double* V = (double*)malloc(sizeof(double) * (size_t)n * head_dim);
+    double* qv = (double*)malloc(sizeof(double) * head_dim);
+    int st = (K && V && qv) ? OR_OK : OR_NO_MEM;
+    if (st == OR_OK)
+      st = unpage(k_cache, v_cache, k_scale, v_scale, cache_dtype,
+                  block_tables + (size_t)s * max_blocks, n, kvh, num_blocks,
+                  num_kv_heads, block_size, head_dim, K, V);
+    if (st == OR_OK) {
+      for (int32_t d = 0; d < head_dim; ++d)
+        qv[d] = load_elem(q, q_dtype, ((size_t)tok * num_q_heads + h) * head_dim + d);
+      st = oracle_attention_dense(qv, K, V, n, head_dim, scale,
+                                  out + (size_t)r * head_dim, NULL);
     }
     if (st != OR_OK) {
 #ifdef _OPENMP

@@ -449,4 +449,95 @@ def pin_int8_attention_dequantizes_exactly(lib):
     assert a.tobytes() == b.tobytes()
 
 
+# ---------------------------------------------------------------- prefill
+
+def _sdpa64_rows(q, K, V, scale, mask):
+    """torch float64 SDPA for several queries with a boolean mask (True = seen)."""
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None, None]
+    Kt = torch.from_numpy(np.asarray(K, np.float64))[None, None]
+    Vt = torch.from_numpy(np.asarray(V, np.float64))[None, None]
+    m = torch.from_numpy(np.asarray(mask, bool))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=m,
+                                                            scale=scale)[0, 0].numpy()
+
+
+def pin_prefill_is_causal_attention(lib):
+    """Whole prompts (T = context): torch's causal SDPA on the dense rows;
+    chunks (T < context, earlier positions cached): SDPA with the mask 'key
+    position <= query position', the query positions being the last T."""
+    rng = np.random.default_rng(21)
+    hq, hkv, d, bs = 4, 2, 16, 4
+    ctx = [1, 5, 19, 23, 9]
+    tq = [1, 5, 19, 7, 3]                       # the last two are chunks
+    K = [rng.standard_normal((c, hkv, d)).astype(np.float32) for c in ctx]
+    V = [rng.standard_normal((c, hkv, d)).astype(np.float32) for c in ctx]
+    kp, vp, bt, ctx_a = _scatter_pool(K, V, bs, 64, rng, np.float32)
+    qs = np.concatenate([[0], np.cumsum(tq)]).astype(np.int32)
+    q = rng.standard_normal((qs[-1], hq, d)).astype(np.float32)
+    out = oracle.paged_prefill_attention(q, kp, vp, bt, qs, ctx_a, 0.25, lib=lib)
+    for s, (c, t) in enumerate(zip(ctx, tq)):
+        for h in range(hq):
+            qq = q[qs[s]:qs[s + 1], h].astype(np.float64)
+            kk, vv = K[s][:, h // 2].astype(np.float64), V[s][:, h // 2].astype(np.float64)
+            if t == c:
+                qt = torch.from_numpy(qq)[None, None]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qt, torch.from_numpy(kk)[None, None], torch.from_numpy(vv)[None, None],
+                    is_causal=True, scale=0.25)[0, 0].numpy()
+            else:
+                mask = np.arange(c)[None, :] <= (c - t + np.arange(t))[:, None]
+                ref = _sdpa64_rows(qq, kk, vv, 0.25, mask)
+            assert np.max(np.abs(out[qs[s]:qs[s + 1], h] - ref)) < 1e-12
+
+
+def pin_prefill_matches_decode_loop(lib):
+    """The pages' loop (3-token prompt, 4 decode steps): one causal prefill
+    over all 7 tokens gives, at every position, exactly the output the loop
+    produced when that position was the newest ("the attention itself is the
+    same in both lanes")."""
+    from oracle import decode_loop
+    rng = np.random.default_rng(14)
+    hq, hkv, d, dm, bs = 4, 2, 64, 64, 4
+    n_tok = 7
+    x = rng.standard_normal((n_tok, dm))
+    Wq = rng.standard_normal((dm, hq * d)) / 8
+    Wk = rng.standard_normal((dm, hkv * d)) / 8
+    Wv = rng.standard_normal((dm, hkv * d)) / 8
+    table = [5, 2, 9]
+    r = decode_loop.run(x, Wq, Wk, Wv, 3, hq, hkv, d, bs, table, 16, 0.125, lib=lib)
+    rows = lambda W, h: np.stack([oracle.project_row(x[t], W, lib).astype(np.float32)
+                                  .reshape(h, d) for t in range(n_tok)])
+    q, k, v = rows(Wq, hq), rows(Wk, hkv), rows(Wv, hkv)
+    kc = np.full((16, hkv, bs, d), np.nan, np.float32)
+    vc = np.full_like(kc, np.nan)
+    bt = np.array([table], np.int32)
+    slots = oracle.slot_mapping(bt, np.zeros(n_tok, np.int32), np.arange(n_tok, dtype=np.int32),
+                                bs, lib=lib)
+    oracle.kv_append(k, v, slots, kc, vc, lib=lib)
+    out = oracle.paged_prefill_attention(q, kc, vc, bt, np.array([0, n_tok], np.int32),
+                                         np.array([n_tok], np.int32), 0.125, lib=lib)
+    for i, n in enumerate(r["prefix_lengths"]):
+        assert out[n - 1].tobytes() == r["out_cache"][i].tobytes()
+
+
+def pin_prefill_chunking_invariance(lib):
+    """A prompt taken in chunks (each attending over the positions cached so
+    far plus itself) gives the same rows as one whole prefill, bit for bit."""
+    rng = np.random.default_rng(22)
+    hq, hkv, d, bs, n = 2, 1, 8, 4, 12
+    K = [rng.standard_normal((n, hkv, d)).astype(np.float32)]
+    V = [rng.standard_normal((n, hkv, d)).astype(np.float32)]
+    kp, vp, bt, _ = _scatter_pool(K, V, bs, 16, rng, np.float32)
+    q = rng.standard_normal((n, hq, d)).astype(np.float32)
+    whole = oracle.paged_prefill_attention(q, kp, vp, bt, np.array([0, n], np.int32),
+                                           np.array([n], np.int32), 0.3, lib=lib)
+    done = 0
+    for t in (5, 4, 3):
+        part = oracle.paged_prefill_attention(q[done:done + t], kp, vp, bt,
+                                              np.array([0, t], np.int32),
+                                              np.array([done + t], np.int32), 0.3, lib=lib)
+        assert part.tobytes() == whole[done:done + t].tobytes()
+        done += t
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -11,7 +11,10 @@ import oracle_pins
 
 MUTANTS = {
     "scale dropped from the scores": ("z[i] = scale * dot;", "z[i] = dot;"),
-    "GQA head mapped round-robin": ("int32_t kvh = h / group;", "int32_t kvh = h % num_kv_heads;"),
+    "GQA head mapped round-robin": (
+        "int32_t kvh = h / group;\n    size_t n =", "int32_t kvh = h % num_kv_heads;\n    size_t n ="),
+    "prefill GQA head mapped round-robin": (
+        "int32_t kvh = h / group;\n    double* K", "int32_t kvh = h % num_kv_heads;\n    double* K"),
     "offset in block taken from the block index": (
         "block_size + i % block_size;\n    double sk", "block_size + i / block_size;\n    double sk"),
     "softmax not normalised": ("double w = z[i] / total;", "double w = z[i];"),
@@ -34,6 +37,13 @@ MUTANTS = {
     "gather offset from block index": (
         "block_size + i % block_size;\n        size_t dst_row", "block_size + i / block_size;\n        size_t dst_row"),
     "binary16 rounding truncates": ("double n = nearbyint(a / quantum);", "double n = floor(a / quantum);"),
+    "prefill position counted from the chunk start": (
+        "int32_t pos = context_lens[s] - t_s + (int32_t)(tok - query_start[s]);",
+        "int32_t pos = (int32_t)(tok - query_start[s]);"),
+    "prefill query excludes its own position": ("int32_t n = pos + 1;                    /*",
+                                                "int32_t n = pos;                    /*"),
+    "prefill token given to the previous sequence": (
+        "while (query_start[s + 1] <= tok) ++s;", "while (query_start[s + 1] < tok) ++s;"),
     "dot product over half the head": (
         "for (int32_t d = 0; d < head_dim; ++d) dot += q[d] * K[i * head_dim + d];",
         "for (int32_t d = 0; d < head_dim / 2; ++d) dot += q[d] * K[i * head_dim + d];"),
