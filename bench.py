@@ -284,13 +284,128 @@ def block_pool_bench(dev, steps: int, warmup: int, cpu: bool) -> dict:
     }
 
 
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16/bf16
+
+
+PREFILL_WORKLOADS = {
+    # name: (description, context lengths, chunk lengths)
+    "prefill-llama3-8b": ("Llama-3-8B layer shape (32 q / 8 KV heads, d 128, block 16, fp16), "
+                          "8 whole prompts of 2048 tokens, 32 layer pools",
+                          [2048] * 8, [2048] * 8),
+    "chunked-prefill-llama3-8b": ("Llama-3-8B layer shape (32 q / 8 KV heads, d 128, block 16, "
+                                  "fp16), 16 sequences each taking a 512-token chunk after 3584 "
+                                  "cached positions, 32 layer pools",
+                                  [4096] * 16, [512] * 16),
+}
+
+
+def prefill_flops(ctx, tq, hq, d) -> int:
+    """Causal attention flops: query at position p scores and mixes p+1 rows,
+    2D flops each for q.k and for w.v."""
+    total = 0
+    for c, t in zip(ctx, tq):
+        first = c - t
+        total += (t * (first + 1) + t * (t - 1) // 2) * 4 * d * hq
+    return total
+
+
+def prefill_bench(name, dev, steps, warmup, cpu: bool) -> dict:
+    import numpy as np
+
+    desc, ctx, tq = PREFILL_WORKLOADS[name]
+    hq, hkv, d, bs, layers = 32, 8, 128, 16, 32
+    g = torch.Generator(device=dev).manual_seed(0)
+    nblk = sum(-(-c // bs) for c in ctx)
+    maxb = max(-(-c // bs) for c in ctx)
+    perm = torch.randperm(nblk, generator=torch.Generator().manual_seed(1))
+    bt = torch.full((len(ctx), maxb), -1, dtype=torch.int32)
+    cur = 0
+    for s, c in enumerate(ctx):
+        k = -(-c // bs)
+        bt[s, :k] = perm[cur:cur + k].to(torch.int32)
+        cur += k
+    bt = bt.to(dev)
+    qs = torch.tensor([0] + list(np.cumsum(tq)), dtype=torch.int32, device=dev)
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    pools = [(torch.randn((nblk, hkv, bs, d), generator=g, device=dev).half(),
+              torch.randn((nblk, hkv, bs, d), generator=g, device=dev).half())
+             for _ in range(layers)]
+    q = torch.randn((sum(tq), hq, d), generator=g, device=dev).half()
+    out = torch.empty_like(q)
+    scale = d ** -0.5
+    maxq = max(tq)
+
+    def step():
+        for kc, vc in pools:
+            pa.paged_prefill_attention(q, kc, vc, bt, qs, ctx_t, scale, out, maxq)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = prefill_flops(ctx, tq, hq, d)
+    launch_ms = ms / layers
+    tflops = flops / (launch_ms / 1e3) / 1e12
+    cpu_block = None
+    if cpu:
+        import oracle
+
+        kh = pools[0][0].cpu().numpy()
+        vh = pools[0][1].cpu().numpy()
+        qh = q.cpu().numpy()
+        rng = np.random.default_rng(3)
+        total = sum(tq)
+        threads = oracle.max_threads()
+        rows, n, t0 = [], 0, time.perf_counter()
+        sample_flops = 0
+        qs_h, bt_h = qs.cpu().numpy(), bt.cpu().numpy()
+        while time.perf_counter() - t0 < 10.0:
+            batch = [(int(rng.integers(total)), int(rng.integers(hq))) for _ in range(64)]
+            oracle.paged_prefill_attention(qh, kh, vh, bt_h, qs_h, np.array(ctx, np.int32),
+                                           scale, rows=batch, num_threads=threads)
+            for tok, _ in batch:
+                s_ = int(np.searchsorted(qs_h, tok, side="right")) - 1
+                pos = ctx[s_] - tq[s_] + tok - int(qs_h[s_])
+                sample_flops += (pos + 1) * 4 * d
+            n += len(batch)
+        dt = time.perf_counter() - t0
+        cpu_block = {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s",
+                     "cores": threads, "kind": "oracle",
+                     "sample": f"{n} random (token, head) rows of layer 0, fp64 oracle, "
+                               f"{dt:.1f} s on {threads} threads"}
+    peak = MFMA_PEAK_TFLOPS["f16"]
+    return {
+        "metric": "prefill attention TFLOP/s (causal, % of fp16 dense MFMA peak)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic: seeded N(0,1) q/k/v at the layer shape; block tables a seeded "
+                "permutation of the pool",
+        "config": {"workload": f"{name}: {desc}; step = pa_paged_prefill_attention on each of "
+                               f"the 32 layers", "num_seqs": len(ctx), "query_tokens": sum(tq),
+                   "context_lens_sum": sum(ctx), "layers": layers},
+        "tokens_per_s": round(sum(tq) * 1e3 / ms, 1),
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel",
+                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_ms": round(launch_ms, 5)},
+        "cpu_baseline": cpu_block,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=W.LLAMA2_7B.name,
-                    choices=sorted(W.SHAPES) + ["block-pool"])
+                    choices=sorted(W.SHAPES) + ["block-pool"] + sorted(PREFILL_WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="0: the workload's own layer count")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="0: the library's own plan (what pa_paged_decode_attention runs)")
@@ -320,6 +435,11 @@ def main():
     if args.workload == "block-pool":
         print(json.dumps(block_pool_bench(dev, args.steps, args.warmup,
                                           not args.no_cpu_baseline)))
+        return
+
+    if args.workload in PREFILL_WORKLOADS:
+        print(json.dumps(prefill_bench(args.workload, dev, args.steps, args.warmup,
+                                       not args.no_cpu_baseline)))
         return
 
     shape = W.SHAPES[args.workload]

@@ -21,7 +21,7 @@ __all__ = [
     "kv_append", "kv_append_int8", "decode_workspace_bytes", "decode_partition_tokens",
     "paged_decode_attention", "paged_decode_attention_int8", "decode_step", "decode_partitions",
     "decode_step_partitions", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
-    "BlockManager", "copy_blocks",
+    "BlockManager", "copy_blocks", "paged_prefill_attention",
 ]
 
 # PA_LIBRARY_PATH may name another build of the same library (e.g. a variant
@@ -88,6 +88,7 @@ def _declare(lib):
                                       P],
         "pa_gather_kv": [P, P, P, P, P, i32, P, i32, P, P, P, P, D, P],
         "pa_copy_blocks": [P, P, P, P, P, i32, D, P],
+        "pa_paged_prefill_attention": [P, P, P, P, i32, P, P, i32, i32, i32, f32, P, D, P],
         "pa_bm_create": [i32, i32, ctypes.POINTER(P)],
         "pa_bm_add_sequence": [P, ctypes.POINTER(i32)],
         "pa_bm_fork": [P, i32, i32, ctypes.POINTER(i32)],
@@ -364,6 +365,38 @@ def gather_kv(k_cache, v_cache, block_tables, context_lens, k_out, v_out, k_scal
                          _dev(k_out, "k_out", k_cache.dtype), _dev(v_out, "v_out", k_cache.dtype),
                          _dev(k_scale_out, "k_scale_out"), _dev(v_scale_out, "v_scale_out"),
                          ctypes.byref(desc), _stream(k_cache)), lib)
+
+
+# ---------------------------------------------------------------- prefill
+
+def paged_prefill_attention(q, k_cache, v_cache, block_tables, query_start, context_lens, scale,
+                            out, max_query_len: int | None = None):
+    """Causal attention of query chunks over the paged cache (prefill and
+    chunked prefill; see pa_paged_prefill_attention).  q, out: [total, Hq, D];
+    query_start: int32 [S+1] on the GPU; sequence s's query tokens are its
+    last query_start[s+1]-query_start[s] cached positions.  max_query_len
+    (the longest chunk) sizes the grid; when None it is read from
+    query_start, which synchronizes."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    if q.dtype != k_cache.dtype or out.dtype != q.dtype:
+        raise ValueError("q, caches and out must share one format")
+    s = block_tables.shape[0]
+    if query_start.numel() != s + 1 or context_lens.numel() != s:
+        raise ValueError("query_start must hold S+1 entries and context_lens S")
+    if max_query_len is None:
+        qs = query_start.cpu()
+        max_query_len = int((qs[1:] - qs[:-1]).max()) if s else 0
+    if q.shape != out.shape or q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q and out must be [total, Hq, D] alike")
+    _ok(lib.pa_paged_prefill_attention(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+        _dev(query_start, "query_start", torch.int32), _dev(context_lens, "context_lens",
+                                                           torch.int32),
+        s, int(max_query_len), q.shape[1], float(scale), _dev(out, "out"), ctypes.byref(desc),
+        _stream(q)), lib)
+    return out
 
 
 # ---------------------------------------------------------------- block pool

@@ -19,8 +19,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libpagedattn.so")
 
-SOURCES = ["api.cpp", "block_manager.cpp", "kv_ops.hip", "lse_merge.hip", "decode_f32.hip", "decode_f16.hip",
-           "decode_bf16.hip", "decode_i8.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "kv_ops.hip", "lse_merge.hip", "decode_f32.hip",
+           "decode_f16.hip", "decode_bf16.hip", "decode_i8.hip", "prefill_f16.hip",
+           "prefill_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -34,9 +35,18 @@ FLAGS = [
 ]
 
 
+# Per-file additions.  The prefill kernels keep their matrix-core
+# accumulators in VGPRs: in the AGPR form the backend copied all 128 of them
+# AGPR -> VGPR on every tile of the KV loop.
+EXTRA_FLAGS = {
+    "prefill_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(line for line in r.stderr.splitlines() if noise not in line)

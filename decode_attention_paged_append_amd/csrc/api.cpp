@@ -8,6 +8,7 @@
 
 #include "pagedattn.h"
 #include "decode_dispatch.h"
+#include "prefill_dispatch.h"
 #include "kv_ops.h"
 #include "status.h"
 
@@ -480,6 +481,59 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
                                          cache->num_blocks, cache->num_kv_heads,
                                          cache->block_size, row_bytes, (hipStream_t)stream),
                     "gather launch");
+}
+
+pa_status pa_paged_prefill_attention(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* query_start, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t max_query_len,
+                                     int32_t num_q_heads, float scale, void* out,
+                                     const pa_cache_desc* cache, pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (cache->dtype != PA_F16 && cache->dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "prefill attention takes fp16 or bf16 caches (dtype %d)",
+                cache->dtype);
+  if (num_seqs < 0 || max_query_len < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "bad sizes (seqs %d, max_query_len %d, max_blocks %d, "
+                "q heads %d)", num_seqs, max_query_len, max_blocks_per_seq, num_q_heads);
+  if (num_q_heads % cache->num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "%d query heads do not divide over %d KV heads",
+                num_q_heads, cache->num_kv_heads);
+  if (!(scale > 0.0f))
+    return fail(PA_ERR_INVALID_ARG, "prefill scale must be positive (got %g)", (double)scale);
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (num_seqs > 65535 || cache->num_kv_heads > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "more than 65535 sequences or KV heads in one launch");
+  if (!q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens || !out)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  pa::PrefillParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.query_start = query_start;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_blocks = cache->num_blocks;
+  p.group = num_q_heads / cache->num_kv_heads;
+  p.scale_log2 = scale * pa::kLog2e;
+  // 256 query rows per workgroup once the chunk fills them; 64 for short
+  // chunks, whose rows would otherwise mostly be padding.
+  const int64_t rows = (int64_t)max_query_len * p.group;
+  const pa::PrefillShape shape = pa::prefill_shape(cache->head_dim, rows);
+  const int64_t row_tiles = (rows + shape.rows() - 1) / shape.rows();
+  if (row_tiles > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "chunk too long");
+  const hipError_t e =
+      cache->dtype == PA_F16
+          ? pa::launch_prefill_f16(p, cache->head_dim, cache->block_size, shape, (int)row_tiles,
+                                   num_seqs, (hipStream_t)stream)
+          : pa::launch_prefill_bf16(p, cache->head_dim, cache->block_size, shape,
+                                    (int)row_tiles, num_seqs, (hipStream_t)stream);
+  return hip_status(e, "prefill launch");
 }
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,

@@ -60,6 +60,10 @@ template <> struct Mfma<Fmt::F16> {
     const f32x2 x = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, h16x2));
   }
+  // acc + both halves of a packed pair (v_dot2 with ones)
+  __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(as_h2(w), h16x2{1, 1}, acc, false);
+  }
 };
 template <> struct Mfma<Fmt::BF16> {
   __device__ static __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
@@ -73,6 +77,9 @@ template <> struct Mfma<Fmt::BF16> {
   __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
     const f32x2 x = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  }
+  __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w), bf16x2{1, 1}, acc, false);
   }
 };
 

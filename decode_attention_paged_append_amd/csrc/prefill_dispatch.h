@@ -1,0 +1,59 @@
+// prefill_dispatch.h -- runtime (head_dim, block size, rows per wave) ->
+// template instance of the prefill kernel (internal).
+#pragma once
+
+#include "prefill_mfma.h"
+
+namespace pa {
+
+// Launch shapes.  Long chunks: 256 query rows per workgroup, as 8 waves x 2
+// row groups (head_dim 128; two waves per SIMD fit in the registers) or 4
+// waves x 4 row groups (head_dim 64).  Short chunks: 4 waves x 1 row group.
+struct PrefillShape {
+  int nr, nw;
+  int rows() const { return nr * nw * 16; }
+};
+inline PrefillShape prefill_shape(int head_dim, int64_t rows) {
+  if (rows < 256) return {1, 4};
+  return head_dim == 128 ? PrefillShape{2, 8} : PrefillShape{4, 4};
+}
+
+template <Fmt F, int D, int BS, int NR, int NW>
+static hipError_t launch_prefill_one(const PrefillParams& p, int row_tiles, int num_seqs,
+                                     hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_mfma_kernel<F, D, BS, NR, NW>),
+                     dim3(row_tiles, p.num_kv_heads, num_seqs), dim3(NW * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <Fmt F, int D, int NR, int NW>
+static hipError_t launch_prefill_bs(const PrefillParams& p, int bs, int row_tiles, int num_seqs,
+                                    hipStream_t stream) {
+  switch (bs) {
+    case 4: return launch_prefill_one<F, D, 4, NR, NW>(p, row_tiles, num_seqs, stream);
+    case 8: return launch_prefill_one<F, D, 8, NR, NW>(p, row_tiles, num_seqs, stream);
+    case 16: return launch_prefill_one<F, D, 16, NR, NW>(p, row_tiles, num_seqs, stream);
+    case 32: return launch_prefill_one<F, D, 32, NR, NW>(p, row_tiles, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <Fmt F>
+static hipError_t launch_prefill_fmt(const PrefillParams& p, int head_dim, int bs,
+                                     PrefillShape shape, int row_tiles, int num_seqs,
+                                     hipStream_t stream) {
+  if (head_dim == 64)
+    return shape.nr == 4 ? launch_prefill_bs<F, 64, 4, 4>(p, bs, row_tiles, num_seqs, stream)
+                         : launch_prefill_bs<F, 64, 1, 4>(p, bs, row_tiles, num_seqs, stream);
+  if (head_dim == 128)
+    return shape.nr == 2 ? launch_prefill_bs<F, 128, 2, 8>(p, bs, row_tiles, num_seqs, stream)
+                         : launch_prefill_bs<F, 128, 1, 4>(p, bs, row_tiles, num_seqs, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_f16(const PrefillParams& p, int head_dim, int bs, PrefillShape shape,
+                              int row_tiles, int num_seqs, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillParams& p, int head_dim, int bs, PrefillShape shape,
+                               int row_tiles, int num_seqs, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,11 @@
+// prefill_f16.hip -- prefill-kernel instances for the f16 cache format.
+#include "prefill_dispatch.h"
+
+namespace pa {
+
+hipError_t launch_prefill_f16(const PrefillParams& p, int head_dim, int bs, PrefillShape shape,
+                             int row_tiles, int num_seqs, hipStream_t stream) {
+  return launch_prefill_fmt<Fmt::F16>(p, head_dim, bs, shape, row_tiles, num_seqs, stream);
+}
+
+}  // namespace pa

@@ -1,0 +1,352 @@
+// prefill_mfma.h -- causal attention of query chunks over the paged cache
+// (prefill and chunked prefill) on the matrix cores.
+//
+// The prefill pass takes all prompt tokens at once and is bound by arithmetic,
+// not memory ("Without vs with the cache" and "Prefill and decode feel
+// different" on the KV-cache visualization page).  Sequence s brings T_s query
+// tokens whose K/V rows already sit in the cache as its last T_s positions;
+// the query at position p attends to positions 0..p (a token never looks
+// ahead: "The idea" on the same page).  Tiles stream through on-chip memory
+// with an online softmax and the score matrix is never stored (the
+// jovanaeducation guide, "Flash attention: don't build the giant matrix").
+//
+// Work split: a workgroup owns RWG = NW waves x 16*NR query rows of one
+// (sequence, KV head); rows are (token, head of the group) pairs, token-major,
+// so all query heads of a KV head share every K/V tile.  The workgroup walks
+// the KV positions 0..(its last row's position) in tiles of 32, staged in LDS
+// (double-buffered, one barrier per tile) and read by all its waves:
+//
+//   S^T[tok][row] = K[tok][:] . Q[row][:]       v_mfma_f32_16x16x32_{f16,bf16}
+//   O^T[dim][row] += V^T[dim][tok] . P^T[tok][row]   v_mfma_f32_16x16x32_{f16,bf16}
+//
+// Lane l = 16g + n.  The two 16-token halves of a score tile leave lane (g, n)
+// holding tokens {4g..4g+3, 16+4g..16+4g+3} of row n, which is the B operand
+// P^T of the value product when its 32 k-slots are mapped to those tokens;
+// the A operand V^T is read from LDS as the same 8 token rows at the lane's
+// dims n*VE.. and packed with v_perm (row r of value MFMA e = dim r*VE + e).
+#pragma once
+
+#include "decode_mfma.h"
+
+namespace pa {
+
+struct PrefillParams {
+  const void* q;            // [total][Hq][D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* query_start;  // [S+1]
+  const int32_t* context_lens; // [S]
+  void* out;                // [total][Hq][D]
+  int32_t max_blocks;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t group;
+  float scale_log2;         // scale * log2(e)
+};
+
+constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr int kPrefillTile = 32;  // KV positions per tile
+
+template <Fmt F, int D, int BS, int NR, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4, 2)))
+void prefill_mfma_kernel(const PrefillParams p) {
+  using MM = Mfma<F>;
+  constexpr int TT = kPrefillTile;
+  constexpr int RW = 16 * NR;                  // query rows per wave
+  constexpr int RWG = NW * RW;                 // query rows per workgroup
+  constexpr int CH = D / 8;                    // 16-byte chunks per row
+  constexpr int QKS = D / 32;                  // score MFMAs per 16 tokens and 16 rows
+  constexpr int VE = D / 16;                   // dims per lane = value MFMAs per 16 rows
+  constexpr int TILE_CHUNKS = TT * CH;         // 16-byte chunks per K (or V) tile
+  constexpr int PER_THREAD = (TILE_CHUNKS + NW * kWave - 1) / (NW * kWave);
+  constexpr bool EVEN = PER_THREAD * NW * kWave == TILE_CHUNKS;  // else the last pass is partial
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int s = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int G = p.group;
+  const int q0 = p.query_start[s];
+  const int T = p.query_start[s + 1] - q0;
+  const int ctx = p.context_lens[s];
+  const int R0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * RWG;  // late rows (most work) first
+  if (R0 >= T * G) return;
+  const int Hq = p.num_q_heads;
+
+  const bool bad_ctx = T < 0 || ctx < T || ctx > p.max_blocks * BS;
+  const int base = ctx - T;  // position of the chunk's first query token
+  if (bad_ctx) {
+    const int rows = min(RWG, T * G - R0);
+    for (int i = threadIdx.x; i < rows * D; i += NW * kWave) {
+      const int rr = R0 + i / D;
+      const size_t orow = (size_t)(q0 + rr / G) * Hq + kvh * G + rr % G;
+      store_out<F>(p.out, orow * D + i % D, __builtin_nanf(""));
+    }
+    return;
+  }
+
+  // ---- this lane's query rows: group r, column n
+  const int Rw = R0 + wave * RW;
+  int qpos[NR];
+  u32x4 qb[NR][QKS];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int rr = Rw + 16 * r + n;
+    const int tok = rr / G;
+    qpos[r] = base + tok;  // rows past the chunk compute garbage that is never stored
+#pragma unroll
+    for (int c = 0; c < QKS; ++c) {
+      qb[r][c] = u32x4{0, 0, 0, 0};
+      if (tok < T) {
+        const size_t qrow = (size_t)(q0 + tok) * Hq + kvh * G + rr % G;
+        qb[r][c] = load16((const char*)p.q + (qrow * D + 32 * c + 8 * g) * 2);
+      }
+    }
+  }
+  const int last_tok_wg = min(T - 1, (R0 + RWG - 1) / G);
+  const int ntiles = (base + last_tok_wg) / TT + 1;
+  const int wave_first_tok = Rw / G;
+  const int wave_last_tok = min(T - 1, (Rw + RW - 1) / G);
+  const bool wave_live = wave_first_tok < T;
+  const int wave_qmin = base + wave_first_tok;
+  const int wave_qmax = base + wave_last_tok;
+
+  float m[NR], lsum[NR];
+  f32x4 o[NR][VE];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    m[r] = kMaxInit;
+    lsum[r] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) o[r][e] = f32x4{0, 0, 0, 0};
+  }
+
+  __shared__ __attribute__((aligned(16))) u32x4 s_k[2][TILE_CHUNKS];
+  __shared__ __attribute__((aligned(16))) u32x4 s_v[2][TILE_CHUNKS];
+
+  const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
+  const char* __restrict__ kbase = (const char*)p.k_cache;
+  const char* __restrict__ vbase = (const char*)p.v_cache;
+  bool bad_block = false;
+
+  // Cooperative tile load: chunk idx = row * CH + c of the tile.  K/V rows
+  // are fetched two tiles ahead of their use (two register stages), and a
+  // tile's block ids one tile ahead of its rows, so neither the table nor the
+  // cache rows are waited for while there is math to do.
+  struct Stage {
+    u32x4 k[PER_THREAD], v[PER_THREAD];
+  };
+  int ids_next[PER_THREAD];
+  auto load_ids = [&](const int t, int (&ids)[PER_THREAD]) {
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int idx = j * NW * kWave + threadIdx.x;
+      const int row = idx / CH;
+      const int pos = t * TT + row;
+      ids[j] = (EVEN || idx < TILE_CHUNKS) && pos < ctx ? table[pos / BS] : 0;
+    }
+  };
+  auto load_tile = [&](const int t, const int (&ids)[PER_THREAD], Stage& st) {
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int idx = j * NW * kWave + threadIdx.x;
+      const int row = idx / CH;
+      const int c = idx - row * CH;
+      const int pos = t * TT + row;
+      st.k[j] = st.v[j] = u32x4{0, 0, 0, 0};
+      if ((EVEN || idx < TILE_CHUNKS) && pos < ctx) {
+        int blk = ids[j];
+        const bool ok = (unsigned)blk < (unsigned)p.num_blocks;
+        bad_block |= !ok;
+        blk = ok ? blk : 0;
+        const size_t off = ((((size_t)blk * p.num_kv_heads + kvh) * BS + pos % BS) * CH + c) * 16;
+        st.k[j] = load16(kbase + off);
+        st.v[j] = load16(vbase + off);
+      }
+    }
+  };
+  auto store_tile = [&](const int buf, const Stage& st) {
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int idx = j * NW * kWave + threadIdx.x;
+      const int row = idx / CH;
+      const int c = idx - row * CH;
+      if (!EVEN && idx >= TILE_CHUNKS) continue;
+      s_k[buf][row * CH + (c ^ (row % CH))] = st.k[j];
+      s_v[buf][idx] = st.v[j];
+    }
+  };
+
+  Stage sa, sb;
+  {
+    int ids[PER_THREAD];
+    load_ids(0, ids);
+    load_tile(0, ids, sa);
+    if (ntiles > 1) {
+      load_ids(1, ids);
+      load_tile(1, ids, sb);
+    }
+  }
+  if (ntiles > 2) load_ids(2, ids_next);
+  store_tile(0, sa);
+  __syncthreads();
+
+  // One tile: start the loads of tile t+2 into `into`, do tile t's math from
+  // LDS, then move tile t+1 (loaded an iteration ago) from `from` to LDS.
+  auto step = [&](const int t, Stage& into, const Stage& from) {
+    const int buf = t & 1;
+    if (t + 2 < ntiles) {
+      int ids[PER_THREAD];
+#pragma unroll
+      for (int j = 0; j < PER_THREAD; ++j) ids[j] = ids_next[j];
+      if (t + 3 < ntiles) load_ids(t + 3, ids_next);
+      load_tile(t + 2, ids, into);
+    }
+    const int t0 = t * TT;
+    if (wave_live && t0 <= wave_qmax) {
+      const bool diag = t0 + TT - 1 > wave_qmin;  // some (row, token) pair is masked
+      // ---- scores: two 16-token halves
+      f32x4 sacc[2][NR];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int krow = 16 * h + n;
+        u32x4 a[QKS];
+#pragma unroll
+        for (int c = 0; c < QKS; ++c) a[c] = s_k[buf][krow * CH + ((4 * c + g) ^ (krow % CH))];
+        // chunk outer, row group inner: NR independent accumulation chains
+#pragma unroll
+        for (int r = 0; r < NR; ++r) sacc[h][r] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < QKS; ++c) {
+#pragma unroll
+          for (int r = 0; r < NR; ++r) sacc[h][r] = MM::qk(a[c], qb[r][c], sacc[h][r]);
+        }
+      }
+      // ---- V^T operands (shared by the NR row groups)
+      uint32_t vh[8][VE / 2];  // token rows {4g+j, 16+4g+j}, dims n*VE..
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int vrow = (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+        if constexpr (VE == 8) {
+          const u32x4 w = s_v[buf][vrow * CH + n];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) vh[j][k] = w[k];
+        } else {
+          const u32x2 w = ((const u32x2*)&s_v[buf][0])[vrow * (CH * 2) + n];
+          vh[j][0] = w[0];
+          vh[j][1] = w[1];
+        }
+      }
+      // V^T operand of value MFMA e: the 8 token rows' values at dim n*VE + e
+      u32x4 va[VE];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const int w = e >> 1;
+        va[e] = u32x4{__builtin_amdgcn_perm(vh[1][w], vh[0][w], sel),
+                      __builtin_amdgcn_perm(vh[3][w], vh[2][w], sel),
+                      __builtin_amdgcn_perm(vh[5][w], vh[4][w], sel),
+                      __builtin_amdgcn_perm(vh[7][w], vh[6][w], sel)};
+      }
+      // ---- online softmax and values, per row group.  Scores stay raw (the
+      // scale is positive, so maxima commute with it); a weight is
+      // exp2(s * scale_log2 - m) in one FMA and one v_exp.
+      auto softmax_values = [&](auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          float sv[2][4];
+          float mt = -__builtin_inff();
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              sv[h][i] = sacc[h][r][i];
+              if (DIAG && t0 + 16 * h + 4 * g + i > qpos[r]) sv[h][i] = -__builtin_inff();
+            }
+            mt = fmaxf(mt, fmaxf(fmaxf(sv[h][0], sv[h][1]), fmaxf(sv[h][2], sv[h][3])));
+          }
+          // The reference max m of a row moves only when one of its scores
+          // exceeds it by more than kLazyRescale.  The result is the same
+          // for any reference (it cancels in the normalisation); weights stay
+          // <= 2^kLazyRescale, far inside the operand formats' range; and
+          // on almost every tile neither the row-wide max (two cross-lane
+          // steps) nor the accumulator rescale is needed.
+          float mn = m[r];
+          float alpha = 1.0f;
+          const bool need = mt * p.scale_log2 > m[r] + kLazyRescale;
+          if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt *= p.scale_log2;
+            if (mt > m[r] + kLazyRescale) mn = mt;  // same decision on the row's 4 lanes
+            alpha = fast_exp2(m[r] - mn);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) o[r][e] *= alpha;
+            m[r] = mn;
+          }
+          float pw[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pw[h][i] = fast_exp2(fmaf(sv[h][i], p.scale_log2, -mn));
+          }
+          const u32x4 pb = {MM::pack(pw[0][0], pw[0][1]), MM::pack(pw[0][2], pw[0][3]),
+                            MM::pack(pw[1][0], pw[1][1]), MM::pack(pw[1][2], pw[1][3])};
+          // the row sum of the rounded weights, the ones the value product uses
+          float ps = lsum[r] * alpha;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) ps = MM::sum2(pb[w], ps);
+          lsum[r] = ps;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) o[r][e] = MM::qk(va[e], pb, o[r][e]);
+        }
+      };
+      if (diag)
+        softmax_values(std::true_type{});
+      else
+        softmax_values(std::false_type{});
+    }
+    if (t + 1 < ntiles) store_tile(buf ^ 1, from);
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < ntiles) step(t + 1, sb, sa);
+  }
+
+  // ---- normalise and store: lane (g, n) holds dims (4g+i)*VE + e of row n
+  const bool bad = __syncthreads_or(bad_block ? 1 : 0) != 0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    float l = lsum[r];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = bad ? __builtin_nanf("") : 1.0f / l;
+    const int rr = Rw + 16 * r + n;
+    const int tok = rr / G;
+    if (tok >= T) continue;
+    const size_t orow = (size_t)(q0 + tok) * Hq + kvh * G + rr % G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t off = orow * D + (4 * g + i) * VE;
+      if constexpr (VE == 8) {
+        const u32x4 w = {MM::pack(o[r][0][i] * inv, o[r][1][i] * inv),
+                         MM::pack(o[r][2][i] * inv, o[r][3][i] * inv),
+                         MM::pack(o[r][4][i] * inv, o[r][5][i] * inv),
+                         MM::pack(o[r][6][i] * inv, o[r][7][i] * inv)};
+        *(u32x4*)((char*)p.out + off * 2) = w;
+      } else {
+        const u32x2 w = {MM::pack(o[r][0][i] * inv, o[r][1][i] * inv),
+                         MM::pack(o[r][2][i] * inv, o[r][3][i] * inv)};
+        *(u32x2*)((char*)p.out + off * 2) = w;
+      }
+    }
+  }
+}
+
+}  // namespace pa

@@ -263,6 +263,35 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
                        int32_t num_seqs, void* k_out, void* v_out, void* k_scale_out,
                        void* v_scale_out, const pa_cache_desc* cache, pa_stream_t stream);
 
+/* ---------------------------------------------------------------- prefill */
+
+/* Causal attention of several query tokens per sequence over the paged cache:
+ * prefill, which takes a whole prompt at once, and chunked prefill, which
+ * takes it in pieces ([viz] "Without vs with the cache", "Prefill and decode
+ * feel different").  Sequence s brings T_s = query_start[s+1] - query_start[s]
+ * query tokens whose K and V rows are already stored as its last T_s cached
+ * positions (append first, e.g. pa_kv_append with pa_slot_mapping), so its
+ * query token i sits at position p = context_lens[s] - T_s + i and attends to
+ * positions 0..p: a token never looks ahead ([viz] "The idea").  Tiles of the
+ * score matrix stay on chip ([guide] "Flash attention").
+ *   q, out         : device [query_start[num_seqs]][num_q_heads][head_dim],
+ *                    fp16 or bf16, the cache's format; out fully written for
+ *                    every token of a chunk no longer than max_query_len
+ *   query_start    : device int32 [num_seqs + 1], non-decreasing, from 0
+ *   context_lens   : device int32 [num_seqs], each >= its chunk length
+ *   max_query_len  : host bound on every T_s (sizes the grid); tokens of a
+ *                    longer chunk are not computed
+ * Only fp16 and bf16 caches (head_dim 64 or 128, any supported block size).
+ * A sequence whose context length is below its chunk length or above
+ * max_blocks_per_seq * block_size gets NaN rows, as does one whose needed
+ * table entries name a block outside the pool. */
+pa_status pa_paged_prefill_attention(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* query_start, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t max_query_len,
+                                     int32_t num_q_heads, float scale, void* out,
+                                     const pa_cache_desc* cache, pa_stream_t stream);
+
 /* ---------------------------------------------------------------- block pool */
 
 /* Host-side owner of one block pool: which pool block holds which positions
