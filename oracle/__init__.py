@@ -26,7 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
 
-F32, F16, BF16, I8 = 0, 1, 2, 3
+F32, F16, BF16, I8, FP8 = 0, 1, 2, 3, 4
 _ERRORS = {
     -1: "bad argument",
     -2: "slot outside the pool",
@@ -73,6 +73,13 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_slot_mapping.argtypes = [P, i32, P, P, i64, i32, P]
     lib.oracle_decode_slot_mapping.argtypes = [P, i32, P, i32, i32, P]
     lib.oracle_kv_append.argtypes = [P, P, P, i64, P, P, i32, i32, i32, i32, i32]
+    lib.oracle_fp8_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_e4m3_to_double.restype = dbl
+    lib.oracle_double_to_fp8_e4m3.argtypes = [dbl]
+    lib.oracle_double_to_fp8_e4m3.restype = ctypes.c_uint8
+    lib.oracle_quantize_row_fp8.argtypes = [P, i32, P, P]
+    lib.oracle_quantize_row_fp8.restype = None
+    lib.oracle_kv_append_fp8.argtypes = [P, P, P, i64, P, P, P, P, i32, i32, i32, i32]
     lib.oracle_quantize_row_int8.argtypes = [P, i32, P, P]
     lib.oracle_quantize_row_int8.restype = None
     lib.oracle_kv_append_int8.argtypes = [P, P, P, i64, P, P, P, P, i32, i32, i32, i32]
@@ -90,7 +97,7 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_kv_bytes_per_token.restype = i64
     lib.oracle_max_threads.restype = i32
     for name in ("oracle_slot_mapping", "oracle_decode_slot_mapping", "oracle_kv_append",
-                 "oracle_kv_append_int8", "oracle_attention_dense",
+                 "oracle_kv_append_int8", "oracle_kv_append_fp8", "oracle_attention_dense",
                  "oracle_paged_decode_attention", "oracle_paged_prefill_attention",
                  "oracle_gather_kv"):
         getattr(lib, name).restype = ctypes.c_int
@@ -123,6 +130,8 @@ def _dtype_code(a: np.ndarray, bf16: bool = False) -> int:
         return BF16 if bf16 else F16
     if a.dtype == np.int8:
         return I8
+    if a.dtype == np.uint8:          # fp8 E4M3 codes
+        return FP8
     raise TypeError(f"unsupported oracle dtype {a.dtype}")
 
 
@@ -186,6 +195,34 @@ def kv_append_int8(k_new, v_new, slots, k_cache, v_cache, k_scale, v_scale, lib=
     vn = np.ascontiguousarray(v_new, dtype=np.float16).view(np.uint16)
     assert k_cache.dtype == np.int8 and k_scale.dtype == np.float16
     _check((lib or load()).oracle_kv_append_int8(
+        _ptr(kn), _ptr(vn), _ptr(slots), slots.shape[0], _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale.view(np.uint16)), _ptr(v_scale.view(np.uint16)), nb, hkv, bs, d))
+
+
+def fp8_e4m3_to_double(code: int, lib=None) -> float:
+    return (lib or load()).oracle_fp8_e4m3_to_double(code)
+
+
+def double_to_fp8_e4m3(x: float, lib=None) -> int:
+    return int((lib or load()).oracle_double_to_fp8_e4m3(x))
+
+
+def quantize_row_fp8(x_f16: np.ndarray, lib=None):
+    """(uint8 E4M3 codes, fp16 scale) of one row."""
+    x = np.ascontiguousarray(x_f16, dtype=np.float16).view(np.uint16)
+    q = np.empty(x.shape[0], dtype=np.uint8)
+    s = np.empty(1, dtype=np.uint16)
+    (lib or load()).oracle_quantize_row_fp8(_ptr(x), x.shape[0], _ptr(q), _ptr(s))
+    return q, s.view(np.float16)[0]
+
+
+def kv_append_fp8(k_new, v_new, slots, k_cache, v_cache, k_scale, v_scale, lib=None) -> None:
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    nb, hkv, bs, d = k_cache.shape
+    kn = np.ascontiguousarray(k_new, dtype=np.float16).view(np.uint16)
+    vn = np.ascontiguousarray(v_new, dtype=np.float16).view(np.uint16)
+    assert k_cache.dtype == np.uint8 and k_scale.dtype == np.float16
+    _check((lib or load()).oracle_kv_append_fp8(
         _ptr(kn), _ptr(vn), _ptr(slots), slots.shape[0], _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale.view(np.uint16)), _ptr(v_scale.view(np.uint16)), nb, hkv, bs, d))
 

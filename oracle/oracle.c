@@ -25,6 +25,9 @@
  *     cache").
  *   - append: the new token's K and V rows are stored into the cache
  *     ([notes] step 4; [guide] "How the cache turns the loop cheap").
+ *   - fp8 (E4M3) cache: the same scheme with 8-bit floating-point codes
+ *     ([viz] "What the page leaves out" names 8- and 4-bit caches).  PARITY
+ *     UNPINNED for the exact codes, as for int8.
  *   - int8 cache ([notes] "How serving systems tame the cost", "Quantized KV
  *     cache"): the pages name the format only; the symmetric per-(token, head)
  *     absmax quantizer below is this project's reading.  PARITY UNPINNED by
@@ -50,7 +53,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_FP8 = 4 };
 
 enum {
   OR_OK = 0,
@@ -86,6 +89,35 @@ double oracle_bf16_to_double(uint16_t b) {
   float f;
   memcpy(&f, &u, sizeof f);
   return (double)f;
+}
+
+/* OCP 8-bit floating point E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits
+ * (bias 7), 3 fraction bits.  Exponent field 0 holds the subnormals
+ * frac/8 * 2^-6; S.1111.111 is NaN; there are no infinities, so the largest
+ * finite magnitude is 1.75 * 2^8 = 448. */
+double oracle_fp8_e4m3_to_double(uint8_t b) {
+  int sign = b >> 7, expo = (b >> 3) & 15, frac = b & 7;
+  if (expo == 15 && frac == 7) return NAN;
+  double v = expo == 0 ? ldexp((double)frac, -9) : ldexp(8.0 + frac, expo - 10);
+  return sign ? -v : v;
+}
+
+/* The E4M3 code nearest to x, found by trying every finite code; a tie goes
+ * to the code with an even last bit.  Magnitudes above 448 give +-448
+ * (saturation); NaN gives 0. */
+uint8_t oracle_double_to_fp8_e4m3(double x) {
+  if (x != x) return 0;
+  double a = fabs(x);
+  int best = 0;
+  double best_err = a;  /* code 0 is the value 0 */
+  for (int c = 1; c < 127; ++c) {
+    double err = fabs(oracle_fp8_e4m3_to_double((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(best | (x < 0 && best != 0 ? 0x80 : 0));
 }
 
 /* Round a finite non-negative value to the nearest binary16 value, ties to
@@ -128,6 +160,7 @@ static size_t elem_bytes(int dtype) {
     case OR_F16: return 2;
     case OR_BF16: return 2;
     case OR_I8: return 1;
+    case OR_FP8: return 1;
     default: return 0;
   }
 }
@@ -152,6 +185,8 @@ static double load_elem(const void* base, int dtype, size_t idx) {
     }
     case OR_I8:
       return (double)((const int8_t*)base)[idx];
+    case OR_FP8:
+      return oracle_fp8_e4m3_to_double(((const uint8_t*)base)[idx]);
     default:
       return NAN;
   }
@@ -296,6 +331,68 @@ int oracle_kv_append_int8(const uint16_t* k_new, const uint16_t* v_new,
   return OR_OK;
 }
 
+/* fp8 quantizer for one row of fp16 values: the int8 scheme above with E4M3
+ * codes ("8-bit or 4-bit" cache quantization: [viz] "What the page leaves
+ * out"; the format and the per-(token, head) scale are this project's
+ * reading, PARITY UNPINNED like the int8 codes):
+ *   a = max |x|                            (exact)
+ *   s = binary16 nearest to fp32(a / 448)  (fp32 IEEE division, then RNE)
+ *   code = E4M3 nearest to fp32(x / s), ties to even, saturating at +-448;
+ *   code = 0 when s == 0 (and for a NaN input).                              */
+void oracle_quantize_row_fp8(const uint16_t* x_f16, int32_t n, uint8_t* q,
+                             uint16_t* scale_f16) {
+  float a = 0.0f;
+  for (int32_t d = 0; d < n; ++d) {
+    float ax = fabsf((float)oracle_f16_to_double(x_f16[d]));
+    if (ax > a) a = ax;
+  }
+  volatile float ratio = a / 448.0f; /* binary32 quotient */
+  uint16_t sbits = oracle_double_to_f16_bits((double)ratio);
+  float s = (float)oracle_f16_to_double(sbits);
+  *scale_f16 = sbits;
+  for (int32_t d = 0; d < n; ++d) {
+    if (s == 0.0f) {
+      q[d] = 0;
+      continue;
+    }
+    volatile float r = (float)oracle_f16_to_double(x_f16[d]) / s; /* binary32 */
+    q[d] = oracle_double_to_fp8_e4m3((double)r);
+  }
+}
+
+/* Append into an fp8 cache: quantize each (token, head) row, then store the
+ * codes and the scale at the token's slot. */
+int oracle_kv_append_fp8(const uint16_t* k_new, const uint16_t* v_new,
+                         const int64_t* slots, int64_t num_tokens,
+                         uint8_t* k_cache, uint8_t* v_cache, uint16_t* k_scale,
+                         uint16_t* v_scale, int32_t num_blocks,
+                         int32_t num_kv_heads, int32_t block_size,
+                         int32_t head_dim) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 ||
+      block_size <= 0 || head_dim <= 0)
+    return OR_BAD_ARG;
+  int64_t pool_slots = (int64_t)num_blocks * block_size;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    if (slots[t] >= pool_slots) return OR_BAD_SLOT;
+    if (slots[t] < 0) continue;
+    for (int64_t u = 0; u < t; ++u)
+      if (slots[u] == slots[t]) return OR_DUP_SLOT;
+  }
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    if (slots[t] < 0) continue;
+    int64_t block = slots[t] / block_size, off = slots[t] % block_size;
+    for (int32_t h = 0; h < num_kv_heads; ++h) {
+      size_t src = ((size_t)t * num_kv_heads + h) * head_dim;
+      size_t srow = ((size_t)block * num_kv_heads + h) * block_size + off;
+      oracle_quantize_row_fp8(k_new + src, head_dim, k_cache + srow * head_dim,
+                              &k_scale[srow]);
+      oracle_quantize_row_fp8(v_new + src, head_dim, v_cache + srow * head_dim,
+                              &v_scale[srow]);
+    }
+  }
+  return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Attention of one query over n cached rows, straight from the definition
  * softmax(q . K^T * scale) . V ([notes] "Concept"), in fp64:
@@ -347,7 +444,7 @@ static int unpage(const void* k_cache, const void* v_cache,
     if (block < 0 || block >= num_blocks) return OR_BAD_BLOCK;
     size_t row = ((size_t)block * num_kv_heads + kvh) * block_size + i % block_size;
     double sk = 1.0, sv = 1.0;
-    if (dtype == OR_I8) {
+    if (dtype == OR_I8 || dtype == OR_FP8) {
       sk = oracle_f16_to_double(k_scale[row]);
       sv = oracle_f16_to_double(v_scale[row]);
     }
@@ -378,7 +475,8 @@ int oracle_paged_decode_attention(
       num_q_heads % num_kv_heads != 0 || block_size <= 0 || head_dim <= 0 ||
       max_blocks <= 0 || !elem_bytes(cache_dtype) || !elem_bytes(q_dtype))
     return OR_BAD_ARG;
-  if (cache_dtype == OR_I8 && (!k_scale || !v_scale)) return OR_BAD_ARG;
+  if ((cache_dtype == OR_I8 || cache_dtype == OR_FP8) && (!k_scale || !v_scale))
+    return OR_BAD_ARG;
   for (int32_t s = 0; s < num_seqs; ++s)
     if (context_lens[s] < 0 || context_lens[s] > max_blocks * block_size)
       return OR_BAD_CTX;
@@ -450,7 +548,8 @@ int oracle_paged_prefill_attention(
       max_blocks <= 0 || !elem_bytes(cache_dtype) || !elem_bytes(q_dtype) ||
       !query_start || query_start[0] != 0)
     return OR_BAD_ARG;
-  if (cache_dtype == OR_I8 && (!k_scale || !v_scale)) return OR_BAD_ARG;
+  if ((cache_dtype == OR_I8 || cache_dtype == OR_FP8) && (!k_scale || !v_scale))
+    return OR_BAD_ARG;
   for (int32_t s = 0; s < num_seqs; ++s) {
     int32_t t = query_start[s + 1] - query_start[s];
     if (t < 0) return OR_BAD_ARG;

@@ -449,6 +449,96 @@ def pin_int8_attention_dequantizes_exactly(lib):
     assert a.tobytes() == b.tobytes()
 
 
+# ---------------------------------------------------------------- fp8 (E4M3)
+
+def _e4m3_table():
+    """torch's float8_e4m3fn decoding of every code (library routine)."""
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def pin_fp8_e4m3_decode_exhaustive(lib):
+    ref = _e4m3_table()
+    got = np.array([oracle.fp8_e4m3_to_double(c, lib) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9
+
+
+def pin_fp8_e4m3_encode(lib):
+    """Every finite code round-trips; a value halfway between two neighbours
+    goes to the one with the even code (as torch's cast does); a hair off the
+    midpoint goes to the nearer; above 448 saturates (this project's reading:
+    torch rounds magnitudes past 464 to NaN); NaN encodes as 0."""
+    enc = lambda x: oracle.double_to_fp8_e4m3(float(x), lib)
+    vals = _e4m3_table()[:127]            # 0 .. 448, increasing
+    for c in range(127):
+        assert enc(vals[c]) == c
+        if c:
+            assert enc(-vals[c]) == c | 0x80
+    for c in range(126):
+        a, b = vals[c], vals[c + 1]
+        mid = (a + b) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert enc(mid) == even
+        assert enc(mid) == torch.tensor(mid, dtype=torch.float64).to(
+            torch.float8_e4m3fn).view(torch.uint8).item()
+        assert enc(mid + (b - a) * 1e-6) == c + 1 and enc(mid - (b - a) * 1e-6) == c
+    assert enc(449.0) == 0x7E and enc(1e6) == 0x7E and enc(-1e6) == 0xFE
+    assert enc(float("nan")) == 0
+
+
+def pin_fp8_quantizer(lib):
+    # worked by hand: 1/448 = 0.0022321... lies in [2^-9, 2^-8) where binary16
+    # steps by 2^-19; 0.0022321 / 2^-19 = 1170.3 -> 1170, s = 1170 * 2^-19.
+    # 1/s = 448.11 saturates to 448 (0x7E); -0.5/s = -224.05 -> -224 = -1.75*2^7
+    # (0xF6); 0.25/s = 112.03 -> 112 = 1.75*2^6 (0x6E); 0.001/s = 0.4483 ->
+    # 0.4375 = 1.75*2^-2 (0x2E), the E4M3 step in [0.25, 0.5) being 2^-5.
+    x = np.array([1.0, -0.5, 0.25, 0.001] + [0.0] * 4, np.float16)
+    q, s = oracle.quantize_row_fp8(x, lib=lib)
+    assert float(s) == 1170 * 2.0 ** -19
+    assert q.tolist() == [0x7E, 0xF6, 0x6E, 0x2E, 0, 0, 0, 0]
+    q, s = oracle.quantize_row_fp8(np.zeros(16, np.float16), lib=lib)
+    assert float(s) == 0 and (q == 0).all()
+    table = _e4m3_table()
+    rng = np.random.default_rng(17)
+    for _ in range(200):
+        x = (rng.standard_normal(128) * rng.uniform(0.01, 100)).astype(np.float16)
+        q, s = oracle.quantize_row_fp8(x, lib=lib)
+        s = float(s)
+        xf = x.astype(np.float64)
+        deq = s * table[q]
+        # half an E4M3 step (2^-4 relative, or 2^-10 absolute among the
+        # subnormals) plus the rounding of the scale
+        assert np.all(np.abs(xf - deq) <= np.abs(xf) * (2.0 ** -4 + 2.0 ** -10)
+                      + s * 2.0 ** -10 * 1.0001)
+        qn, sn = oracle.quantize_row_fp8(-x, lib=lib)
+        assert float(sn) == s and np.array_equal(qn, np.where(q == 0, 0, q ^ 0x80))
+
+
+def pin_fp8_attention_dequantizes_exactly(lib):
+    """The fp8 path equals the float path on code * scale, exact in binary32
+    (4 significant bits times 11)."""
+    rng = np.random.default_rng(18)
+    nb, hkv, bs, d, hq = 10, 2, 4, 32, 4
+    src_k = rng.standard_normal((nb * bs, hkv, d)).astype(np.float16)
+    src_v = rng.standard_normal((nb * bs, hkv, d)).astype(np.float16)
+    kq = np.zeros((nb, hkv, bs, d), np.uint8)
+    vq = np.zeros_like(kq)
+    ks = np.zeros((nb, hkv, bs), np.float16)
+    vs = np.zeros_like(ks)
+    oracle.kv_append_fp8(src_k, src_v, np.arange(nb * bs, dtype=np.int64), kq, vq, ks, vs,
+                         lib=lib)
+    table = _e4m3_table().astype(np.float32)
+    kf = (table[kq] * ks[..., None].astype(np.float32)).astype(np.float32)
+    vf = (table[vq] * vs[..., None].astype(np.float32)).astype(np.float32)
+    bt = rng.permutation(nb)[:8].reshape(2, 4).astype(np.int32)
+    ctx = np.array([13, 16], np.int32)
+    q = rng.standard_normal((2, hq, d)).astype(np.float16)
+    a = oracle.paged_decode_attention(q, kq, vq, bt, ctx, 0.2, k_scale=ks, v_scale=vs, lib=lib)
+    b = oracle.paged_decode_attention(q, kf, vf, bt, ctx, 0.2, lib=lib)
+    assert a.tobytes() == b.tobytes()
+
+
 # ---------------------------------------------------------------- prefill
 
 def _sdpa64_rows(q, K, V, scale, mask):

@@ -44,6 +44,13 @@ MUTANTS = {
                                                 "int32_t n = pos;                    /*"),
     "prefill token given to the previous sequence": (
         "while (query_start[s + 1] <= tok) ++s;", "while (query_start[s + 1] < tok) ++s;"),
+    "fp8 exponent bias off by one": ("ldexp(8.0 + frac, expo - 10)", "ldexp(8.0 + frac, expo - 9)"),
+    "fp8 subnormals scaled as normals": ("ldexp((double)frac, -9)", "ldexp((double)frac, -10)"),
+    "fp8 ties to odd": ("(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
+    "fp8 quantizer range 240": ("volatile float ratio = a / 448.0f;",
+                                "volatile float ratio = a / 240.0f;"),
+    "fp8 scales ignored by attention": ("if (dtype == OR_I8 || dtype == OR_FP8) {\n      sk",
+                                        "if (dtype == OR_I8) {\n      sk"),
     "dot product over half the head": (
         "for (int32_t d = 0; d < head_dim; ++d) dot += q[d] * K[i * head_dim + d];",
         "for (int32_t d = 0; d < head_dim / 2; ++d) dot += q[d] * K[i * head_dim + d];"),
