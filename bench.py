@@ -62,12 +62,14 @@ class Bench:
         lay = self.layout
         self.bt = lay.block_tables.to(dev)
         self.ctx = lay.context_lens.to(dev)
-        self.int8 = shape.cache_dtype == "i8"
+        # quantized caches (int8, fp8): codes + fp16 scales, appended by the
+        # quantizing append; attention reads them through the partitions call
+        self.quant = shape.cache_dtype in W.QUANTIZED
         self.append = shape.name != W.LLAMA2_70B.name   # shared-prefix blocks are not appended
         self.cases = []
         for layer in range(layers):
             c = W.make_case(shape, lay, device=dev, seed=layer, poison=False)
-            if self.int8:
+            if self.quant:
                 c = self._quantize(c)
             self.cases.append(c)
         s, hq, d = shape.num_seqs, shape.num_q_heads, shape.head_dim
@@ -83,15 +85,19 @@ class Bench:
         self.outs = [torch.empty_like(c.q) for c in self.cases]
         self.slots = torch.empty(s, dtype=torch.int64, device=dev)
 
+    def quant_append(self, *args):
+        (pa.kv_append_int8 if self.shape.cache_dtype == "i8" else pa.kv_append_fp8)(*args)
+
     def _quantize(self, c):
         nb, hkv, bs, d = c.k_cache.shape
         rows = lambda x: x.permute(0, 2, 1, 3).reshape(nb * bs, hkv, d).contiguous()
         slots = torch.arange(nb * bs, dtype=torch.int64, device=self.dev)
-        kq = torch.empty((nb, hkv, bs, d), dtype=torch.int8, device=self.dev)
+        kq = torch.empty((nb, hkv, bs, d), dtype=W.TORCH_DTYPE[self.shape.cache_dtype],
+                         device=self.dev)
         vq = torch.empty_like(kq)
         ks = torch.empty((nb, hkv, bs), dtype=torch.float16, device=self.dev)
         vs = torch.empty_like(ks)
-        pa.kv_append_int8(rows(c.k_cache), rows(c.v_cache), slots, kq, vq, ks, vs)
+        self.quant_append(rows(c.k_cache), rows(c.v_cache), slots, kq, vq, ks, vs)
         torch.cuda.synchronize()
         c.k_cache, c.v_cache = kq, vq
         c.k_scale, c.v_scale = ks, vs
@@ -100,13 +106,13 @@ class Bench:
     def step(self):
         """One decode step over every layer."""
         sh = self.shape
-        fused_append = self.append and not self.int8 and not self.separate
+        fused_append = self.append and not self.quant and not self.separate
         if self.append and not fused_append:
             pa.decode_slot_mapping(self.bt, self.ctx, sh.block_size, out=self.slots)
         for layer, c in enumerate(self.cases):
             if self.append and not fused_append:
-                if self.int8:
-                    pa.kv_append_int8(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache,
+                if self.quant:
+                    self.quant_append(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache,
                                       c.k_scale, c.v_scale)
                 else:
                     pa.kv_append(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache)
@@ -130,7 +136,7 @@ class Bench:
 
     @property
     def fused_append(self) -> bool:
-        return self.append and not self.int8 and not self.separate
+        return self.append and not self.quant and not self.separate
 
     def kv_bytes_per_layer(self) -> int:
         return W.kv_bytes_per_layer_step(self.shape, self.layout.context_lens.tolist())
@@ -155,8 +161,8 @@ def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
     c = b.cases[0]
     lay = b.layout
     host = W.to_numpy_bits
-    args = dict(k_scale=host(c.k_scale) if b.int8 else None,
-                v_scale=host(c.v_scale) if b.int8 else None,
+    args = dict(k_scale=host(c.k_scale) if b.quant else None,
+                v_scale=host(c.v_scale) if b.quant else None,
                 bf16=b.shape.cache_dtype == "bf16")
     q, kc, vc = host(c.q), host(c.k_cache), host(c.v_cache)
     bt, ctx = host(lay.block_tables), host(lay.context_lens)

@@ -20,6 +20,7 @@ __all__ = [
     "PagedAttnError", "library", "CacheDesc", "slot_mapping", "decode_slot_mapping",
     "kv_append", "kv_append_int8", "decode_workspace_bytes", "decode_partition_tokens",
     "paged_decode_attention", "paged_decode_attention_int8", "decode_step", "decode_partitions",
+    "kv_append_fp8", "paged_decode_attention_fp8",
     "decode_step_partitions", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
     "BlockManager", "copy_blocks", "paged_prefill_attention",
 ]
@@ -29,7 +30,10 @@ __all__ = [
 LIBRARY_PATH = os.environ.get(
     "PA_LIBRARY_PATH",
     os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so"))
-DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int8: 3}
+# fp8 caches hold OCP E4M3 codes (torch.float8_e4m3fn storage).
+DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int8: 3,
+              torch.float8_e4m3fn: 4}
+QUANTIZED = (torch.int8, torch.float8_e4m3fn)
 CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 
 
@@ -79,8 +83,10 @@ def _declare(lib):
         "pa_decode_slot_mapping": [P, i32, P, i32, i32, P, P],
         "pa_kv_append": [P, P, P, i64, P, P, D, P],
         "pa_kv_append_int8": [P, P, P, i64, P, P, P, P, D, P],
+        "pa_kv_append_fp8": [P, P, P, i64, P, P, P, P, D, P],
         "pa_paged_decode_attention": [P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
         "pa_paged_decode_attention_int8": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
+        "pa_paged_decode_attention_fp8": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
         "pa_decode_partitions": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D, P, sz, P],
         "pa_lse_merge": [P, sz, P, i32, i32, i32, i32, i32, i32, i32, P, P],
         "pa_decode_step": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
@@ -210,6 +216,24 @@ def kv_append_int8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scal
                               _stream(k_cache)), lib)
 
 
+def kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale):
+    """Quantize fp16 rows [T, Hkv, D] to fp8 E4M3 codes + fp16 scales."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    t = slot_mapping.numel()
+    if k_new.shape != (t, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{t}, {desc.num_kv_heads}, {desc.head_dim}]")
+    if k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_scale.shape:
+        raise ValueError("scales must be [NB, Hkv, BS]")
+    e4m3 = torch.float8_e4m3fn
+    _ok(lib.pa_kv_append_fp8(_dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),
+                             _dev(slot_mapping, "slot_mapping", torch.int64), t,
+                             _dev(k_cache, "k_cache", e4m3, 4), _dev(v_cache, "v_cache", e4m3, 4),
+                             _dev(k_scale, "k_scale", torch.float16),
+                             _dev(v_scale, "v_scale", torch.float16), ctypes.byref(desc),
+                             _stream(k_cache)), lib)
+
+
 # ---------------------------------------------------------------- attention
 
 def decode_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks, partition_tokens=0) -> int:
@@ -277,6 +301,25 @@ def paged_decode_attention_int8(q, k_cache, v_cache, k_scale, v_scale, block_tab
     return out
 
 
+def paged_decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                               context_lens, scale, out, workspace=None):
+    """Decode attention over an fp8 (E4M3) cache with fp16 per-(token, head) scales."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    need = decode_workspace_bytes(desc, s, hq, maxb)
+    ws = _workspace(workspace, need, q.device)
+    e4m3 = torch.float8_e4m3fn
+    _ok(lib.pa_paged_decode_attention_fp8(
+        _dev(q, "q", torch.float16, 3), _dev(k_cache, "k_cache", e4m3, 4),
+        _dev(v_cache, "v_cache", e4m3, 4), _dev(k_scale, "k_scale", torch.float16),
+        _dev(v_scale, "v_scale", torch.float16), _dev(block_tables, "block_tables", torch.int32),
+        maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
+        _dev(out, "out", torch.float16), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _stream(q)), lib)
+    return out
+
+
 def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
                 workspace=None):
     """One decode step: store each sequence's k_new/v_new [S, Hkv, D] rows at
@@ -305,7 +348,7 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     lib = library()
     desc = CacheDesc.of(k_cache)
     s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
-    q_dtype = torch.float16 if k_cache.dtype == torch.int8 else k_cache.dtype
+    q_dtype = torch.float16 if k_cache.dtype in QUANTIZED else k_cache.dtype
     _ok(lib.pa_decode_partitions(
         _dev(q, "q", q_dtype, 3), _dev(k_cache, "k_cache", ndim=4),
         _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(k_scale, "k_scale", torch.float16),
@@ -493,7 +536,7 @@ def copy_blocks(k_cache, v_cache, block_pairs, k_scale=None, v_scale=None):
         block_pairs = torch.as_tensor(np.ascontiguousarray(block_pairs, np.int32).reshape(-1, 2),
                                       device=k_cache.device)
     n = block_pairs.shape[0]
-    i8 = k_cache.dtype == torch.int8
+    i8 = k_cache.dtype in QUANTIZED
     desc = CacheDesc.of(k_cache)
     _ok(lib.pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(k_scale, "k_scale", torch.float16) if i8 else None,

@@ -44,9 +44,13 @@ int elem_bytes(int32_t dtype) {
     case PA_F16: return 2;
     case PA_BF16: return 2;
     case PA_I8: return 1;
+    case PA_FP8: return 1;
     default: return 0;
   }
 }
+
+// int8 or fp8 (E4M3) codes with fp16 per-(token, head) scales
+bool quantized(int32_t dtype) { return dtype == PA_I8 || dtype == PA_FP8; }
 
 bool supported_block(int32_t bs) { return bs == 4 || bs == 8 || bs == 16 || bs == 32; }
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
@@ -147,7 +151,8 @@ pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_head
     const int64_t unit = (int64_t)p.tile * pa::kDecodeWaves;
     const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads * p.chunks;
     const int64_t target = !p.mfma ? kTargetWorkgroups
-                           : c->dtype == PA_I8 ? kTargetWorkgroupsMfmaInt8 : kTargetWorkgroupsMfma;
+                           : quantized(c->dtype) ? kTargetWorkgroupsMfmaInt8
+                                                 : kTargetWorkgroupsMfma;
     const int64_t want_parts = (target + units - 1) / units;
     part = (max_tok + want_parts - 1) / want_parts;
     part = std::max<int64_t>(part, kMinPartitionTokens);
@@ -173,8 +178,8 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
                          const void* v_new = nullptr) {
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PA_ERR_INVALID_ARG, "NULL tensor pointer");
-  if (cache->dtype == PA_I8 && (!k_scale || !v_scale))
-    return fail(PA_ERR_INVALID_ARG, "int8 cache needs k_scale and v_scale");
+  if (quantized(cache->dtype) && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARG, "a quantized cache needs k_scale and v_scale");
   if (plan.num_parts > 1 && (!workspace || workspace_bytes < plan.ws_bytes))
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes,
                 plan.ws_bytes);
@@ -207,6 +212,7 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
       case PA_F16: e = pa::launch_mfma_f16(p, D, BS, plan.gc, num_seqs, stream); break;
       case PA_BF16: e = pa::launch_mfma_bf16(p, D, BS, plan.gc, num_seqs, stream); break;
       case PA_I8: e = pa::launch_mfma_i8(p, D, BS, plan.gc, num_seqs, stream); break;
+      case PA_FP8: e = pa::launch_mfma_fp8(p, D, BS, plan.gc, num_seqs, stream); break;
       default: return fail(PA_ERR_UNSUPPORTED, "dtype %d", cache->dtype);
     }
     return hip_status(e, "decode partitions launch");
@@ -216,6 +222,7 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
     case PA_F16: e = pa::launch_decode_f16(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
     case PA_BF16: e = pa::launch_decode_bf16(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
     case PA_I8: e = pa::launch_decode_i8(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
+    case PA_FP8: e = pa::launch_decode_fp8(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
     default: return fail(PA_ERR_UNSUPPORTED, "dtype %d", cache->dtype);
   }
   return hip_status(e, "decode partitions launch");
@@ -236,20 +243,25 @@ pa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
                         int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
                         int32_t num_q_heads, float scale, void* out, const pa_cache_desc* cache,
                         void* workspace, size_t workspace_bytes, hipStream_t stream,
-                        bool want_int8, const void* k_new = nullptr,
+                        int32_t want_dtype, const void* k_new = nullptr,
                         const void* v_new = nullptr) {
   Plan plan;
   pa_status st = make_plan(cache, num_seqs, num_q_heads, max_blocks, 0, &plan);
   if (st != PA_OK) return st;
-  if ((cache->dtype == PA_I8) != want_int8)
-    return fail(PA_ERR_UNSUPPORTED, want_int8 ? "int8 entry point needs an int8 cache"
-                                              : "int8 cache: use pa_paged_decode_attention_int8");
+  // want_dtype: the quantized format an entry point is for, or -1 for the
+  // entry points of unquantized caches.
+  if (want_dtype >= 0 ? cache->dtype != want_dtype : quantized(cache->dtype))
+    return fail(PA_ERR_UNSUPPORTED,
+                want_dtype == PA_I8    ? "the int8 entry point needs an int8 cache"
+                : want_dtype == PA_FP8 ? "the fp8 entry point needs an fp8 cache"
+                : cache->dtype == PA_I8 ? "int8 cache: use pa_paged_decode_attention_int8"
+                                        : "fp8 cache: use pa_paged_decode_attention_fp8");
   if (num_seqs == 0) return PA_OK;
   st = run_partitions(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks,
                       context_lens, num_seqs, num_q_heads, scale, out, cache, plan, workspace,
                       workspace_bytes, stream, k_new, v_new);
   if (st != PA_OK || plan.num_parts == 1) return st;
-  const int32_t out_dtype = cache->dtype == PA_I8 ? PA_F16 : cache->dtype;
+  const int32_t out_dtype = quantized(cache->dtype) ? PA_F16 : cache->dtype;
   return run_merge(plan, workspace, context_lens, num_seqs, num_q_heads, cache->head_dim,
                    max_blocks * cache->block_size, out_dtype, out, stream);
 }
@@ -312,8 +324,8 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot
                        const pa_cache_desc* cache, pa_stream_t stream) {
   pa_status st = check_cache(cache);
   if (st != PA_OK) return st;
-  if (cache->dtype == PA_I8)
-    return fail(PA_ERR_UNSUPPORTED, "int8 cache: use pa_kv_append_int8");
+  if (quantized(cache->dtype))
+    return fail(PA_ERR_UNSUPPORTED, "quantized cache: use pa_kv_append_int8 or pa_kv_append_fp8");
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
@@ -326,22 +338,43 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, const int64_t* slot
                     "kv_append launch");
 }
 
-pa_status pa_kv_append_int8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
-                            int64_t num_tokens, int8_t* k_cache, int8_t* v_cache, void* k_scale,
-                            void* v_scale, const pa_cache_desc* cache, pa_stream_t stream) {
+namespace {
+
+pa_status kv_append_quantized(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                              int64_t num_tokens, void* k_cache, void* v_cache, void* k_scale,
+                              void* v_scale, const pa_cache_desc* cache, int32_t want,
+                              hipStream_t stream) {
   pa_status st = check_cache(cache);
   if (st != PA_OK) return st;
-  if (cache->dtype != PA_I8) return fail(PA_ERR_UNSUPPORTED, "pa_kv_append_int8 needs an int8 cache");
+  if (cache->dtype != want)
+    return fail(PA_ERR_UNSUPPORTED, want == PA_I8 ? "pa_kv_append_int8 needs an int8 cache"
+                                                  : "pa_kv_append_fp8 needs an fp8 cache");
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
     return fail(PA_ERR_INVALID_ARG, "NULL pointer");
-  return hip_status(pa::launch_kv_append_int8(k_new, v_new, slot_mapping, num_tokens, k_cache,
-                                              v_cache, k_scale, v_scale, cache->num_kv_heads,
-                                              cache->block_size, cache->head_dim,
-                                              (int64_t)cache->num_blocks * cache->block_size,
-                                              (hipStream_t)stream),
-                    "kv_append_int8 launch");
+  return hip_status(pa::launch_kv_append_quant(k_new, v_new, slot_mapping, num_tokens, k_cache,
+                                               v_cache, k_scale, v_scale, cache->num_kv_heads,
+                                               cache->block_size, cache->head_dim,
+                                               (int64_t)cache->num_blocks * cache->block_size,
+                                               want == PA_FP8, stream),
+                    "quantizing append launch");
+}
+
+}  // namespace
+
+pa_status pa_kv_append_int8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                            int64_t num_tokens, int8_t* k_cache, int8_t* v_cache, void* k_scale,
+                            void* v_scale, const pa_cache_desc* cache, pa_stream_t stream) {
+  return kv_append_quantized(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, k_scale,
+                             v_scale, cache, PA_I8, (hipStream_t)stream);
+}
+
+pa_status pa_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                           int64_t num_tokens, void* k_cache, void* v_cache, void* k_scale,
+                           void* v_scale, const pa_cache_desc* cache, pa_stream_t stream) {
+  return kv_append_quantized(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, k_scale,
+                             v_scale, cache, PA_FP8, (hipStream_t)stream);
 }
 
 size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
@@ -368,7 +401,7 @@ pa_status pa_paged_decode_attention(const void* q, const void* k_cache, const vo
                                     size_t workspace_bytes, pa_stream_t stream) {
   return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
-                       workspace_bytes, (hipStream_t)stream, false);
+                       workspace_bytes, (hipStream_t)stream, -1);
 }
 
 pa_status pa_paged_decode_attention_int8(const void* q, const int8_t* k_cache,
@@ -381,7 +414,20 @@ pa_status pa_paged_decode_attention_int8(const void* q, const int8_t* k_cache,
                                          size_t workspace_bytes, pa_stream_t stream) {
   return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
-                       workspace_bytes, (hipStream_t)stream, true);
+                       workspace_bytes, (hipStream_t)stream, PA_I8);
+}
+
+pa_status pa_paged_decode_attention_fp8(const void* q, const void* k_cache,
+                                        const void* v_cache, const void* k_scale,
+                                        const void* v_scale, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, float scale, void* out,
+                                        const pa_cache_desc* cache, void* workspace,
+                                        size_t workspace_bytes, pa_stream_t stream) {
+  return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
+                       workspace_bytes, (hipStream_t)stream, PA_FP8);
 }
 
 pa_status pa_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
@@ -407,12 +453,13 @@ pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, vo
                          size_t workspace_bytes, pa_stream_t stream) {
   pa_status st = check_cache(cache);
   if (st != PA_OK) return st;
-  if (cache->dtype == PA_I8)
-    return fail(PA_ERR_UNSUPPORTED, "int8 cache: use pa_kv_append_int8 + pa_paged_decode_attention_int8");
+  if (quantized(cache->dtype))
+    return fail(PA_ERR_UNSUPPORTED,
+                "quantized cache: append with pa_kv_append_int8/_fp8, then attend");
   if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
   return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
-                       workspace_bytes, (hipStream_t)stream, false, k_new, v_new);
+                       workspace_bytes, (hipStream_t)stream, -1, k_new, v_new);
 }
 
 pa_status pa_decode_step_partitions(const void* q, const void* k_new, const void* v_new,
@@ -425,8 +472,9 @@ pa_status pa_decode_step_partitions(const void* q, const void* k_new, const void
   Plan plan;
   pa_status st = make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan);
   if (st != PA_OK) return st;
-  if (cache->dtype == PA_I8)
-    return fail(PA_ERR_UNSUPPORTED, "int8 cache: use pa_kv_append_int8 + pa_decode_partitions");
+  if (quantized(cache->dtype))
+    return fail(PA_ERR_UNSUPPORTED,
+                "quantized cache: append with pa_kv_append_int8/_fp8, then pa_decode_partitions");
   if (num_seqs == 0) return PA_OK;
   if (!k_new || !v_new) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
   return run_partitions(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,
@@ -473,7 +521,7 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
   if (!k_cache || !v_cache || !block_tables || !context_lens || !k_out || !v_out)
     return fail(PA_ERR_INVALID_ARG, "NULL pointer");
   const int32_t row_bytes = cache->head_dim * elem_bytes(cache->dtype);
-  const bool i8 = cache->dtype == PA_I8;
+  const bool i8 = quantized(cache->dtype);
   return hip_status(pa::launch_gather_kv(k_cache, v_cache, i8 ? k_scale : nullptr,
                                          i8 ? v_scale : nullptr, block_tables, max_blocks_per_seq,
                                          context_lens, num_seqs, k_out, v_out,
@@ -543,7 +591,7 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_sc
   if (st != PA_OK) return st;
   if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs %d < 0", num_pairs);
   if (num_pairs == 0) return PA_OK;
-  const bool i8 = cache->dtype == PA_I8;
+  const bool i8 = quantized(cache->dtype);
   if (!k_cache || !v_cache || !block_pairs || (i8 && (!k_scale || !v_scale)))
     return fail(PA_ERR_INVALID_ARG, "NULL pointer");
   const int32_t row_bytes = cache->head_dim * elem_bytes(cache->dtype);

@@ -85,6 +85,8 @@ hipError_t launch_mfma_bf16(const DecodeParams& p, int head_dim, int bs, int gc,
                             hipStream_t stream);
 hipError_t launch_mfma_i8(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                           hipStream_t stream);
+hipError_t launch_mfma_fp8(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                           hipStream_t stream);
 
 hipError_t launch_decode_f32(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                              hipStream_t stream);
@@ -94,5 +96,7 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int head_dim, int bs, int g
                               hipStream_t stream);
 hipError_t launch_decode_i8(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                             hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                             hipStream_t stream);
 
 }  // namespace pa

@@ -41,7 +41,7 @@ struct DecodeParams {
   const void* q;
   const void* k_cache;
   const void* v_cache;
-  const uint16_t* k_scale;  // int8 cache only: fp16 [NB][Hkv][BS]
+  const uint16_t* k_scale;  // quantized caches only: fp16 [NB][Hkv][BS]
   const uint16_t* v_scale;
   const int32_t* block_tables;
   const int32_t* context_lens;
@@ -71,7 +71,7 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
     ((float*)out)[idx] = x;
   } else if constexpr (F == Fmt::BF16) {
     ((uint16_t*)out)[idx] = float_to_bf16_rne(x);
-  } else {  // fp16 output (also for the int8 cache)
+  } else {  // fp16 output (also for the quantized caches)
     ((uint16_t*)out)[idx] = float_to_f16_rne(x);
   }
 }
@@ -185,6 +185,39 @@ template <> struct Frag<Fmt::I8> {
   }
 };
 
+// fp8 E4M3 codes: 16 per fragment, dotted with 16 fp16 query values.  Codes
+// are widened to binary16 exactly as value * 2^-8 (e4m3_pair_to_f16); the
+// key/value scales carry the 2^8 (FmtInfo<FP8>::code_scale).
+template <> struct Frag<Fmt::FP8> {
+  static constexpr int VE = 16;
+  static constexpr int QW = 8;
+  __device__ static __forceinline__ void codes_to_half2(uint32_t w, h16x2& lo, h16x2& hi) {
+    lo = as_h2(e4m3_pair_to_f16(w, kE4m3Lo));
+    hi = as_h2(e4m3_pair_to_f16(w, kE4m3Hi));
+  }
+  __device__ static __forceinline__ float dot(const uint32_t* q, u32x4 k) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h16x2 lo, hi;
+      codes_to_half2(k[i], lo, hi);
+      s = __builtin_amdgcn_fdot2(as_h2(q[2 * i]), lo, s, false);
+      s = __builtin_amdgcn_fdot2(as_h2(q[2 * i + 1]), hi, s, false);
+    }
+    return s;
+  }
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h16x2 lo, hi;
+      codes_to_half2(v[i], lo, hi);
+      f[4 * i] = (float)lo[0];
+      f[4 * i + 1] = (float)lo[1];
+      f[4 * i + 2] = (float)hi[0];
+      f[4 * i + 3] = (float)hi[1];
+    }
+  }
+};
 
 // Result of one workgroup for one query head row of one sequence: final when
 // the partition is the sequence's only one, else a partial (running max M in
@@ -217,7 +250,7 @@ void decode_partition_kernel(const DecodeParams p) {
   constexpr int NJ = TT / RPI;                // fragments per lane per tile (K, and V)
   constexpr int BPT = TT / BS;                // blocks per tile
   constexpr int ROWB = D * CB;                // bytes per cached row
-  constexpr bool kInt8 = F == Fmt::I8;
+  constexpr bool kQuant = FmtInfo<F>::quantized;
   static_assert(LR >= 1 && LR <= kWave && (kWave % LR) == 0, "row must split over lanes");
   static_assert(TT % RPI == 0 && TT % BS == 0, "tile must be whole loads and blocks");
 
@@ -249,7 +282,7 @@ void decode_partition_kernel(const DecodeParams p) {
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
   // Fused append: the decoded token (position ctx-1) is this partition's last
   // row when tok_end == ctx.
-  if (!kInt8 && p.k_new != nullptr && tok_end == ctx)
+  if (!kQuant && p.k_new != nullptr && tok_end == ctx)
     append_new_rows<ROWB, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
 
   const int lrow = lane / LR;  // row of this lane inside a wave-load
@@ -320,9 +353,10 @@ void decode_partition_kernel(const DecodeParams p) {
         kf[j] = u32x4{0, 0, 0, 0};
         vf[j] = u32x4{0, 0, 0, 0};
       }
-      if constexpr (kInt8) {
-        ks[j] = valid ? (float)__builtin_bit_cast(_Float16, p.k_scale[row]) : 0.0f;
-        vs[j] = valid ? (float)__builtin_bit_cast(_Float16, p.v_scale[row]) : 0.0f;
+      if constexpr (kQuant) {
+        constexpr float cs = FmtInfo<F>::code_scale;
+        ks[j] = valid ? (float)__builtin_bit_cast(_Float16, p.k_scale[row]) * cs : 0.0f;
+        vs[j] = valid ? (float)__builtin_bit_cast(_Float16, p.v_scale[row]) * cs : 0.0f;
       } else {
         ks[j] = 1.0f;
         vs[j] = 1.0f;
@@ -338,7 +372,7 @@ void decode_partition_kernel(const DecodeParams p) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const float d = group_sum<LR>(FR::dot(qf[g], kf[j]));
-        z[g][j] = kInt8 ? d * (ks[j] * p.scale_log2) : d * p.scale_log2;
+        z[g][j] = kQuant ? d * (ks[j] * p.scale_log2) : d * p.scale_log2;
         if (PARTIAL && j * RPI + lrow >= nvalid) z[g][j] = -__builtin_inff();
       }
     }
@@ -360,7 +394,7 @@ void decode_partition_kernel(const DecodeParams p) {
       for (int j = 0; j < NJ; ++j) {
         const float pj = fast_exp2(z[g][j] - mn);
         lsum += pj;
-        const float pv = kInt8 ? pj * vs[j] : pj;
+        const float pv = kQuant ? pj * vs[j] : pj;
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pv, vv[j][e], acc[g][e]);
       }

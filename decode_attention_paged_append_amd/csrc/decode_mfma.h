@@ -83,10 +83,11 @@ template <> struct Mfma<Fmt::BF16> {
   }
 };
 
-// Four int8 codes -> four exact fp16 values (two words, element order kept).
+// Four 8-bit codes -> four exact fp16 values (two words, element order kept).
+template <Fmt F>
 __device__ __forceinline__ u32x2 codes4_to_f16(uint32_t w) {
   h16x2 lo, hi;
-  Frag<Fmt::I8>::codes_to_half2(w, lo, hi);
+  Frag<F>::codes_to_half2(w, lo, hi);
   return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
@@ -94,8 +95,8 @@ __device__ __forceinline__ u32x2 codes4_to_f16(uint32_t w) {
 template <Fmt F, int D, int BS, int GC, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void decode_mfma_kernel(const DecodeParams p) {
-  constexpr bool kInt8 = F == Fmt::I8;
-  constexpr Fmt OF = kInt8 ? Fmt::F16 : F;      // MFMA operand format
+  constexpr bool kQuant = FmtInfo<F>::quantized;
+  constexpr Fmt OF = kQuant ? Fmt::F16 : F;     // MFMA operand format
   using MM = Mfma<OF>;
   constexpr int EB = FmtInfo<F>::bytes;         // cache element bytes
   constexpr int TT = 16;                        // positions per tile
@@ -140,7 +141,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
   // Fused append: the decoded token (position ctx-1) is this partition's last
   // row when tok_end == ctx.
-  if (!kInt8 && p.k_new != nullptr && tok_end == ctx)
+  if (!kQuant && p.k_new != nullptr && tok_end == ctx)
     append_new_rows<ROWB, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
 
   // B operand of the score product: Q^T, lane (g, n) holds head n's dims
@@ -231,14 +232,17 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
     float* const ksc = raw.ks;
     float* const vsc = raw.vs;
-    if constexpr (kInt8) {
+    if constexpr (kQuant) {
       // scales of tokens 4g..4g+3: 8 contiguous bytes
       const size_t srow = row0 + 4 * g;
       const bool any = !PARTIAL || 4 * g < nvalid;
       const u32x2 kw = any ? *(const u32x2*)(p.k_scale + srow) : u32x2{0, 0};
       const u32x2 vw = any ? *(const u32x2*)(p.v_scale + srow) : u32x2{0, 0};
-      ksc[0] = f16_lo(kw[0]); ksc[1] = f16_hi(kw[0]); ksc[2] = f16_lo(kw[1]); ksc[3] = f16_hi(kw[1]);
-      vsc[0] = f16_lo(vw[0]); vsc[1] = f16_hi(vw[0]); vsc[2] = f16_lo(vw[1]); vsc[3] = f16_hi(vw[1]);
+      constexpr float cs = FmtInfo<F>::code_scale;
+      ksc[0] = f16_lo(kw[0]) * cs; ksc[1] = f16_hi(kw[0]) * cs;
+      ksc[2] = f16_lo(kw[1]) * cs; ksc[3] = f16_hi(kw[1]) * cs;
+      vsc[0] = f16_lo(vw[0]) * cs; vsc[1] = f16_hi(vw[0]) * cs;
+      vsc[2] = f16_lo(vw[1]) * cs; vsc[3] = f16_hi(vw[1]) * cs;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (PARTIAL && 4 * g + i >= nvalid) ksc[i] = vsc[i] = 0.0f;  // never read past the context
@@ -259,10 +263,10 @@ void decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
     for (int j = 0; j < K_LOADS; ++j) {
       const int r = j * K_RPL + lane / K_LPR;
-      if constexpr (kInt8) {
+      if constexpr (kQuant) {
         const int c0 = 2 * (lane % K_LPR);
-        const u32x2 a = codes4_to_f16(kraw[j][0]), b = codes4_to_f16(kraw[j][1]);
-        const u32x2 c = codes4_to_f16(kraw[j][2]), d = codes4_to_f16(kraw[j][3]);
+        const u32x2 a = codes4_to_f16<F>(kraw[j][0]), b = codes4_to_f16<F>(kraw[j][1]);
+        const u32x2 c = codes4_to_f16<F>(kraw[j][2]), d = codes4_to_f16<F>(kraw[j][3]);
         ktile[r * CHUNKS + (c0 ^ (r % CHUNKS))] = u32x4{a[0], a[1], b[0], b[1]};
         ktile[r * CHUNKS + ((c0 + 1) ^ (r % CHUNKS))] = u32x4{c[0], c[1], d[0], d[1]};
       } else {
@@ -284,7 +288,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     float z[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = kInt8 ? sacc[i] * (ksc[i] * p.scale_log2) : sacc[i] * p.scale_log2;
+      z[i] = kQuant ? sacc[i] * (ksc[i] * p.scale_log2) : sacc[i] * p.scale_log2;
       if (PARTIAL && 4 * g + i >= nvalid) z[i] = -__builtin_inff();
     }
     float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -306,7 +310,7 @@ void decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < VE; ++e) o[e] *= alpha;
     }
-    if constexpr (kInt8) {
+    if constexpr (kQuant) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) pw[i] *= vsc[i];
     }
@@ -316,10 +320,10 @@ void decode_mfma_kernel(const DecodeParams p) {
     uint32_t vh[4][VE / 2];  // fp16/bf16 words of tokens 4g+j, dims of lane n
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if constexpr (kInt8) {
+      if constexpr (kQuant) {
 #pragma unroll
         for (int w = 0; w < VW / 4; ++w) {
-          const u32x2 h = codes4_to_f16(vraw[j][w]);
+          const u32x2 h = codes4_to_f16<F>(vraw[j][w]);
           vh[j][2 * w] = h[0];
           vh[j][2 * w + 1] = h[1];
         }

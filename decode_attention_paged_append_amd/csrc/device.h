@@ -18,14 +18,35 @@ constexpr int kWave = 64;
 constexpr float kMaxInit = -1.0e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum class Fmt : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3 };
+enum class Fmt : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3, FP8 = 4 };
 
+// bytes: cache element; q_bytes: query/output element.  Quantized caches
+// (int8, fp8 E4M3) hold codes with an fp16 scale per (token, head) and take
+// fp16 queries; their codes are widened to fp16 exactly, as the stored value
+// times 1/code_scale (the kernels multiply the scales by code_scale).
 template <Fmt F> struct FmtInfo;
-template <> struct FmtInfo<Fmt::F32> { static constexpr int bytes = 4; static constexpr int q_bytes = 4; };
-template <> struct FmtInfo<Fmt::F16> { static constexpr int bytes = 2; static constexpr int q_bytes = 2; };
-template <> struct FmtInfo<Fmt::BF16> { static constexpr int bytes = 2; static constexpr int q_bytes = 2; };
-// int8 cache: fp16 queries and outputs.
-template <> struct FmtInfo<Fmt::I8> { static constexpr int bytes = 1; static constexpr int q_bytes = 2; };
+template <> struct FmtInfo<Fmt::F32> {
+  static constexpr int bytes = 4, q_bytes = 4;
+  static constexpr bool quantized = false;
+};
+template <> struct FmtInfo<Fmt::F16> {
+  static constexpr int bytes = 2, q_bytes = 2;
+  static constexpr bool quantized = false;
+};
+template <> struct FmtInfo<Fmt::BF16> {
+  static constexpr int bytes = 2, q_bytes = 2;
+  static constexpr bool quantized = false;
+};
+template <> struct FmtInfo<Fmt::I8> {
+  static constexpr int bytes = 1, q_bytes = 2;
+  static constexpr bool quantized = true;
+  static constexpr float code_scale = 1.0f;
+};
+template <> struct FmtInfo<Fmt::FP8> {
+  static constexpr int bytes = 1, q_bytes = 2;
+  static constexpr bool quantized = true;
+  static constexpr float code_scale = 256.0f;
+};
 
 __device__ __forceinline__ float bits_to_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t float_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -101,5 +122,22 @@ __device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
+
+}  // namespace pa
+
+namespace pa {
+
+// Two OCP E4M3 codes (bytes `b` and `b+1` of w, picked by the v_perm
+// selector) -> two binary16 values equal to the codes' values times 2^-8,
+// exactly: the sign moves to bit 15 and the 7 exponent/fraction bits to bits
+// 13..7, so an E4M3 exponent field e (bias 7) becomes a binary16 exponent
+// field e (bias 15) and subnormals stay subnormal.  The NaN code is never
+// stored by the quantizer.
+__device__ __forceinline__ uint32_t e4m3_pair_to_f16(uint32_t w, uint32_t sel) {
+  const uint32_t x = __builtin_amdgcn_perm(0u, w, sel);  // codes in bits 15..8 and 31..24
+  return ((x >> 1) & 0x3F803F80u) | (x & 0x80008000u);
+}
+constexpr uint32_t kE4m3Lo = 0x010C000Cu;  // bytes 0, 1
+constexpr uint32_t kE4m3Hi = 0x030C020Cu;  // bytes 2, 3
 
 }  // namespace pa

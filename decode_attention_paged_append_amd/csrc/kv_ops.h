@@ -16,11 +16,12 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
                             int64_t num_tokens, void* k_cache, void* v_cache,
                             int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,
                             int64_t pool_slots, hipStream_t stream);
-hipError_t launch_kv_append_int8(const void* k_new, const void* v_new, const int64_t* slots,
-                                 int64_t num_tokens, int8_t* k_cache, int8_t* v_cache,
-                                 void* k_scale, void* v_scale, int32_t num_kv_heads,
-                                 int32_t block_size, int32_t head_dim, int64_t pool_slots,
-                                 hipStream_t stream);
+// Quantizing append into an int8 (fp8 false) or fp8 E4M3 (fp8 true) cache.
+hipError_t launch_kv_append_quant(const void* k_new, const void* v_new, const int64_t* slots,
+                                  int64_t num_tokens, void* k_cache, void* v_cache,
+                                  void* k_scale, void* v_scale, int32_t num_kv_heads,
+                                  int32_t block_size, int32_t head_dim, int64_t pool_slots,
+                                  bool fp8, hipStream_t stream);
 hipError_t launch_gather_kv(const void* k_cache, const void* v_cache, const void* k_scale,
                             const void* v_scale, const int32_t* tables, int32_t max_blocks,
                             const int32_t* context_lens, int32_t num_seqs, void* k_out,

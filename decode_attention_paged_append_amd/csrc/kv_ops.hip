@@ -70,17 +70,39 @@ __global__ void kv_append_kernel(const u32x4* __restrict__ k_new, const u32x4* _
   v_cache[dst] = v_new[i];
 }
 
-// int8: LQ = D/8 lanes hold one (token, head) row of fp16 values, 8 each.
-//   a = max |x| over the row (exact);  s = fp16(a / 127)  (IEEE fp32 divide,
-//   round to nearest even);  code = clamp(rint(x / s), -127, 127), 0 if s == 0
-//   (and 0 for a NaN input).
-template <int D>
-__global__ __launch_bounds__(256) void kv_append_int8_kernel(
+// OCP E4M3 code of r: nearest value, ties to even, magnitudes above 448
+// saturate, NaN gives 0.  Exponent e = floor(log2 |r|) from the float's bits;
+// from 2^-6 up the code is (e + 7) * 8 + (q - 8) with q = rint(|r| * 2^(3-e))
+// in [8, 16] (q = 16 carries into the next exponent); below 2^-6 the step is
+// 2^-9 and the code is rint(|r| * 2^9), whose 8 is again the smallest normal.
+__device__ __forceinline__ uint32_t e4m3_code(float r) {
+  if (r != r) return 0u;
+  const float a = fminf(fabsf(r), 448.0f);
+  const int e = (int)((float_to_bits(a) >> 23) & 0xffu) - 127;
+  uint32_t code;
+  if (e < -6) {
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    const float q = rintf(a * bits_to_float((uint32_t)(127 + 3 - e) << 23));
+    code = (uint32_t)((e + 7) * 8) + (uint32_t)q - 8u;
+  }
+  return code | (r < 0.0f && code != 0u ? 0x80u : 0u);
+}
+
+// Quantizing append, int8 or fp8 (E4M3) codes with one fp16 scale per
+// (token, head) row.  LQ = D/8 lanes hold one row of fp16 values, 8 each.
+//   a = max |x| over the row (exact);  s = fp16(a / R)  (IEEE fp32 divide,
+//   round to nearest even), R = 127 (int8) or 448 (E4M3 maximum);
+//   int8: code = clamp(rint(x / s), -127, 127);  fp8: code = E4M3(x / s);
+//   codes are 0 when s == 0 (and for a NaN input).
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void kv_append_quant_kernel(
     const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
     const int64_t* __restrict__ slots, int64_t num_tokens, u32x2* __restrict__ k_cache,
     u32x2* __restrict__ v_cache, uint16_t* __restrict__ k_scale, uint16_t* __restrict__ v_scale,
     int32_t num_kv_heads, int32_t block_size, int64_t pool_slots) {
   constexpr int LQ = D / 8;  // lanes per row
+  constexpr float R = FP8 ? 448.0f : 127.0f;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / LQ;        // (token, head) row
   const int c = (int)(gid % LQ);       // 8-value piece of the row
@@ -107,17 +129,21 @@ __global__ __launch_bounds__(256) void kv_append_int8_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
     a = group_max<LQ>(a);
-    const _Float16 s16 = (_Float16)(a / 127.0f);
+    const _Float16 s16 = (_Float16)(a / R);
     const float s = (float)s16;
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float code = 0.0f;
+      uint32_t code = 0u;
       if (s != 0.0f) {
-        const float r = rintf(f[i] / s);
-        code = r != r ? 0.0f : fminf(fmaxf(r, -127.0f), 127.0f);
+        if constexpr (FP8) {
+          code = e4m3_code(f[i] / s);
+        } else {
+          const float r = rintf(f[i] / s);
+          code = (uint32_t)(int32_t)(r != r ? 0.0f : fminf(fmaxf(r, -127.0f), 127.0f)) & 0xffu;
+        }
       }
-      packed[i / 4] |= ((uint32_t)(int32_t)code & 0xffu) << (8 * (i % 4));
+      packed[i / 4] |= code << (8 * (i % 4));
     }
     if (store) {
       const int64_t block = slot / block_size;
@@ -204,22 +230,28 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
   return hipGetLastError();
 }
 
-hipError_t launch_kv_append_int8(const void* k_new, const void* v_new, const int64_t* slots,
-                                 int64_t num_tokens, int8_t* k_cache, int8_t* v_cache,
-                                 void* k_scale, void* v_scale, int32_t num_kv_heads,
-                                 int32_t block_size, int32_t head_dim, int64_t pool_slots,
-                                 hipStream_t stream) {
+hipError_t launch_kv_append_quant(const void* k_new, const void* v_new, const int64_t* slots,
+                                  int64_t num_tokens, void* k_cache, void* v_cache,
+                                  void* k_scale, void* v_scale, int32_t num_kv_heads,
+                                  int32_t block_size, int32_t head_dim, int64_t pool_slots,
+                                  bool fp8, hipStream_t stream) {
   const int64_t lanes = num_tokens * num_kv_heads * (head_dim / 8);
   const dim3 grid(blocks_for(lanes, 256));
-#define PA_APPEND_I8(D)                                                                        \
-  hipLaunchKernelGGL(kv_append_int8_kernel<D>, grid, dim3(256), 0, stream,                      \
+#define PA_APPEND_Q(D, FP8)                                                                    \
+  hipLaunchKernelGGL((kv_append_quant_kernel<D, FP8>), grid, dim3(256), 0, stream,              \
                      (const u32x4*)k_new, (const u32x4*)v_new, slots, num_tokens,               \
                      (u32x2*)k_cache, (u32x2*)v_cache, (uint16_t*)k_scale, (uint16_t*)v_scale, \
                      num_kv_heads, block_size, pool_slots)
-  if (head_dim == 64) PA_APPEND_I8(64);
-  else if (head_dim == 128) PA_APPEND_I8(128);
-  else return hipErrorInvalidValue;
-#undef PA_APPEND_I8
+  if (head_dim == 64) {
+    if (fp8) PA_APPEND_Q(64, true);
+    else PA_APPEND_Q(64, false);
+  } else if (head_dim == 128) {
+    if (fp8) PA_APPEND_Q(128, true);
+    else PA_APPEND_Q(128, false);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef PA_APPEND_Q
   return hipGetLastError();
 }
 

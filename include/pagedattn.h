@@ -22,7 +22,8 @@
  *   k_cache, v_cache : [num_blocks][num_kv_heads][block_size][head_dim]
  *                      one contiguous block_size x head_dim tile per
  *                      (block, KV head)
- *   k_scale, v_scale : [num_blocks][num_kv_heads][block_size] fp16, int8 only
+ *   k_scale, v_scale : [num_blocks][num_kv_heads][block_size] fp16, quantized
+ *                      (int8, fp8) caches only
  *   block_tables     : int32 [num_seqs][max_blocks_per_seq]; entry j of row s
  *                      is the pool block holding positions [j*BS, (j+1)*BS)
  *                      of sequence s.  Entries past ceil(ctx/BS) are never read.
@@ -36,8 +37,8 @@
  * memory").
  *
  * Supported: head_dim in {64, 128}; block_size in {4, 8, 16, 32}; element
- * formats fp32, fp16, bf16 (q, caches and out share one format), and int8
- * caches with fp16 q/out and per-(token, head) fp16 scales.
+ * formats fp32, fp16, bf16 (q, caches and out share one format), and int8 or
+ * fp8 (E4M3) caches with fp16 q/out and per-(token, head) fp16 scales.
  *
  * Errors: arguments are checked on the host before anything is enqueued.
  * A non-PA_OK status means nothing was enqueued (except PA_ERR_HIP, which
@@ -69,7 +70,8 @@ typedef enum {
   PA_F32 = 0,
   PA_F16 = 1,
   PA_BF16 = 2,
-  PA_I8 = 3
+  PA_I8 = 3,
+  PA_FP8 = 4  /* OCP fp8 E4M3 codes (1 sign, 4 exponent bits of bias 7, 3 fraction bits) */
 } pa_dtype;
 
 typedef enum {
@@ -140,6 +142,20 @@ pa_status pa_kv_append_int8(const void* k_new, const void* v_new,
                             void* v_scale, const pa_cache_desc* cache,
                             pa_stream_t stream);
 
+/* fp8 cache ([viz] "What the page leaves out" names 8- and 4-bit cache
+ * quantization; the format and the quantizer are this library's reading):
+ * the int8 scheme with OCP E4M3 codes,
+ *   a = max |x|,  s = fp16_rne(fp32(a / 448)),
+ *   code = the E4M3 value nearest fp32(x / s), ties to even, saturating at
+ *          +-448 (0 when s == 0 or x is NaN; the NaN code is never stored).
+ * Codes go to k_cache/v_cache (device byte pools, cache->dtype == PA_FP8),
+ * s to k_scale/v_scale (device fp16 [NB][Hkv][BS]).  k_new, v_new: device
+ * fp16 [num_tokens][Hkv][D]. */
+pa_status pa_kv_append_fp8(const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int64_t num_tokens,
+                           void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                           const pa_cache_desc* cache, pa_stream_t stream);
+
 /* ---------------------------------------------------------------- attention */
 
 /* Workspace the decode entry points need for this shape: fp32 partial
@@ -189,6 +205,17 @@ pa_status pa_paged_decode_attention_int8(const void* q, const int8_t* k_cache,
                                          const pa_cache_desc* cache, void* workspace,
                                          size_t workspace_bytes, pa_stream_t stream);
 
+/* The same over an fp8 (E4M3) cache: keys and values are decode(code) *
+ * scale, exact in binary32; q and out fp16. */
+pa_status pa_paged_decode_attention_fp8(const void* q, const void* k_cache,
+                                        const void* v_cache, const void* k_scale,
+                                        const void* v_scale, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, float scale, void* out,
+                                        const pa_cache_desc* cache, void* workspace,
+                                        size_t workspace_bytes, pa_stream_t stream);
+
 /* One decode step for a fp32 / fp16 / bf16 cache: store each
  * sequence's new K and V rows (k_new, v_new: device [S][Hkv][D] in the
  * cache's format) at position context_lens[s] - 1, i.e. at slot
@@ -217,7 +244,7 @@ pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, vo
  * workspace.  When the partition covers the whole table width
  * (partition_tokens >= max_blocks_per_seq * BS) the result is final and is
  * written to out directly; otherwise pa_lse_merge must follow.  k_scale and
- * v_scale are used only for an int8 cache (NULL otherwise). */
+ * v_scale are used only for a quantized (int8, fp8) cache (NULL otherwise). */
 pa_status pa_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
                                const void* k_scale, const void* v_scale,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -256,7 +283,7 @@ pa_status pa_lse_merge(const void* workspace, size_t workspace_bytes,
  * rows at or past the length are left untouched.  k_out, v_out: device
  * [num_seqs][max_blocks_per_seq * BS][Hkv][D] in the cache's format (int8
  * codes for an int8 cache).  k_scale/v_scale and k_scale_out/v_scale_out
- * ([S][maxB*BS][Hkv] fp16) are used for an int8 cache only (may be NULL). */
+ * ([S][maxB*BS][Hkv] fp16) are used for a quantized cache only (may be NULL). */
 pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_scale,
                        const void* v_scale, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -359,7 +386,7 @@ int32_t pa_bm_sequence_length(const pa_block_manager* bm, int32_t seq); /* -1 if
  * one holder writes into it).  block_pairs: device int32 [num_pairs][2] of
  * (source, destination) block ids; every KV head's rows of the source block
  * are copied to the destination block, in k_cache and v_cache, and for an
- * int8 cache also in k_scale and v_scale (NULL otherwise).  Pairs with an id
+ * int8 or fp8 cache also in k_scale and v_scale (NULL otherwise).  Pairs with an id
  * outside [0, num_blocks) are skipped.  A destination must not be the source
  * or the destination of another pair in the same call. */
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,

@@ -10,8 +10,9 @@ import oracle
 import workloads as W
 
 # max-abs tolerances of the attention output against the fp64 oracle
-TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 8e-3, "i8": 1e-2}
-ELEM = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
+# (int8 and fp8 caches: against the oracle over the same codes and scales)
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 8e-3, "i8": 1e-2, "fp8": 1e-2}
+ELEM = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "fp8": 1}
 
 
 def dev():
@@ -34,6 +35,8 @@ def decode_gpu(q, kc, vc, bt, ctx, scale, partition_tokens=None, k_scale=None, v
     if partition_tokens is None:
         if kc.dtype == torch.int8:
             pa.paged_decode_attention_int8(q, kc, vc, k_scale, v_scale, bt, ctx, scale, out)
+        elif kc.dtype == torch.float8_e4m3fn:
+            pa.paged_decode_attention_fp8(q, kc, vc, k_scale, v_scale, bt, ctx, scale, out)
         else:
             pa.paged_decode_attention(q, kc, vc, bt, ctx, scale, out)
     else:
@@ -62,22 +65,24 @@ def max_abs_err(out: torch.Tensor, ref: np.ndarray, pairs=None) -> float:
     return float(np.max(np.abs(got - ref))) if ref.size else 0.0
 
 
-def quantize_pool_gpu(src_k, src_v, layout_blocks):
-    """int8 pool filled by the GPU append of every pool row (identity slots)."""
+def quantize_pool_gpu(src_k, src_v, layout_blocks, fmt="i8"):
+    """int8 / fp8 pool filled by the GPU append of every pool row (identity slots)."""
     nb, hkv, bs, d = src_k.shape
     rows_k = src_k.permute(0, 2, 1, 3).reshape(nb * bs, hkv, d).contiguous()
     rows_v = src_v.permute(0, 2, 1, 3).reshape(nb * bs, hkv, d).contiguous()
     slots = torch.arange(nb * bs, dtype=torch.int64, device=src_k.device)
-    kq = torch.zeros((nb, hkv, bs, d), dtype=torch.int8, device=src_k.device)
+    codes = torch.int8 if fmt == "i8" else torch.float8_e4m3fn
+    kq = torch.zeros((nb, hkv, bs, d), dtype=codes, device=src_k.device)
     vq = torch.zeros_like(kq)
     ks = torch.zeros((nb, hkv, bs), dtype=torch.float16, device=src_k.device)
     vs = torch.zeros_like(ks)
-    pa.kv_append_int8(rows_k, rows_v, slots, kq, vq, ks, vs)
+    append = pa.kv_append_int8 if fmt == "i8" else pa.kv_append_fp8
+    append(rows_k, rows_v, slots, kq, vq, ks, vs)
     return kq, vq, ks, vs
 
 
-def quantize_blocks_oracle(src_k, src_v, blocks):
-    """Oracle int8 pool holding only the given blocks (others zero)."""
+def quantize_blocks_oracle(src_k, src_v, blocks, fmt="i8"):
+    """Oracle int8 / fp8 pool holding only the given blocks (others zero)."""
     nb, hkv, bs, d = src_k.shape
     blocks = np.asarray(sorted(set(int(b) for b in blocks)), dtype=np.int64)
     sk = host(src_k[torch.as_tensor(blocks, device=src_k.device)])   # [n, Hkv, BS, D]
@@ -85,9 +90,10 @@ def quantize_blocks_oracle(src_k, src_v, blocks):
     rows_k = np.ascontiguousarray(sk.transpose(0, 2, 1, 3).reshape(-1, hkv, d))
     rows_v = np.ascontiguousarray(sv.transpose(0, 2, 1, 3).reshape(-1, hkv, d))
     slots = (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
-    kq = np.zeros((nb, hkv, bs, d), np.int8)
+    kq = np.zeros((nb, hkv, bs, d), np.int8 if fmt == "i8" else np.uint8)
     vq = np.zeros_like(kq)
     ks = np.zeros((nb, hkv, bs), np.float16)
     vs = np.zeros_like(ks)
-    oracle.kv_append_int8(rows_k, rows_v, slots, kq, vq, ks, vs)
+    append = oracle.kv_append_int8 if fmt == "i8" else oracle.kv_append_fp8
+    append(rows_k, rows_v, slots, kq, vq, ks, vs)
     return kq, vq, ks, vs, blocks

@@ -63,6 +63,17 @@ def test_append_argument_checks(lib):
                                  None) == UNSUPPORTED
     assert lib.pa_kv_append_int8(FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, FAKE, ctypes.byref(i8),
                                  None) == INVALID
+    fp8 = desc(dtype=4)
+    assert lib.pa_kv_append(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(fp8), None) == UNSUPPORTED
+    assert lib.pa_kv_append_fp8(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d),
+                                None) == UNSUPPORTED
+    assert b"fp8 cache" in lib.pa_last_error()
+    assert lib.pa_kv_append_fp8(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, ctypes.byref(i8),
+                                None) == UNSUPPORTED
+    assert lib.pa_kv_append_int8(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, ctypes.byref(fp8),
+                                 None) == UNSUPPORTED
+    assert lib.pa_kv_append_fp8(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, ctypes.byref(fp8),
+                                None) == INVALID
 
 
 def test_decode_argument_checks(lib):
@@ -75,6 +86,19 @@ def test_decode_argument_checks(lib):
     assert call(4, FAKE, 1 << 30, maxb=0) == INVALID
     assert call(4, FAKE, 1 << 30, desc_=desc(dtype=3)) == UNSUPPORTED  # int8 needs its entry
     assert call(4, FAKE, 1 << 30, desc_=desc(dtype=7)) == UNSUPPORTED
+    assert call(4, FAKE, 1 << 30, desc_=desc(dtype=4)) == UNSUPPORTED  # fp8 needs its entry
+    assert b"pa_paged_decode_attention_fp8" in lib.pa_last_error()
+    fp8 = desc(dtype=4)
+    i8 = desc(dtype=3)
+    assert lib.pa_paged_decode_attention_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 4,
+                                             0.1, FAKE, ctypes.byref(i8), FAKE, 1 << 30,
+                                             None) == UNSUPPORTED
+    assert lib.pa_paged_decode_attention_int8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 4,
+                                              0.1, FAKE, ctypes.byref(fp8), FAKE, 1 << 30,
+                                              None) == UNSUPPORTED
+    assert lib.pa_paged_decode_attention_fp8(FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, 4, 4,
+                                             0.1, FAKE, ctypes.byref(fp8), FAKE, 1 << 30,
+                                             None) == INVALID
     need = lib.pa_decode_workspace_bytes(ctypes.byref(d), 4, 4, 16, 64)
     assert need > 0
     assert lib.pa_decode_partitions(FAKE, FAKE, FAKE, None, None, FAKE, 16, FAKE, 4, 4, 0.1, 64,
@@ -89,7 +113,8 @@ def test_decode_argument_checks(lib):
 
 
 @pytest.mark.parametrize("dtype,d,bs,tile", [(0, 64, 4, 4), (1, 128, 16, 16), (1, 64, 4, 8),
-                                              (3, 64, 4, 16), (3, 128, 32, 32), (0, 128, 8, 8)])
+                                              (3, 64, 4, 16), (3, 128, 32, 32), (0, 128, 8, 8),
+                                              (4, 64, 4, 16), (4, 128, 16, 16)])
 def test_workspace_and_plan(lib, dtype, d, bs, tile):
     dd = desc(nb=4096, hkv=8, bs=bs, d=d, dtype=dtype)
     s, hq, maxb = 16, 32, 4096 // bs

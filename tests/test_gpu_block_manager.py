@@ -18,7 +18,8 @@ from oracle import block_manager as bm
 
 pytestmark = pytest.mark.gpu
 
-TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
+         "fp8": torch.float8_e4m3fn}
 
 
 def random_pool(rng, nb, hkv, bs, d, fmt):
@@ -26,14 +27,14 @@ def random_pool(rng, nb, hkv, bs, d, fmt):
     return torch.from_numpy(raw).to(dev()).view(TORCH[fmt])
 
 
-@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "i8"])
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16", "i8", "fp8"])
 @pytest.mark.parametrize("d,bs,hkv", [(64, 4, 3), (128, 16, 8), (128, 32, 1)])
 def test_copy_blocks_bit_exact(fmt, d, bs, hkv):
     rng = np.random.default_rng(d + bs + hkv)
     nb = 64
     kc, vc = random_pool(rng, nb, hkv, bs, d, fmt), random_pool(rng, nb, hkv, bs, d, fmt)
     ks = vs = None
-    if fmt == "i8":
+    if fmt in ("i8", "fp8"):
         ks = torch.from_numpy(rng.integers(0, 1 << 16, (nb, hkv, bs), dtype=np.uint16)
                               .view(np.float16)).to(dev())
         vs = torch.from_numpy(rng.integers(0, 1 << 16, (nb, hkv, bs), dtype=np.uint16)

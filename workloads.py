@@ -23,14 +23,15 @@ import torch
 SEED_DATA, SEED_TABLES, SEED_LENGTHS = 0, 1, 2
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-               "i8": torch.int8}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
+               "i8": torch.int8, "fp8": torch.float8_e4m3fn}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "fp8": 1}
+QUANTIZED = ("i8", "fp8")   # codes + fp16 per-(token, head) scales
 
 
 @dataclasses.dataclass(frozen=True)
 class Shape:
     name: str
-    cache_dtype: str          # "f32" | "f16" | "bf16" | "i8"
+    cache_dtype: str          # "f32" | "f16" | "bf16" | "i8" | "fp8"
     num_seqs: int
     num_q_heads: int
     num_kv_heads: int
@@ -41,8 +42,8 @@ class Shape:
 
     @property
     def q_dtype(self) -> str:
-        """Queries and outputs: the cache format, or fp16 for an int8 cache."""
-        return "f16" if self.cache_dtype == "i8" else self.cache_dtype
+        """Queries and outputs: the cache format, or fp16 for a quantized cache."""
+        return "f16" if self.cache_dtype in QUANTIZED else self.cache_dtype
 
     @property
     def scale(self) -> float:
@@ -65,7 +66,11 @@ LLAMA2_70B = Shape("llama2-70b-bf16", "bf16", 64, 64, 8, 128, 16,
 LLAMA3_8B_I8 = Shape("llama3-8b-int8kv", "i8", 64, 32, 8, 128, 16,
                      description="Llama-3-8B layer, int8 KV + fp16 scales, 64 seqs x 8192")
 
-SHAPES = {s.name: s for s in (TINY, LLAMA3_8B, LLAMA2_7B, LLAMA2_70B, LLAMA3_8B_I8)}
+LLAMA3_8B_FP8 = Shape("llama3-8b-fp8kv", "fp8", 64, 32, 8, 128, 16,
+                      description="Llama-3-8B layer, fp8 (E4M3) KV + fp16 scales, 64 seqs x 8192")
+
+SHAPES = {s.name: s for s in (TINY, LLAMA3_8B, LLAMA2_7B, LLAMA2_70B, LLAMA3_8B_I8,
+                              LLAMA3_8B_FP8)}
 
 TINY_POOL_BLOCKS = 64
 PREFIX_GROUP = 8          # sequences per shared-prefix group (Llama-2-70B workload)
@@ -84,7 +89,7 @@ def context_lengths(shape: Shape) -> list[int]:
         return [3, 7, 16, 33]
     if shape.name in (LLAMA3_8B.name, LLAMA2_7B.name):
         return [4096] * shape.num_seqs
-    if shape.name == LLAMA3_8B_I8.name:
+    if shape.name in (LLAMA3_8B_I8.name, LLAMA3_8B_FP8.name):
         return [8192] * shape.num_seqs
     if shape.name == LLAMA2_70B.name:
         lens = torch.randint(128, 32769, (shape.num_seqs,), generator=generator(SEED_LENGTHS))
@@ -195,7 +200,7 @@ class Case:
     shape: Shape
     layout: Layout
     q: torch.Tensor                 # [S, Hq, D] (q_dtype)
-    k_cache: torch.Tensor           # [NB, Hkv, BS, D] (cache dtype; fp16 source for int8)
+    k_cache: torch.Tensor           # [NB, Hkv, BS, D] (cache dtype; fp16 source if quantized)
     v_cache: torch.Tensor
     k_new: torch.Tensor             # [S, Hkv, D]: the decoded token's rows
     v_new: torch.Tensor
@@ -203,15 +208,15 @@ class Case:
 
 def make_case(shape: Shape, layout: Layout | None = None, device="cpu", seed=SEED_DATA,
               poison=True, poison_new_slot=True) -> Case:
-    """Seeded Q/K/V for one layer.  For an int8 cache, k_cache/v_cache hold the
-    fp16 source rows that the append quantizes.
+    """Seeded Q/K/V for one layer.  For a quantized cache, k_cache/v_cache hold
+    the fp16 source rows that the append quantizes.
 
     poison: NaN in every slot outside all contexts (never to be read).
     poison_new_slot: also NaN at each sequence's last position, which the
     decode step's append must overwrite.
     """
     layout = layout or layout_for(shape)
-    src = shape.q_dtype if shape.cache_dtype == "i8" else shape.cache_dtype
+    src = shape.q_dtype if shape.cache_dtype in QUANTIZED else shape.cache_dtype
     nb, hkv, bs, d = layout.num_blocks, shape.num_kv_heads, shape.block_size, shape.head_dim
     s, hq = shape.num_seqs, shape.num_q_heads
     k = randn((nb, hkv, bs, d), src, seed * 1000 + 1, device)
@@ -234,18 +239,22 @@ def make_case(shape: Shape, layout: Layout | None = None, device="cpu", seed=SEE
 
 
 def to_numpy_bits(t: torch.Tensor):
-    """Host numpy view of a tensor; bfloat16 travels as uint16 bit patterns."""
+    """Host numpy view of a tensor; bfloat16 travels as uint16 bit patterns and
+    fp8 E4M3 as uint8 codes."""
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
 def kv_bytes_per_layer_step(shape: Shape, ctx_lens) -> int:
     """Logical K+V bytes one decode step of one layer reads (every sequence reads
-    its whole context, shared blocks included), plus int8 scale bytes."""
+    its whole context, shared blocks included), plus the scale bytes of a
+    quantized cache."""
     total = sum(int(c) for c in ctx_lens)
     b = total * shape.num_kv_heads * shape.head_dim * 2 * ELEM_BYTES[shape.cache_dtype]
-    if shape.cache_dtype == "i8":
+    if shape.cache_dtype in QUANTIZED:
         b += total * shape.num_kv_heads * 2 * 2
     return b
