@@ -86,6 +86,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_attention_dense.argtypes = [P, P, P, i64, i32, dbl, P, P]
     lib.oracle_paged_decode_attention.argtypes = [
         P, i32, P, P, P, P, i32, P, i32, P, i32, i32, i32, i32, i32, i32, dbl, P, i64, P, i32]
+    lib.oracle_paged_decode_attention_window.argtypes = [
+        P, i32, P, P, P, P, i32, P, i32, P, i32, i32, i32, i32, i32, i32, dbl, i32, P, i64, P,
+        i32]
     lib.oracle_paged_prefill_attention.argtypes = [
         P, i32, P, P, P, P, i32, P, i32, P, P, i32, i32, i32, i32, i32, i32, dbl, P, i64, P,
         i32]
@@ -99,6 +102,7 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     for name in ("oracle_slot_mapping", "oracle_decode_slot_mapping", "oracle_kv_append",
                  "oracle_kv_append_int8", "oracle_kv_append_fp8", "oracle_attention_dense",
                  "oracle_paged_decode_attention", "oracle_paged_prefill_attention",
+                 "oracle_paged_decode_attention_window",
                  "oracle_gather_kv"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -270,6 +274,33 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
         _ptr(q), q_code, _ptr(k_cache), _ptr(v_cache), _ptr(ks), _ptr(vs), cache_code,
         _ptr(bt), bt.shape[1], _ptr(ctx), s_, hq, hkv, nb, bs, d, float(scale), _ptr(pp),
         n_pairs, _ptr(out), int(num_threads)))
+    return out
+
+
+def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                  window, k_scale=None, v_scale=None, pairs=None, bf16=False,
+                                  num_threads=0, lib=None) -> np.ndarray:
+    """fp64 decode attention over each sequence's last `window` positions
+    (window <= 0: all).  Arguments and result as paged_decode_attention."""
+    q = np.ascontiguousarray(q)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    nb, hkv, bs, d = k_cache.shape
+    s_, hq, dq = q.shape
+    assert dq == d and bt.shape[0] == s_ and ctx.shape[0] == s_
+    ks = None if k_scale is None else np.ascontiguousarray(k_scale).view(np.uint16)
+    vs = None if v_scale is None else np.ascontiguousarray(v_scale).view(np.uint16)
+    if pairs is None:
+        out = np.empty((s_, hq, d), dtype=np.float64)
+        pp, n_pairs = None, s_ * hq
+    else:
+        pp = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+        n_pairs = pp.shape[0]
+        out = np.empty((n_pairs, d), dtype=np.float64)
+    _check((lib or load()).oracle_paged_decode_attention_window(
+        _ptr(q), _dtype_code(q, bf16), _ptr(k_cache), _ptr(v_cache), _ptr(ks), _ptr(vs),
+        _dtype_code(k_cache, bf16), _ptr(bt), bt.shape[1], _ptr(ctx), s_, hq, hkv, nb, bs, d,
+        float(scale), int(window), _ptr(pp), n_pairs, _ptr(out), int(num_threads)))
     return out
 
 

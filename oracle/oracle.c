@@ -524,6 +524,79 @@ int oracle_paged_decode_attention(
   return status;
 }
 
+/* Sliding-window decode attention ([viz] "What the page leaves out" names
+ * sliding-window attention): the new token attends only to the last `window`
+ * positions of its sequence, [max(0, ctx - window), ctx); window <= 0 means
+ * the whole context.  The rows of that range are un-paged and the dense
+ * definition above applied, exactly as for the whole context.  Blocks wholly
+ * before the window are never read, so their table entries may be anything. */
+int oracle_paged_decode_attention_window(
+    const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+    const uint16_t* k_scale, const uint16_t* v_scale, int32_t cache_dtype,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t num_blocks,
+    int32_t block_size, int32_t head_dim, double scale, int32_t window,
+    const int32_t* pairs, int64_t n_pairs, double* out, int32_t num_threads) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || block_size <= 0 || head_dim <= 0 ||
+      max_blocks <= 0 || !elem_bytes(cache_dtype) || !elem_bytes(q_dtype))
+    return OR_BAD_ARG;
+  if ((cache_dtype == OR_I8 || cache_dtype == OR_FP8) && (!k_scale || !v_scale))
+    return OR_BAD_ARG;
+  for (int32_t s = 0; s < num_seqs; ++s)
+    if (context_lens[s] < 0 || context_lens[s] > max_blocks * block_size)
+      return OR_BAD_CTX;
+  if (!pairs) n_pairs = (int64_t)num_seqs * num_q_heads;
+  for (int64_t p = 0; pairs && p < n_pairs; ++p)
+    if (pairs[2 * p] < 0 || pairs[2 * p] >= num_seqs || pairs[2 * p + 1] < 0 ||
+        pairs[2 * p + 1] >= num_q_heads)
+      return OR_BAD_ARG;
+  int32_t group = num_q_heads / num_kv_heads;
+  int status = OR_OK;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int64_t p = 0; p < n_pairs; ++p) {
+    int32_t s = pairs ? pairs[2 * p] : (int32_t)(p / num_q_heads);
+    int32_t h = pairs ? pairs[2 * p + 1] : (int32_t)(p % num_q_heads);
+    int32_t ctx = context_lens[s];
+    int32_t first = window > 0 && ctx > window ? ctx - window : 0;
+    int32_t n = ctx - first;
+    int32_t kvh = h / group;
+    size_t rows = (size_t)(ctx > 0 ? ctx : 1) * head_dim;
+    double* K = (double*)malloc(sizeof(double) * rows);
+    double* V = (double*)malloc(sizeof(double) * rows);
+    double* qv = (double*)malloc(sizeof(double) * head_dim);
+    int st = (K && V && qv) ? OR_OK : OR_NO_MEM;
+    /* un-page positions first..ctx-1 only: un-page the whole context through
+     * a table shifted to start at the window's first block, then drop the
+     * leading rows of that block */
+    int32_t b0 = first / block_size;
+    if (st == OR_OK)
+      st = unpage(k_cache, v_cache, k_scale, v_scale, cache_dtype,
+                  block_tables + (size_t)s * max_blocks + b0, ctx - b0 * block_size, kvh,
+                  num_blocks, num_kv_heads, block_size, head_dim, K, V);
+    if (st == OR_OK) {
+      size_t skip = (size_t)(first - b0 * block_size) * head_dim;
+      for (int32_t d = 0; d < head_dim; ++d)
+        qv[d] = load_elem(q, q_dtype, ((size_t)s * num_q_heads + h) * head_dim + d);
+      st = oracle_attention_dense(qv, K + skip, V + skip, n, head_dim, scale,
+                                  out + (size_t)p * head_dim, NULL);
+    }
+    if (st != OR_OK) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+      status = st;
+    }
+    free(K);
+    free(V);
+    free(qv);
+  }
+  return status;
+}
+
 /* Prefill (and chunked prefill) attention: several query tokens of one
  * sequence at once ([viz] "Without vs with the cache": the prefill pass takes
  * all prompt tokens in one go; [viz] "Prefill and decode feel different").

@@ -449,6 +449,69 @@ def pin_int8_attention_dequantizes_exactly(lib):
     assert a.tobytes() == b.tobytes()
 
 
+# ---------------------------------------------------------------- sliding window
+
+def _window_batch(rng, ctx, bs=4, hkv=2, d=16, nb=96):
+    K = [rng.standard_normal((c, hkv, d)).astype(np.float32) for c in ctx]
+    V = [rng.standard_normal((c, hkv, d)).astype(np.float32) for c in ctx]
+    kp, vp, bt, ctx_a = _scatter_pool(K, V, bs, nb, rng, np.float32)
+    return K, V, kp, vp, bt, ctx_a
+
+
+def pin_window_whole_context(lib):
+    """No window, or one at least as long as the context, is plain decode."""
+    rng = np.random.default_rng(31)
+    _, _, kp, vp, bt, ctx = _window_batch(rng, [1, 7, 23, 40])
+    q = rng.standard_normal((4, 4, 16)).astype(np.float32)
+    full = oracle.paged_decode_attention(q, kp, vp, bt, ctx, 0.3, lib=lib)
+    for w in (0, -5, 40, 41, 1000):
+        got = oracle.paged_decode_attention_window(q, kp, vp, bt, ctx, 0.3, w, lib=lib)
+        assert got.tobytes() == full.tobytes(), w
+
+
+def pin_window_is_attention_over_last_rows(lib):
+    """torch's float64 SDPA over the last `window` rows of each sequence; a
+    window of one row returns that row."""
+    rng = np.random.default_rng(32)
+    K, V, kp, vp, bt, ctx = _window_batch(rng, [5, 23, 40, 17])
+    q = rng.standard_normal((4, 4, 16)).astype(np.float32)
+    for w in (1, 3, 4, 9, 16, 22):
+        got = oracle.paged_decode_attention_window(q, kp, vp, bt, ctx, 0.3, w, lib=lib)
+        for s in range(4):
+            lo = max(0, int(ctx[s]) - w)
+            for h in range(4):
+                ref = _sdpa64(q[s, h], K[s][lo:, h // 2], V[s][lo:, h // 2], 0.3)
+                assert np.max(np.abs(got[s, h] - ref)) < 1e-12, (w, s, h)
+                if w == 1:
+                    assert np.array_equal(got[s, h], V[s][-1, h // 2].astype(np.float64))
+
+
+def pin_window_reads_nothing_before_it(lib):
+    """Blocks wholly before the window may be freed: NaN in their rows and -1
+    in their table entries change nothing; a block-aligned window equals the
+    whole-context attention of the table that starts at the window's block."""
+    rng = np.random.default_rng(33)
+    _, _, kp, vp, bt, ctx = _window_batch(rng, [40, 37, 16])
+    q = rng.standard_normal((3, 4, 16)).astype(np.float32)
+    w = 12
+    ref = oracle.paged_decode_attention_window(q, kp, vp, bt, ctx, 0.3, w, lib=lib)
+    kp2, vp2, bt2 = kp.copy(), vp.copy(), bt.copy()
+    for s in range(3):
+        first = max(0, int(ctx[s]) - w)
+        for j in range(first // 4):
+            kp2[bt[s, j]] = np.nan
+            vp2[bt[s, j]] = np.nan
+            bt2[s, j] = -1
+    got = oracle.paged_decode_attention_window(q, kp2, vp2, bt2, ctx, 0.3, w, lib=lib)
+    assert got.tobytes() == ref.tobytes()
+    # sequence 0: ctx 40, window 12 -> positions 28..39 = blocks 7..9, aligned
+    shifted = np.full((1, bt.shape[1]), -1, np.int32)
+    shifted[0, :3] = bt[0, 7:10]
+    whole = oracle.paged_decode_attention(q[:1], kp, vp, shifted, np.array([12], np.int32),
+                                          0.3, lib=lib)
+    assert whole.tobytes() == ref[:1].tobytes()
+
+
 # ---------------------------------------------------------------- fp8 (E4M3)
 
 def _e4m3_table():

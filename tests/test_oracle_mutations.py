@@ -51,6 +51,9 @@ MUTANTS = {
                                 "volatile float ratio = a / 240.0f;"),
     "fp8 scales ignored by attention": ("if (dtype == OR_I8 || dtype == OR_FP8) {\n      sk",
                                         "if (dtype == OR_I8) {\n      sk"),
+    "window one row too short": ("int32_t first = window > 0 && ctx > window ? ctx - window : 0;",
+                                 "int32_t first = window > 0 && ctx > window ? ctx - window + 1 : 0;"),
+    "window start not skipped inside its block": ("K + skip, V + skip, n,", "K, V, n,"),
     "dot product over half the head": (
         "for (int32_t d = 0; d < head_dim; ++d) dot += q[d] * K[i * head_dim + d];",
         "for (int32_t d = 0; d < head_dim / 2; ++d) dot += q[d] * K[i * head_dim + d];"),
