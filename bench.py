@@ -65,6 +65,7 @@ class Bench:
         # quantized caches (int8, fp8): codes + fp16 scales, appended by the
         # quantizing append; attention reads them through the partitions call
         self.quant = shape.cache_dtype in W.QUANTIZED
+        self.window = shape.window
         self.append = shape.name != W.LLAMA2_70B.name   # shared-prefix blocks are not appended
         self.cases = []
         for layer in range(layers):
@@ -76,6 +77,10 @@ class Bench:
         desc = pa.CacheDesc(lay.num_blocks, shape.num_kv_heads, shape.block_size, d,
                             pa.DTYPE_CODE[W.TORCH_DTYPE[shape.cache_dtype]])
         self.part = partition_tokens or pa.decode_partition_tokens(desc, s, hq, lay.max_blocks)
+        if self.window:
+            # the library plans a windowed call itself (partitions + merge)
+            self.wws = torch.empty(max(pa.decode_window_workspace_bytes(
+                desc, s, hq, lay.max_blocks, self.window), 256), dtype=torch.uint8, device=dev)
         # the library routes >= 4 query heads per KV head with 16/32 blocks to matrix cores
         self.mfma = (shape.cache_dtype != "f32" and shape.block_size in (16, 32)
                      and shape.group % 4 == 0)
@@ -106,7 +111,7 @@ class Bench:
     def step(self):
         """One decode step over every layer."""
         sh = self.shape
-        fused_append = self.append and not self.quant and not self.separate
+        fused_append = self.fused_append
         if self.append and not fused_append:
             pa.decode_slot_mapping(self.bt, self.ctx, sh.block_size, out=self.slots)
         for layer, c in enumerate(self.cases):
@@ -117,7 +122,7 @@ class Bench:
                 else:
                     pa.kv_append(c.k_new, c.v_new, self.slots, c.k_cache, c.v_cache)
             self.attend(layer)
-            if self.nparts > 1:
+            if self.nparts > 1 and not self.window:
                 pa.lse_merge(self.ws, self.ctx, sh.num_q_heads, sh.head_dim,
                              self.layout.max_blocks, sh.block_size, self.part, self.outs[layer])
 
@@ -126,7 +131,10 @@ class Bench:
         the append fused into it for 16/32-bit caches)."""
         c, sh = self.cases[layer], self.shape
         out = self.outs[layer]
-        if self.fused_append:
+        if self.window:
+            pa.paged_decode_attention_window(c.q, c.k_cache, c.v_cache, self.bt, self.ctx,
+                                             sh.scale, self.window, out, workspace=self.wws)
+        elif self.fused_append:
             pa.decode_step_partitions(c.q, c.k_new, c.v_new, c.k_cache, c.v_cache, self.bt,
                                       self.ctx, sh.scale, out, self.part, self.ws)
         else:
@@ -136,7 +144,7 @@ class Bench:
 
     @property
     def fused_append(self) -> bool:
-        return self.append and not self.quant and not self.separate
+        return self.append and not self.quant and not self.separate and not self.window
 
     def kv_bytes_per_layer(self) -> int:
         return W.kv_bytes_per_layer_step(self.shape, self.layout.context_lens.tolist())
@@ -147,7 +155,11 @@ class Bench:
         append the new rows read and written."""
         sh = self.shape
         qo = 2 * sh.num_seqs * sh.num_q_heads * sh.head_dim * W.ELEM_BYTES[sh.q_dtype]
-        tables = sum(W.blocks_needed(int(c), sh.block_size) for c in self.layout.context_lens) * 4
+        bs = sh.block_size
+        first = [max(0, int(c) - sh.window) // bs if sh.window else 0
+                 for c in self.layout.context_lens]
+        tables = sum(W.blocks_needed(int(c), bs) - f
+                     for c, f in zip(self.layout.context_lens, first)) * 4
         new_rows = 0
         if self.fused_append:
             new_rows = 2 * 2 * sh.num_seqs * sh.num_kv_heads * sh.head_dim * W.ELEM_BYTES[sh.cache_dtype]
@@ -169,7 +181,12 @@ def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
     threads = oracle.max_threads()
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.paged_decode_attention(q, kc, vc, bt, ctx, b.shape.scale, num_threads=threads, **args)
+        if b.window:
+            oracle.paged_decode_attention_window(q, kc, vc, bt, ctx, b.shape.scale, b.window,
+                                                 num_threads=threads, **args)
+        else:
+            oracle.paged_decode_attention(q, kc, vc, bt, ctx, b.shape.scale,
+                                          num_threads=threads, **args)
         reps += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
@@ -500,22 +517,26 @@ def main():
                 "permutation of the pool",
         "config": {
             "workload": f"{shape.name}: {shape.description}; step = per layer "
-                        + ("attention launch with the slot and append fused in, then merge"
+                        + ("append, then the windowed attention call (partitions, merge)"
+                           if b.window
+                           else "attention launch with the slot and append fused in, then merge"
                            if b.fused_append
                            else "slots, append, attention partitions, merge launches"
                            if b.append else "attention partitions, merge launches"),
             "num_seqs": shape.num_seqs, "context_lens_sum": int(b.layout.context_lens.sum()),
             "layers": layers, "num_q_heads": shape.num_q_heads,
             "num_kv_heads": shape.num_kv_heads, "head_dim": shape.head_dim,
-            "block_size": shape.block_size, "partition_tokens": b.part,
-            "partitions": b.nparts,
+            "block_size": shape.block_size,
+            **({"window": b.window} if b.window else
+               {"partition_tokens": b.part, "partitions": b.nparts}),
         },
         "seq_steps_per_s": round(shape.num_seqs * 1e3 / ms_step, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": kv_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_mfma_kernel" if b.mfma else "decode_partition_kernel",
+            "kernel": ("decode_mfma_kernel" if b.mfma else "decode_partition_kernel")
+                      + (" + lse_merge_kernel (one windowed call)" if b.window else ""),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

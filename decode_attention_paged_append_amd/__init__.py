@@ -22,7 +22,8 @@ __all__ = [
     "paged_decode_attention", "paged_decode_attention_int8", "decode_step", "decode_partitions",
     "kv_append_fp8", "paged_decode_attention_fp8",
     "decode_step_partitions", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
-    "BlockManager", "copy_blocks", "paged_prefill_attention",
+    "BlockManager", "copy_blocks", "paged_prefill_attention", "paged_decode_attention_window",
+    "decode_window_workspace_bytes",
 ]
 
 # PA_LIBRARY_PATH may name another build of the same library (e.g. a variant
@@ -95,6 +96,8 @@ def _declare(lib):
         "pa_gather_kv": [P, P, P, P, P, i32, P, i32, P, P, P, P, D, P],
         "pa_copy_blocks": [P, P, P, P, P, i32, D, P],
         "pa_paged_prefill_attention": [P, P, P, P, i32, P, P, i32, i32, i32, f32, P, D, P],
+        "pa_paged_decode_attention_window": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D,
+                                             P, sz, P],
         "pa_bm_create": [i32, i32, ctypes.POINTER(P)],
         "pa_bm_add_sequence": [P, ctypes.POINTER(i32)],
         "pa_bm_fork": [P, i32, i32, ctypes.POINTER(i32)],
@@ -108,6 +111,8 @@ def _declare(lib):
         fn.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [D, i32, i32, i32, i32]
     lib.pa_decode_workspace_bytes.restype = sz
+    lib.pa_decode_window_workspace_bytes.argtypes = [D, i32, i32, i32, i32]
+    lib.pa_decode_window_workspace_bytes.restype = sz
     lib.pa_decode_partition_tokens.argtypes = [D, i32, i32, i32]
     lib.pa_decode_partition_tokens.restype = i32
     lib.pa_bm_destroy.argtypes = [P]
@@ -408,6 +413,37 @@ def gather_kv(k_cache, v_cache, block_tables, context_lens, k_out, v_out, k_scal
                          _dev(k_out, "k_out", k_cache.dtype), _dev(v_out, "v_out", k_cache.dtype),
                          _dev(k_scale_out, "k_scale_out"), _dev(v_scale_out, "v_scale_out"),
                          ctypes.byref(desc), _stream(k_cache)), lib)
+
+
+# ---------------------------------------------------------------- sliding window
+
+def decode_window_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks, window) -> int:
+    desc = k_cache if isinstance(k_cache, CacheDesc) else CacheDesc.of(k_cache)
+    return library().pa_decode_window_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
+                                                      max_blocks, window)
+
+
+def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_lens, scale, window,
+                                  out, k_scale=None, v_scale=None, workspace=None):
+    """Decode attention over each sequence's last `window` positions (0: all);
+    any cache format, scales for int8 / fp8 (see pa_paged_decode_attention_window)."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    quant = k_cache.dtype in QUANTIZED
+    q_dtype = torch.float16 if quant else k_cache.dtype
+    need = decode_window_workspace_bytes(desc, s, hq, maxb, int(window))
+    ws = _workspace(workspace, need, q.device)
+    _ok(lib.pa_paged_decode_attention_window(
+        _dev(q, "q", q_dtype, 3), _dev(k_cache, "k_cache", ndim=4),
+        _dev(v_cache, "v_cache", k_cache.dtype, 4),
+        _dev(k_scale, "k_scale", torch.float16) if quant else None,
+        _dev(v_scale, "v_scale", torch.float16) if quant else None,
+        _dev(block_tables, "block_tables", torch.int32), maxb,
+        _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale), int(window),
+        _dev(out, "out", q_dtype), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _stream(q)), lib)
+    return out
 
 
 # ---------------------------------------------------------------- prefill

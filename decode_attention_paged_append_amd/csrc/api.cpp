@@ -85,6 +85,9 @@ constexpr int32_t kTargetWorkgroups = 2048;
 constexpr int32_t kTargetWorkgroupsMfma = 256;
 constexpr int32_t kTargetWorkgroupsMfmaInt8 = 2048;
 constexpr int32_t kMinPartitionTokens = 256;
+// A windowed plan: workgroups over the window only (measured on a 4096-token
+// window: 512 beat 256, 1024 and 2048 with the neutral-partition grid).
+constexpr int32_t kTargetWorkgroupsWindow = 512;
 
 struct Plan {
   bool mfma = false;      // matrix-core kernel (grouped-query heads)
@@ -113,8 +116,10 @@ void size_workspace(Plan& p, int32_t num_seqs, int32_t num_q_heads, int32_t head
   p.ws_bytes = p.o_offset + rows * head_dim * sizeof(float);
 }
 
+// window > 0: a sliding-window plan, whose partitions are sized from the
+// window rather than the table (the partitions before it are no-ops).
 pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t max_blocks, int32_t requested, Plan* out) {
+                    int32_t max_blocks, int32_t requested, Plan* out, int32_t window = 0) {
   pa_status st = check_cache(c);
   if (st != PA_OK) return st;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
@@ -125,6 +130,7 @@ pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_head
   if ((int64_t)max_blocks * c->block_size > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "block table width x block size exceeds 2^31 positions");
   if (requested < 0) return fail(PA_ERR_INVALID_ARG, "partition_tokens %d < 0", requested);
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
   Plan p;
   const int32_t group = num_q_heads / c->num_kv_heads;
   // Four or more query heads per KV head: the score and value products are
@@ -150,17 +156,24 @@ pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_head
     // Enough workgroups to fill the chip, each wave owning whole tiles.
     const int64_t unit = (int64_t)p.tile * pa::kDecodeWaves;
     const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads * p.chunks;
-    const int64_t target = !p.mfma ? kTargetWorkgroups
+    const int64_t target = window > 0 ? kTargetWorkgroupsWindow
+                           : !p.mfma ? kTargetWorkgroups
                            : quantized(c->dtype) ? kTargetWorkgroupsMfmaInt8
                                                  : kTargetWorkgroupsMfma;
     const int64_t want_parts = (target + units - 1) / units;
-    part = (max_tok + want_parts - 1) / want_parts;
+    const int64_t span = window > 0 ? std::min<int64_t>(max_tok, window) : max_tok;
+    part = (span + want_parts - 1) / want_parts;
     part = std::max<int64_t>(part, kMinPartitionTokens);
     part = (part + unit - 1) / unit * unit;
   }
   if (part >= max_tok) part = (max_tok + p.tile - 1) / p.tile * p.tile;
   p.part_tokens = (int32_t)std::min<int64_t>(part, INT32_MAX / 2);
   p.num_parts = (int32_t)((max_tok + p.part_tokens - 1) / p.part_tokens);
+  // A window touches at most ceil(window / part) + 1 partitions of a
+  // sequence: the grid and the workspace hold that many slots.
+  if (window > 0 && p.num_parts > 1)
+    p.num_parts = (int32_t)std::min<int64_t>(p.num_parts,
+                                             (window + p.part_tokens - 1) / p.part_tokens + 1);
   if (num_seqs > 65535 || (int64_t)c->num_kv_heads * p.chunks > 65535)
     return fail(PA_ERR_UNSUPPORTED, "grid too large (%d sequences, %d KV heads x %d chunks)",
                 num_seqs, c->num_kv_heads, p.chunks);
@@ -175,7 +188,7 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
                          int32_t num_q_heads, float scale, void* out, const pa_cache_desc* cache,
                          const Plan& plan, void* workspace, size_t workspace_bytes,
                          hipStream_t stream, const void* k_new = nullptr,
-                         const void* v_new = nullptr) {
+                         const void* v_new = nullptr, int32_t window = 0) {
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (quantized(cache->dtype) && (!k_scale || !v_scale))
@@ -205,6 +218,7 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
   p.scale_log2 = scale * pa::kLog2e;
   p.k_new = k_new;
   p.v_new = v_new;
+  p.window = window;
   hipError_t e;
   const int D = cache->head_dim, BS = cache->block_size;
   if (plan.mfma) {
@@ -230,11 +244,11 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
 
 pa_status run_merge(const Plan& plan, const void* workspace, const int32_t* context_lens,
                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_tokens,
-                    int32_t out_dtype, void* out, hipStream_t stream) {
+                    int32_t out_dtype, void* out, hipStream_t stream, int32_t window = 0) {
   const hipError_t e = pa::launch_lse_merge(
       (const float*)workspace, (const float*)((const char*)workspace + plan.o_offset),
       context_lens, num_seqs, num_q_heads, head_dim, max_tokens, plan.part_tokens,
-      plan.num_parts, out_dtype, out, stream);
+      plan.num_parts, window, out_dtype, out, stream);
   return hip_status(e, "lse merge launch");
 }
 
@@ -244,9 +258,9 @@ pa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
                         int32_t num_q_heads, float scale, void* out, const pa_cache_desc* cache,
                         void* workspace, size_t workspace_bytes, hipStream_t stream,
                         int32_t want_dtype, const void* k_new = nullptr,
-                        const void* v_new = nullptr) {
+                        const void* v_new = nullptr, int32_t window = 0) {
   Plan plan;
-  pa_status st = make_plan(cache, num_seqs, num_q_heads, max_blocks, 0, &plan);
+  pa_status st = make_plan(cache, num_seqs, num_q_heads, max_blocks, 0, &plan, window);
   if (st != PA_OK) return st;
   // want_dtype: the quantized format an entry point is for, or -1 for the
   // entry points of unquantized caches.
@@ -259,11 +273,11 @@ pa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
   if (num_seqs == 0) return PA_OK;
   st = run_partitions(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks,
                       context_lens, num_seqs, num_q_heads, scale, out, cache, plan, workspace,
-                      workspace_bytes, stream, k_new, v_new);
+                      workspace_bytes, stream, k_new, v_new, window);
   if (st != PA_OK || plan.num_parts == 1) return st;
   const int32_t out_dtype = quantized(cache->dtype) ? PA_F16 : cache->dtype;
   return run_merge(plan, workspace, context_lens, num_seqs, num_q_heads, cache->head_dim,
-                   max_blocks * cache->block_size, out_dtype, out, stream);
+                   max_blocks * cache->block_size, out_dtype, out, stream, window);
 }
 
 }  // namespace
@@ -415,6 +429,33 @@ pa_status pa_paged_decode_attention_int8(const void* q, const int8_t* k_cache,
   return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
                        workspace_bytes, (hipStream_t)stream, PA_I8);
+}
+
+size_t pa_decode_window_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                        int32_t window) {
+  Plan plan;
+  if (make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, &plan, window) != PA_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+pa_status pa_paged_decode_attention_window(const void* q, const void* k_cache,
+                                           const void* v_cache, const void* k_scale,
+                                           const void* v_scale, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, float scale, int32_t window,
+                                           void* out, const pa_cache_desc* cache,
+                                           void* workspace, size_t workspace_bytes,
+                                           pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
+  return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
+                       workspace_bytes, (hipStream_t)stream,
+                       quantized(cache->dtype) ? cache->dtype : -1, nullptr, nullptr, window);
 }
 
 pa_status pa_paged_decode_attention_fp8(const void* q, const void* k_cache,

@@ -63,7 +63,45 @@ struct DecodeParams {
   // it reads the pool (identical bytes when several head chunks do so).
   const void* k_new;
   const void* v_new;
+  // Sliding window (0: none): the token attends to the last `window`
+  // positions, [ctx - window, ctx).  The grid then covers only the
+  // partitions a window can touch: partition slot k of a sequence is its
+  // partition start / part_tokens + k, and partials are stored by slot
+  // (num_parts = slots); slots past the sequence's end are left unwritten.
+  int32_t window;
 };
+
+// Workgroup coordinates (partition, KV head x chunk, sequence).  Workgroups
+// are dealt to the 8 XCDs round-robin by linear id; the linear id is
+// renumbered so that each XCD runs one contiguous eighth of the
+// (partition-fastest) grid.  Otherwise partition p of every sequence lands
+// on XCD p mod 8: a windowed plan, whose active partitions are the last few
+// of each sequence, would load two XCDs only, and the multi-partition
+// headline plans run ~2-4 % faster this way as well (measured).
+struct WgCoord {
+  int part, y, s;
+};
+__device__ __forceinline__ WgCoord wg_coord() {
+  const uint32_t nx = gridDim.x, ny = gridDim.y;
+  const uint32_t n = nx * ny * gridDim.z;
+  const uint32_t lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  constexpr uint32_t kXcds = 8;
+  const uint32_t per = n / kXcds;                 // whole eighths; the tail stays put
+  const uint32_t logical = lin < per * kXcds ? (lin % kXcds) * per + lin / kXcds : lin;
+  return {(int)(logical % nx), (int)(logical / nx % ny), (int)(logical / (nx * ny))};
+}
+
+// First position a sequence attends to.
+__device__ __forceinline__ int window_start(const DecodeParams& p, int ctx) {
+  return p.window > 0 && ctx > p.window ? ctx - p.window : 0;
+}
+
+// Partition of a grid slot: the slot itself, or for a windowed plan the
+// slot-th partition from the one holding the window's first position.
+__device__ __forceinline__ int partition_of_slot(const DecodeParams& p, int slot, int ctx) {
+  if (p.window <= 0 || ctx < 0) return slot;
+  return window_start(p, ctx) / p.part_tokens + slot;
+}
 
 template <Fmt F>
 __device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
@@ -256,16 +294,17 @@ void decode_partition_kernel(const DecodeParams p) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y / p.head_chunks;
-  const int chunk = blockIdx.y - kvh * p.head_chunks;
-  const int s = blockIdx.z;
+  const WgCoord wc = wg_coord();
+  const int slot = wc.part;
+  const int kvh = wc.y / p.head_chunks;
+  const int chunk = wc.y - kvh * p.head_chunks;
+  const int s = wc.s;
   const int h0 = kvh * p.group + chunk * GC;
   const size_t out_row0 = (size_t)s * p.num_q_heads + h0;
 
   const int ctx = p.context_lens[s];
   const bool single = p.num_parts == 1;
-  const int tok0 = part * p.part_tokens;
+  const int tok0 = partition_of_slot(p, slot, ctx) * p.part_tokens;
   const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
   if (bad_ctx || tok0 >= ctx) {
     // Nothing to attend in this partition.  The merge skips it; a single
@@ -278,7 +317,15 @@ void decode_partition_kernel(const DecodeParams p) {
     return;
   }
   const int tok_end = min(ctx, tok0 + p.part_tokens);
+  const int start = window_start(p, ctx);
+  if (tok_end <= start) {  // wholly before the window (never the only partition)
+    for (int i = threadIdx.x; i < GC * D; i += NW * kWave)
+      store_result<F, D>(p, false, out_row0 + i / D, slot, i % D, kMaxInit, 0.0f, 0.0f);
+    return;
+  }
   const int ntiles = (tok_end - tok0 + TT - 1) / TT;
+  const int t_first = (max(tok0, start) - tok0) / TT;   // first tile holding the window
+  const bool low_cut = start > tok0 + t_first * TT;      // which then starts mid-tile
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
   // Fused append: the decoded token (position ctx-1) is this partition's last
   // row when tok_end == ctx.
@@ -321,6 +368,7 @@ void decode_partition_kernel(const DecodeParams p) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     const int ttok = tok0 + t * TT;
     const int nvalid = tok_end - ttok;  // rows of the tile inside the partition
+    const int nlow = start - ttok;      // rows below this are before the window
     const int lb = t * BPT;             // first block of the tile
     if (lb >= ids_base + kWave) {       // a wave's tiles come in increasing order
       ids_base = lb & ~(kWave - 1);
@@ -332,7 +380,9 @@ void decode_partition_kernel(const DecodeParams p) {
     for (int b = 0; b < BPT; ++b) {
       const int id = __builtin_amdgcn_readlane(ids, lb - ids_base + b);
       const bool ok = (unsigned)id < (unsigned)p.num_blocks;
-      bad_block |= !ok;
+      // a block wholly before the window is never read: its entry may be stale
+      const bool needed = !PARTIAL || (b + 1) * BS > nlow;
+      bad_block |= !ok && needed;
       phys[b] = ok ? id : 0;
     }
     u32x4 kf[NJ], vf[NJ];
@@ -345,7 +395,7 @@ void decode_partition_kernel(const DecodeParams p) {
       for (int b = 1; b < BPT; ++b) pid = (r / BS == b) ? phys[b] : pid;
       const size_t row = ((size_t)pid * p.num_kv_heads + kvh) * BS + (BPT == 1 ? r : r % BS);
       const size_t off = row * ROWB + (size_t)lcol * 16;
-      const bool valid = !PARTIAL || r < nvalid;
+      const bool valid = !PARTIAL || (r >= nlow && r < nvalid);
       if (valid) {
         kf[j] = load16_stream(kbase + off);
         vf[j] = load16_stream(vbase + off);
@@ -373,7 +423,8 @@ void decode_partition_kernel(const DecodeParams p) {
       for (int j = 0; j < NJ; ++j) {
         const float d = group_sum<LR>(FR::dot(qf[g], kf[j]));
         z[g][j] = kQuant ? d * (ks[j] * p.scale_log2) : d * p.scale_log2;
-        if (PARTIAL && j * RPI + lrow >= nvalid) z[g][j] = -__builtin_inff();
+        if (PARTIAL && (j * RPI + lrow >= nvalid || j * RPI + lrow < nlow))
+          z[g][j] = -__builtin_inff();
       }
     }
     float vv[NJ][VE];
@@ -403,8 +454,8 @@ void decode_partition_kernel(const DecodeParams p) {
   };
 
   const int nfull = (tok_end - tok0) / TT;  // tiles with every row valid
-  for (int t = wave; t < ntiles; t += NW) {
-    if (t < nfull) tile(t, std::false_type{});
+  for (int t = t_first + wave; t < ntiles; t += NW) {
+    if (t < nfull && !(low_cut && t == t_first)) tile(t, std::false_type{});
     else tile(t, std::true_type{});
   }
 
@@ -460,7 +511,7 @@ void decode_partition_kernel(const DecodeParams p) {
       o = fmaf(a, s_acc[w][g][d], o);
     }
     if (bad) M = L = o = __builtin_nanf("");
-    store_result<F, D>(p, single, out_row0 + g, part, d, M, L, o);
+    store_result<F, D>(p, single, out_row0 + g, slot, d, M, L, o);
   }
 }
 

@@ -117,16 +117,17 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4;
   const int n = lane & 15;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y / p.head_chunks;
-  const int chunk = blockIdx.y - kvh * p.head_chunks;
-  const int s = blockIdx.z;
+  const WgCoord wc = wg_coord();
+  const int slot = wc.part;
+  const int kvh = wc.y / p.head_chunks;
+  const int chunk = wc.y - kvh * p.head_chunks;
+  const int s = wc.s;
   const int h0 = kvh * p.group + chunk * GC;
   const size_t out_row0 = (size_t)s * p.num_q_heads + h0;
 
   const int ctx = p.context_lens[s];
   const bool single = p.num_parts == 1;
-  const int tok0 = part * p.part_tokens;
+  const int tok0 = partition_of_slot(p, slot, ctx) * p.part_tokens;
   const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
   if (bad_ctx || tok0 >= ctx) {
     if (single) {
@@ -137,7 +138,15 @@ void decode_mfma_kernel(const DecodeParams p) {
     return;
   }
   const int tok_end = min(ctx, tok0 + p.part_tokens);
+  const int start = window_start(p, ctx);
+  if (tok_end <= start) {  // wholly before the window (never the only partition)
+    for (int i = threadIdx.x; i < GC * D; i += NW * kWave)
+      store_result<F, D>(p, false, out_row0 + i / D, slot, i % D, kMaxInit, 0.0f, 0.0f);
+    return;
+  }
   const int ntiles = (tok_end - tok0 + TT - 1) / TT;
+  const int t_first = (max(tok0, start) - tok0) / TT;   // first tile holding the window
+  const bool low_cut = start > tok0 + t_first * TT;      // which then starts mid-tile
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
   // Fused append: the decoded token (position ctx-1) is this partition's last
   // row when tok_end == ctx.
@@ -182,6 +191,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     uint32_t v[4][VW / 4];
     float ks[4], vs[4];
     int nvalid;  // rows of the tile inside the partition
+    int nlow;    // rows below this one are before the window
   };
 
   auto fetch = [&](const int t, auto partial_tag) {
@@ -189,7 +199,9 @@ void decode_mfma_kernel(const DecodeParams p) {
     Raw raw;
     const int ttok = tok0 + t * TT;
     const int nvalid = tok_end - ttok;
+    const int nlow = start - ttok;
     raw.nvalid = nvalid;
+    raw.nlow = nlow;
     const int rel = ttok / BS - blk0;  // block of the tile, from the partition's first
     if (rel >= ids_base + kWave) {
       ids_base = rel & ~(kWave - 1);
@@ -210,14 +222,15 @@ void decode_mfma_kernel(const DecodeParams p) {
     for (int j = 0; j < K_LOADS; ++j) {
       const int r = j * K_RPL + lane / K_LPR;
       kraw[j] = u32x4{0, 0, 0, 0};
-      if (!PARTIAL || r < nvalid) kraw[j] = load16_stream(kt + j * 1024 + lane * 16);
+      if (!PARTIAL || (r >= nlow && r < nvalid))
+        kraw[j] = load16_stream(kt + j * 1024 + lane * 16);
     }
     uint32_t (*const vraw)[VW / 4] = raw.v;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * g + j;
       const char* src = vt + (size_t)r * ROWB + n * VW;
-      const bool valid = !PARTIAL || r < nvalid;
+      const bool valid = !PARTIAL || (r >= nlow && r < nvalid);
       if constexpr (VW == 16) {
         u32x4 v = valid ? load16_stream(src) : u32x4{0, 0, 0, 0};
 #pragma unroll
@@ -235,7 +248,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     if constexpr (kQuant) {
       // scales of tokens 4g..4g+3: 8 contiguous bytes
       const size_t srow = row0 + 4 * g;
-      const bool any = !PARTIAL || 4 * g < nvalid;
+      const bool any = !PARTIAL || (4 * g < nvalid && 4 * g + 3 >= nlow);
       const u32x2 kw = any ? *(const u32x2*)(p.k_scale + srow) : u32x2{0, 0};
       const u32x2 vw = any ? *(const u32x2*)(p.v_scale + srow) : u32x2{0, 0};
       constexpr float cs = FmtInfo<F>::code_scale;
@@ -245,7 +258,8 @@ void decode_mfma_kernel(const DecodeParams p) {
       vsc[2] = f16_lo(vw[1]) * cs; vsc[3] = f16_hi(vw[1]) * cs;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (PARTIAL && 4 * g + i >= nvalid) ksc[i] = vsc[i] = 0.0f;  // never read past the context
+        // rows outside [nlow, nvalid) never contribute (their weight is 0)
+        if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) ksc[i] = vsc[i] = 0.0f;
       }
     }
     return raw;
@@ -254,6 +268,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   auto consume = [&](const Raw& raw, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     const int nvalid = raw.nvalid;
+    const int nlow = raw.nlow;
     const u32x4* const kraw = raw.k;
     const uint32_t (*const vraw)[VW / 4] = raw.v;
     const float* const ksc = raw.ks;
@@ -289,7 +304,7 @@ void decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       z[i] = kQuant ? sacc[i] * (ksc[i] * p.scale_log2) : sacc[i] * p.scale_log2;
-      if (PARTIAL && 4 * g + i >= nvalid) z[i] = -__builtin_inff();
+      if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) z[i] = -__builtin_inff();
     }
     float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -345,7 +360,13 @@ void decode_mfma_kernel(const DecodeParams p) {
   // Every load of TPI tiles is issued before the first of them is used, so a
   // wave keeps TPI tiles in flight (int8 tiles are half the bytes).
   const int nfull = (tok_end - tok0) / TT;  // tiles with every row valid
-  int t = wave;
+  int t = t_first + wave;
+  if (low_cut && wave == 0) {  // the window starts inside this wave's first tile
+    const Raw a = fetch(t, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    consume(a, std::true_type{});
+    t += NW;
+  }
   if constexpr (TPI == 2) {
     for (; t + NW < nfull; t += 2 * NW) {
       const Raw a = fetch(t, std::false_type{});
@@ -398,7 +419,7 @@ void decode_mfma_kernel(const DecodeParams p) {
       acc = fmaf(a, ((const float*)(s_mem + w * REGION))[h * D + d], acc);
     }
     if (bad) M = L = acc = __builtin_nanf("");
-    store_result<F, D>(p, single, out_row0 + h, part, d, M, L, acc);
+    store_result<F, D>(p, single, out_row0 + h, slot, d, M, L, acc);
   }
 }
 

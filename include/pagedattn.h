@@ -290,6 +290,32 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
                        int32_t num_seqs, void* k_out, void* v_out, void* k_scale_out,
                        void* v_scale_out, const pa_cache_desc* cache, pa_stream_t stream);
 
+/* ---------------------------------------------------------------- sliding window */
+
+/* Sliding-window decode attention ([viz] "What the page leaves out" names
+ * sliding-window attention; the reading here: the newest token attends to
+ * the last `window` positions of its sequence, [max(0, ctx - window), ctx)).
+ * Otherwise as pa_paged_decode_attention, for every cache format: k_scale and
+ * v_scale are used for an int8 or fp8 cache (q/out fp16) and ignored
+ * otherwise.  window == 0 attends to the whole context; window < 0 is
+ * PA_ERR_INVALID_ARG.  Positions before the window are never read, and
+ * neither are the table entries of blocks wholly before it: a caller may
+ * free those blocks and leave any value in their entries.  The workspace is
+ * sized by pa_decode_window_workspace_bytes with the same window (the plan's
+ * partitions follow the window's length). */
+size_t pa_decode_window_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                        int32_t window);
+pa_status pa_paged_decode_attention_window(const void* q, const void* k_cache,
+                                           const void* v_cache, const void* k_scale,
+                                           const void* v_scale, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, float scale, int32_t window,
+                                           void* out, const pa_cache_desc* cache,
+                                           void* workspace, size_t workspace_bytes,
+                                           pa_stream_t stream);
+
 /* ---------------------------------------------------------------- prefill */
 
 /* Causal attention of several query tokens per sequence over the paged cache:

@@ -39,6 +39,7 @@ class Shape:
     block_size: int
     layers: int = 1
     description: str = ""
+    window: int = 0           # sliding window (0: the whole context)
 
     @property
     def q_dtype(self) -> str:
@@ -69,8 +70,13 @@ LLAMA3_8B_I8 = Shape("llama3-8b-int8kv", "i8", 64, 32, 8, 128, 16,
 LLAMA3_8B_FP8 = Shape("llama3-8b-fp8kv", "fp8", 64, 32, 8, 128, 16,
                       description="Llama-3-8B layer, fp8 (E4M3) KV + fp16 scales, 64 seqs x 8192")
 
+LLAMA3_8B_WINDOW = Shape("llama3-8b-f16-window4k", "f16", 16, 32, 8, 128, 16, layers=32,
+                         description="Llama-3-8B layer, fp16, 16 seqs x 16384, sliding window "
+                                     "of 4096 positions, 32 layers",
+                         window=4096)
+
 SHAPES = {s.name: s for s in (TINY, LLAMA3_8B, LLAMA2_7B, LLAMA2_70B, LLAMA3_8B_I8,
-                              LLAMA3_8B_FP8)}
+                              LLAMA3_8B_FP8, LLAMA3_8B_WINDOW)}
 
 TINY_POOL_BLOCKS = 64
 PREFIX_GROUP = 8          # sequences per shared-prefix group (Llama-2-70B workload)
@@ -91,6 +97,8 @@ def context_lengths(shape: Shape) -> list[int]:
         return [4096] * shape.num_seqs
     if shape.name in (LLAMA3_8B_I8.name, LLAMA3_8B_FP8.name):
         return [8192] * shape.num_seqs
+    if shape.name == LLAMA3_8B_WINDOW.name:
+        return [16384] * shape.num_seqs
     if shape.name == LLAMA2_70B.name:
         lens = torch.randint(128, 32769, (shape.num_seqs,), generator=generator(SEED_LENGTHS))
         return [int(x) for x in lens]
@@ -251,9 +259,9 @@ def to_numpy_bits(t: torch.Tensor):
 
 def kv_bytes_per_layer_step(shape: Shape, ctx_lens) -> int:
     """Logical K+V bytes one decode step of one layer reads (every sequence reads
-    its whole context, shared blocks included), plus the scale bytes of a
-    quantized cache."""
-    total = sum(int(c) for c in ctx_lens)
+    its whole context, shared blocks included, or its last `window` positions),
+    plus the scale bytes of a quantized cache."""
+    total = sum(min(int(c), shape.window) if shape.window > 0 else int(c) for c in ctx_lens)
     b = total * shape.num_kv_heads * shape.head_dim * 2 * ELEM_BYTES[shape.cache_dtype]
     if shape.cache_dtype in QUANTIZED:
         b += total * shape.num_kv_heads * 2 * 2
