@@ -26,7 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
 
-F32, F16, BF16, I8, FP8 = 0, 1, 2, 3, 4
+F32, F16, BF16, I8, FP8, I4 = 0, 1, 2, 3, 4, 5
 _ERRORS = {
     -1: "bad argument",
     -2: "slot outside the pool",
@@ -80,6 +80,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_quantize_row_fp8.argtypes = [P, i32, P, P]
     lib.oracle_quantize_row_fp8.restype = None
     lib.oracle_kv_append_fp8.argtypes = [P, P, P, i64, P, P, P, P, i32, i32, i32, i32]
+    lib.oracle_quantize_row_int4.argtypes = [P, i32, P, P]
+    lib.oracle_quantize_row_int4.restype = None
+    lib.oracle_kv_append_int4.argtypes = [P, P, P, i64, P, P, P, P, i32, i32, i32, i32]
     lib.oracle_quantize_row_int8.argtypes = [P, i32, P, P]
     lib.oracle_quantize_row_int8.restype = None
     lib.oracle_kv_append_int8.argtypes = [P, P, P, i64, P, P, P, P, i32, i32, i32, i32]
@@ -100,7 +103,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_kv_bytes_per_token.restype = i64
     lib.oracle_max_threads.restype = i32
     for name in ("oracle_slot_mapping", "oracle_decode_slot_mapping", "oracle_kv_append",
-                 "oracle_kv_append_int8", "oracle_kv_append_fp8", "oracle_attention_dense",
+                 "oracle_kv_append_int8", "oracle_kv_append_fp8", "oracle_kv_append_int4",
+                 "oracle_attention_dense",
                  "oracle_paged_decode_attention", "oracle_paged_prefill_attention",
                  "oracle_paged_decode_attention_window",
                  "oracle_gather_kv"):
@@ -124,7 +128,7 @@ def _ptr(a: np.ndarray | None):
     return a.ctypes.data
 
 
-def _dtype_code(a: np.ndarray, bf16: bool = False) -> int:
+def _dtype_code(a: np.ndarray, bf16: bool = False, int4: bool = False) -> int:
     """Format code of a numpy array; bf16 data travels as uint16 bit patterns."""
     if a.dtype == np.float32:
         return F32
@@ -134,8 +138,8 @@ def _dtype_code(a: np.ndarray, bf16: bool = False) -> int:
         return BF16 if bf16 else F16
     if a.dtype == np.int8:
         return I8
-    if a.dtype == np.uint8:          # fp8 E4M3 codes
-        return FP8
+    if a.dtype == np.uint8:          # fp8 E4M3 codes, or packed int4 pairs
+        return I4 if int4 else FP8
     raise TypeError(f"unsupported oracle dtype {a.dtype}")
 
 
@@ -231,6 +235,30 @@ def kv_append_fp8(k_new, v_new, slots, k_cache, v_cache, k_scale, v_scale, lib=N
         _ptr(k_scale.view(np.uint16)), _ptr(v_scale.view(np.uint16)), nb, hkv, bs, d))
 
 
+INT4_GROUP = 32
+
+
+def quantize_row_int4(x_f16: np.ndarray, lib=None):
+    """(packed uint8 [n/2], fp16 scales [n/32]) of one row."""
+    x = np.ascontiguousarray(x_f16, dtype=np.float16).view(np.uint16)
+    q = np.empty(x.shape[0] // 2, dtype=np.uint8)
+    s = np.empty(x.shape[0] // INT4_GROUP, dtype=np.uint16)
+    (lib or load()).oracle_quantize_row_int4(_ptr(x), x.shape[0], _ptr(q), _ptr(s))
+    return q, s.view(np.float16)
+
+
+def kv_append_int4(k_new, v_new, slots, k_cache, v_cache, k_scale, v_scale, lib=None) -> None:
+    """k_cache, v_cache: uint8 [NB, Hkv, BS, D/2]; scales fp16 [NB, Hkv, BS, D/32]."""
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    nb, hkv, bs, half = k_cache.shape
+    kn = np.ascontiguousarray(k_new, dtype=np.float16).view(np.uint16)
+    vn = np.ascontiguousarray(v_new, dtype=np.float16).view(np.uint16)
+    assert k_cache.dtype == np.uint8 and k_scale.shape == (nb, hkv, bs, 2 * half // INT4_GROUP)
+    _check((lib or load()).oracle_kv_append_int4(
+        _ptr(kn), _ptr(vn), _ptr(slots), slots.shape[0], _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale.view(np.uint16)), _ptr(v_scale.view(np.uint16)), nb, hkv, bs, 2 * half))
+
+
 def attention_dense(q, K, V, scale, lib=None):
     """softmax(q K^T scale) V for one query; returns (out, weights), fp64."""
     q = np.ascontiguousarray(q, dtype=np.float64)
@@ -245,7 +273,7 @@ def attention_dense(q, K, V, scale, lib=None):
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
-                           k_scale=None, v_scale=None, pairs=None, bf16=False,
+                           k_scale=None, v_scale=None, pairs=None, bf16=False, int4=False,
                            num_threads=0, lib=None) -> np.ndarray:
     """fp64 attention output for every (seq, head) pair, or for the listed pairs.
 
@@ -257,9 +285,11 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
     nb, hkv, bs, d = k_cache.shape
+    if int4:                     # packed pairs: D / 2 bytes per row
+        d *= 2
     s_, hq, dq = q.shape
     assert dq == d and bt.shape[0] == s_ and ctx.shape[0] == s_
-    cache_code = _dtype_code(k_cache, bf16)
+    cache_code = _dtype_code(k_cache, bf16, int4)
     q_code = _dtype_code(q, bf16)
     ks = None if k_scale is None else np.ascontiguousarray(k_scale).view(np.uint16)
     vs = None if v_scale is None else np.ascontiguousarray(v_scale).view(np.uint16)
@@ -279,6 +309,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
 
 def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_lens, scale,
                                   window, k_scale=None, v_scale=None, pairs=None, bf16=False,
+                                  int4=False,
                                   num_threads=0, lib=None) -> np.ndarray:
     """fp64 decode attention over each sequence's last `window` positions
     (window <= 0: all).  Arguments and result as paged_decode_attention."""
@@ -286,6 +317,8 @@ def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_len
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
     nb, hkv, bs, d = k_cache.shape
+    if int4:                     # packed pairs: D / 2 bytes per row
+        d *= 2
     s_, hq, dq = q.shape
     assert dq == d and bt.shape[0] == s_ and ctx.shape[0] == s_
     ks = None if k_scale is None else np.ascontiguousarray(k_scale).view(np.uint16)
@@ -299,7 +332,7 @@ def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_len
         out = np.empty((n_pairs, d), dtype=np.float64)
     _check((lib or load()).oracle_paged_decode_attention_window(
         _ptr(q), _dtype_code(q, bf16), _ptr(k_cache), _ptr(v_cache), _ptr(ks), _ptr(vs),
-        _dtype_code(k_cache, bf16), _ptr(bt), bt.shape[1], _ptr(ctx), s_, hq, hkv, nb, bs, d,
+        _dtype_code(k_cache, bf16, int4), _ptr(bt), bt.shape[1], _ptr(ctx), s_, hq, hkv, nb, bs, d,
         float(scale), int(window), _ptr(pp), n_pairs, _ptr(out), int(num_threads)))
     return out
 
@@ -336,17 +369,19 @@ def paged_prefill_attention(q, k_cache, v_cache, block_tables, query_start, cont
 
 def gather_kv(k_cache, v_cache, block_tables, context_lens, k_out, v_out,
               k_scale=None, v_scale=None, k_scale_out=None, v_scale_out=None,
-              bf16=False, lib=None) -> None:
+              bf16=False, int4=False, lib=None) -> None:
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
     nb, hkv, bs, d = k_cache.shape
+    if int4:                     # packed pairs: D / 2 bytes per row
+        d *= 2
 
     def u16(a):
         return None if a is None else a.view(np.uint16)
 
     _check((lib or load()).oracle_gather_kv(
         _ptr(k_cache), _ptr(v_cache), _ptr(u16(k_scale)), _ptr(u16(v_scale)), _ptr(bt),
-        bt.shape[1], _ptr(ctx), bt.shape[0], nb, hkv, bs, d, _dtype_code(k_cache, bf16),
+        bt.shape[1], _ptr(ctx), bt.shape[0], nb, hkv, bs, d, _dtype_code(k_cache, bf16, int4),
         _ptr(k_out), _ptr(v_out), _ptr(u16(k_scale_out)), _ptr(u16(v_scale_out))))
 
 

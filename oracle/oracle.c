@@ -28,6 +28,9 @@
  *   - fp8 (E4M3) cache: the same scheme with 8-bit floating-point codes
  *     ([viz] "What the page leaves out" names 8- and 4-bit caches).  PARITY
  *     UNPINNED for the exact codes, as for int8.
+ *   - int4 cache: signed 4-bit codes with a scale per group of 32 dims, two
+ *     codes per byte (the 4-bit half of [viz]'s "8-bit or 4-bit").  PARITY
+ *     UNPINNED for the exact codes.
  *   - int8 cache ([notes] "How serving systems tame the cost", "Quantized KV
  *     cache"): the pages name the format only; the symmetric per-(token, head)
  *     absmax quantizer below is this project's reading.  PARITY UNPINNED by
@@ -53,7 +56,10 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_FP8 = 4 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_FP8 = 4, OR_I4 = 5 };
+
+/* int4 caches: one fp16 scale per group of this many dims of a row. */
+enum { OR_I4_GROUP = 32 };
 
 enum {
   OR_OK = 0,
@@ -161,6 +167,7 @@ static size_t elem_bytes(int dtype) {
     case OR_BF16: return 2;
     case OR_I8: return 1;
     case OR_FP8: return 1;
+    case OR_I4: return 1; /* two codes per byte: rows are head_dim / 2 bytes */
     default: return 0;
   }
 }
@@ -187,6 +194,13 @@ static double load_elem(const void* base, int dtype, size_t idx) {
       return (double)((const int8_t*)base)[idx];
     case OR_FP8:
       return oracle_fp8_e4m3_to_double(((const uint8_t*)base)[idx]);
+    case OR_I4: {
+      /* element 2i in the low nibble of byte i, 2i+1 in the high nibble,
+       * stored as code + 8 */
+      uint8_t byte = ((const uint8_t*)base)[idx / 2];
+      int nib = idx % 2 ? byte >> 4 : byte & 15;
+      return (double)(nib - 8);
+    }
     default:
       return NAN;
   }
@@ -393,6 +407,79 @@ int oracle_kv_append_fp8(const uint16_t* k_new, const uint16_t* v_new,
   return OR_OK;
 }
 
+/* int4 quantizer for one row of fp16 values ("8-bit or 4-bit" cache
+ * quantization: [viz] "What the page leaves out"; groups and scales are this
+ * project's reading, PARITY UNPINNED like the int8 codes).  For each group of
+ * OR_I4_GROUP consecutive dims:
+ *   a = max |x| over the group         (exact)
+ *   s = binary16 nearest to fp32(a / 7)  (fp32 IEEE division, then RNE)
+ *   q = clamp(round_half_even(fp32(x / s)), -7, 7), 0 when s == 0 or x is NaN,
+ * stored as the nibble q + 8: dim 2i in the low half of byte i, dim 2i + 1
+ * in the high half.  scales receives n / OR_I4_GROUP binary16 values.      */
+void oracle_quantize_row_int4(const uint16_t* x_f16, int32_t n, uint8_t* packed,
+                              uint16_t* scales_f16) {
+  for (int32_t i = 0; i < n / 2; ++i) packed[i] = 0;
+  for (int32_t g = 0; g < n / OR_I4_GROUP; ++g) {
+    const uint16_t* x = x_f16 + g * OR_I4_GROUP;
+    float a = 0.0f;
+    for (int32_t d = 0; d < OR_I4_GROUP; ++d) {
+      float ax = fabsf((float)oracle_f16_to_double(x[d]));
+      if (ax > a) a = ax;
+    }
+    volatile float ratio = a / 7.0f; /* binary32 quotient */
+    uint16_t sbits = oracle_double_to_f16_bits((double)ratio);
+    float s = (float)oracle_f16_to_double(sbits);
+    scales_f16[g] = sbits;
+    for (int32_t d = 0; d < OR_I4_GROUP; ++d) {
+      float c = 0.0f;
+      if (s != 0.0f) {
+        volatile float r = (float)oracle_f16_to_double(x[d]) / s; /* binary32 */
+        c = rintf(r);
+        if (c != c) c = 0.0f;
+        if (c > 7.0f) c = 7.0f;
+        if (c < -7.0f) c = -7.0f;
+      }
+      int32_t e = g * OR_I4_GROUP + d;
+      uint8_t nib = (uint8_t)((int)c + 8);
+      packed[e / 2] |= (uint8_t)(e % 2 ? nib << 4 : nib);
+    }
+  }
+}
+
+/* Append into an int4 cache: quantize each (token, head) row, then store the
+ * packed codes and its group scales at the token's slot. */
+int oracle_kv_append_int4(const uint16_t* k_new, const uint16_t* v_new,
+                          const int64_t* slots, int64_t num_tokens,
+                          uint8_t* k_cache, uint8_t* v_cache, uint16_t* k_scale,
+                          uint16_t* v_scale, int32_t num_blocks,
+                          int32_t num_kv_heads, int32_t block_size,
+                          int32_t head_dim) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 ||
+      block_size <= 0 || head_dim <= 0 || head_dim % OR_I4_GROUP)
+    return OR_BAD_ARG;
+  int64_t pool_slots = (int64_t)num_blocks * block_size;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    if (slots[t] >= pool_slots) return OR_BAD_SLOT;
+    if (slots[t] < 0) continue;
+    for (int64_t u = 0; u < t; ++u)
+      if (slots[u] == slots[t]) return OR_DUP_SLOT;
+  }
+  int32_t groups = head_dim / OR_I4_GROUP;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    if (slots[t] < 0) continue;
+    int64_t block = slots[t] / block_size, off = slots[t] % block_size;
+    for (int32_t h = 0; h < num_kv_heads; ++h) {
+      size_t src = ((size_t)t * num_kv_heads + h) * head_dim;
+      size_t srow = ((size_t)block * num_kv_heads + h) * block_size + off;
+      oracle_quantize_row_int4(k_new + src, head_dim, k_cache + srow * (head_dim / 2),
+                               &k_scale[srow * groups]);
+      oracle_quantize_row_int4(v_new + src, head_dim, v_cache + srow * (head_dim / 2),
+                               &v_scale[srow * groups]);
+    }
+  }
+  return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Attention of one query over n cached rows, straight from the definition
  * softmax(q . K^T * scale) . V ([notes] "Concept"), in fp64:
@@ -449,6 +536,11 @@ static int unpage(const void* k_cache, const void* v_cache,
       sv = oracle_f16_to_double(v_scale[row]);
     }
     for (int32_t d = 0; d < head_dim; ++d) {
+      if (dtype == OR_I4) { /* a scale per group of OR_I4_GROUP dims */
+        size_t g = row * (head_dim / OR_I4_GROUP) + d / OR_I4_GROUP;
+        sk = oracle_f16_to_double(k_scale[g]);
+        sv = oracle_f16_to_double(v_scale[g]);
+      }
       K[(size_t)i * head_dim + d] = load_elem(k_cache, dtype, row * head_dim + d) * sk;
       V[(size_t)i * head_dim + d] = load_elem(v_cache, dtype, row * head_dim + d) * sv;
     }
@@ -475,7 +567,8 @@ int oracle_paged_decode_attention(
       num_q_heads % num_kv_heads != 0 || block_size <= 0 || head_dim <= 0 ||
       max_blocks <= 0 || !elem_bytes(cache_dtype) || !elem_bytes(q_dtype))
     return OR_BAD_ARG;
-  if ((cache_dtype == OR_I8 || cache_dtype == OR_FP8) && (!k_scale || !v_scale))
+  if ((cache_dtype == OR_I8 || cache_dtype == OR_FP8 || cache_dtype == OR_I4) &&
+      (!k_scale || !v_scale))
     return OR_BAD_ARG;
   for (int32_t s = 0; s < num_seqs; ++s)
     if (context_lens[s] < 0 || context_lens[s] > max_blocks * block_size)
@@ -541,7 +634,8 @@ int oracle_paged_decode_attention_window(
       num_q_heads % num_kv_heads != 0 || block_size <= 0 || head_dim <= 0 ||
       max_blocks <= 0 || !elem_bytes(cache_dtype) || !elem_bytes(q_dtype))
     return OR_BAD_ARG;
-  if ((cache_dtype == OR_I8 || cache_dtype == OR_FP8) && (!k_scale || !v_scale))
+  if ((cache_dtype == OR_I8 || cache_dtype == OR_FP8 || cache_dtype == OR_I4) &&
+      (!k_scale || !v_scale))
     return OR_BAD_ARG;
   for (int32_t s = 0; s < num_seqs; ++s)
     if (context_lens[s] < 0 || context_lens[s] > max_blocks * block_size)
@@ -621,7 +715,8 @@ int oracle_paged_prefill_attention(
       max_blocks <= 0 || !elem_bytes(cache_dtype) || !elem_bytes(q_dtype) ||
       !query_start || query_start[0] != 0)
     return OR_BAD_ARG;
-  if ((cache_dtype == OR_I8 || cache_dtype == OR_FP8) && (!k_scale || !v_scale))
+  if ((cache_dtype == OR_I8 || cache_dtype == OR_FP8 || cache_dtype == OR_I4) &&
+      (!k_scale || !v_scale))
     return OR_BAD_ARG;
   for (int32_t s = 0; s < num_seqs; ++s) {
     int32_t t = query_start[s + 1] - query_start[s];
@@ -690,7 +785,8 @@ int oracle_gather_kv(const void* k_cache, const void* v_cache,
                      uint16_t* v_scale_out) {
   size_t eb = elem_bytes(dtype);
   if (!eb || num_seqs < 0 || max_blocks <= 0) return OR_BAD_ARG;
-  size_t row = (size_t)head_dim * eb;
+  size_t row = dtype == OR_I4 ? (size_t)head_dim / 2 : (size_t)head_dim * eb;
+  size_t spr = dtype == OR_I4 ? (size_t)head_dim / OR_I4_GROUP : 1; /* scales per row */
   int64_t cap = (int64_t)max_blocks * block_size;
   for (int32_t s = 0; s < num_seqs; ++s) {
     int32_t ctx = context_lens[s];
@@ -703,8 +799,10 @@ int oracle_gather_kv(const void* k_cache, const void* v_cache,
         size_t dst_row = ((size_t)s * cap + i) * num_kv_heads + h;
         memcpy((char*)k_out + dst_row * row, (const char*)k_cache + src_row * row, row);
         memcpy((char*)v_out + dst_row * row, (const char*)v_cache + src_row * row, row);
-        if (k_scale && k_scale_out) k_scale_out[dst_row] = k_scale[src_row];
-        if (v_scale && v_scale_out) v_scale_out[dst_row] = v_scale[src_row];
+        for (size_t g = 0; g < spr; ++g) {
+          if (k_scale && k_scale_out) k_scale_out[dst_row * spr + g] = k_scale[src_row * spr + g];
+          if (v_scale && v_scale_out) v_scale_out[dst_row * spr + g] = v_scale[src_row * spr + g];
+        }
       }
     }
   }

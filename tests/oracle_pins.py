@@ -602,6 +602,80 @@ def pin_fp8_attention_dequantizes_exactly(lib):
     assert a.tobytes() == b.tobytes()
 
 
+# ---------------------------------------------------------------- int4
+
+def _int4_unpack(packed):
+    """Codes of packed int4 rows: dim 2i low nibble of byte i, 2i+1 high,
+    stored as code + 8 (test-side numpy, from the documented layout)."""
+    lo = (packed & 15).astype(np.int16) - 8
+    hi = (packed >> 4).astype(np.int16) - 8
+    return np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+
+
+def pin_int4_quantizer(lib):
+    # worked by hand, group 0: max 7 -> s = fp16(7 / 7) = 1 exactly, so the
+    # codes are the values rounded half to even and clamped: 7, -3.5 -> -4,
+    # 2.5 -> 2, 0.4 -> 0, -0.6 -> -1, 6.5 -> 6, -7, 0; nibbles (+8) 15, 4, 10,
+    # 8, 7, 14, 1, 8 pack as bytes 0x4F, 0x8A, 0xE7, 0x81.  Group 1 is zero:
+    # scale 0, every nibble 8 (byte 0x88).  Group 2 holds a NaN: it codes as 0.
+    x = np.zeros(96, np.float16)
+    x[:8] = [7, -3.5, 2.5, 0.4, -0.6, 6.5, -7, 0]
+    x[64:72] = [1, 2, 3, float("nan"), -4, 0.5, 0, 0]
+    q, sc = oracle.quantize_row_int4(x, lib=lib)
+    assert q[:4].tolist() == [0x4F, 0x8A, 0xE7, 0x81] and (q[4:16] == 0x88).all()
+    assert float(sc[0]) == 1.0 and float(sc[1]) == 0.0
+    assert (q[16:32] == 0x88).all()            # group 1: dims 32..63 are zero
+    codes = _int4_unpack(q)
+    assert codes[67] == 0 and codes[68] == -7 and codes[64:67].tolist() == [2, 4, 5]
+    rng = np.random.default_rng(41)
+    for _ in range(200):
+        x = (rng.standard_normal(128) * rng.uniform(0.01, 100)).astype(np.float16)
+        q, sc = oracle.quantize_row_int4(x, lib=lib)
+        c = _int4_unpack(q).astype(np.float64)
+        s = np.repeat(sc.astype(np.float64), 32)
+        xf = x.astype(np.float64)
+        assert np.abs(c).max() == 7 and np.abs(c).min() >= 0
+        assert np.all(np.abs(xf - s * c) <= s / 2 * (1 + 1e-6) + np.abs(xf) * 2.0 ** -10)
+        qn, sn = oracle.quantize_row_int4(-x, lib=lib)
+        assert np.array_equal(sn, sc) and np.array_equal(_int4_unpack(qn), -_int4_unpack(q))
+
+
+def pin_int4_attention_dequantizes_exactly(lib):
+    """The int4 path equals the float path on code * group scale (exact in
+    binary32), and the gather copies packed rows and their group scales."""
+    rng = np.random.default_rng(42)
+    nb, hkv, bs, d, hq = 10, 2, 4, 64, 4
+    src_k = (rng.standard_normal((nb * bs, hkv, d)) *
+             np.repeat(rng.uniform(0.1, 10, (1, 1, d // 32)), 32, axis=2)).astype(np.float16)
+    src_v = rng.standard_normal((nb * bs, hkv, d)).astype(np.float16)
+    kq = np.zeros((nb, hkv, bs, d // 2), np.uint8)
+    vq = np.zeros_like(kq)
+    ks = np.zeros((nb, hkv, bs, d // 32), np.float16)
+    vs = np.zeros_like(ks)
+    oracle.kv_append_int4(src_k, src_v, np.arange(nb * bs, dtype=np.int64), kq, vq, ks, vs,
+                          lib=lib)
+    kf = (_int4_unpack(kq) * np.repeat(ks.astype(np.float32), 32, axis=3)).astype(np.float32)
+    vf = (_int4_unpack(vq) * np.repeat(vs.astype(np.float32), 32, axis=3)).astype(np.float32)
+    bt = rng.permutation(nb)[:8].reshape(2, 4).astype(np.int32)
+    ctx = np.array([13, 16], np.int32)
+    q = rng.standard_normal((2, hq, d)).astype(np.float16)
+    a = oracle.paged_decode_attention(q, kq, vq, bt, ctx, 0.2, k_scale=ks, v_scale=vs,
+                                      int4=True, lib=lib)
+    b = oracle.paged_decode_attention(q, kf, vf, bt, ctx, 0.2, lib=lib)
+    assert a.tobytes() == b.tobytes()
+    ko = np.zeros((2, 16, hkv, d // 2), np.uint8)
+    vo = np.zeros_like(ko)
+    kso = np.zeros((2, 16, hkv, d // 32), np.float16)
+    vso = np.zeros_like(kso)
+    oracle.gather_kv(kq, vq, bt, ctx, ko, vo, k_scale=ks, v_scale=vs, k_scale_out=kso,
+                     v_scale_out=vso, int4=True, lib=lib)
+    for s_ in range(2):
+        for i in range(int(ctx[s_])):
+            b_, o = divmod(i, bs)
+            assert np.array_equal(ko[s_, i], kq[bt[s_, b_], :, o])
+            assert np.array_equal(kso[s_, i], ks[bt[s_, b_], :, o])
+
+
 # ---------------------------------------------------------------- prefill
 
 def _sdpa64_rows(q, K, V, scale, mask):

@@ -54,6 +54,12 @@ MUTANTS = {
     "window one row too short": ("int32_t first = window > 0 && ctx > window ? ctx - window : 0;",
                                  "int32_t first = window > 0 && ctx > window ? ctx - window + 1 : 0;"),
     "window start not skipped inside its block": ("K + skip, V + skip, n,", "K, V, n,"),
+    "int4 nibbles swapped": ("packed[e / 2] |= (uint8_t)(e % 2 ? nib << 4 : nib);",
+                             "packed[e / 2] |= (uint8_t)(e % 2 ? nib : nib << 4);"),
+    "int4 offset 7": ("uint8_t nib = (uint8_t)((int)c + 8);", "uint8_t nib = (uint8_t)((int)c + 7);"),
+    "int4 range 8": ("volatile float ratio = a / 7.0f;", "volatile float ratio = a / 8.0f;"),
+    "int4 one scale per row": ("size_t g = row * (head_dim / OR_I4_GROUP) + d / OR_I4_GROUP;",
+                               "size_t g = row * (head_dim / OR_I4_GROUP);"),
     "dot product over half the head": (
         "for (int32_t d = 0; d < head_dim; ++d) dot += q[d] * K[i * head_dim + d];",
         "for (int32_t d = 0; d < head_dim / 2; ++d) dot += q[d] * K[i * head_dim + d];"),
