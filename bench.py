@@ -65,6 +65,7 @@ class Bench:
         # quantized caches (int8, fp8): codes + fp16 scales, appended by the
         # quantizing append; attention reads them through the partitions call
         self.quant = shape.cache_dtype in W.QUANTIZED
+        self.int4 = shape.cache_dtype == "i4"
         self.window = shape.window
         self.append = shape.name != W.LLAMA2_70B.name   # shared-prefix blocks are not appended
         self.cases = []
@@ -75,6 +76,7 @@ class Bench:
             self.cases.append(c)
         s, hq, d = shape.num_seqs, shape.num_q_heads, shape.head_dim
         desc = pa.CacheDesc(lay.num_blocks, shape.num_kv_heads, shape.block_size, d,
+                            pa.INT4 if self.int4 else
                             pa.DTYPE_CODE[W.TORCH_DTYPE[shape.cache_dtype]])
         self.part = partition_tokens or pa.decode_partition_tokens(desc, s, hq, lay.max_blocks)
         if self.window:
@@ -82,7 +84,7 @@ class Bench:
             self.wws = torch.empty(max(pa.decode_window_workspace_bytes(
                 desc, s, hq, lay.max_blocks, self.window), 256), dtype=torch.uint8, device=dev)
         # the library routes >= 4 query heads per KV head with 16/32 blocks to matrix cores
-        self.mfma = (shape.cache_dtype != "f32" and shape.block_size in (16, 32)
+        self.mfma = (shape.cache_dtype not in ("f32", "i4") and shape.block_size in (16, 32)
                      and shape.group % 4 == 0)
         self.nparts = -(-lay.max_blocks * shape.block_size // self.part)
         nbytes = pa.decode_workspace_bytes(desc, s, hq, lay.max_blocks, self.part)
@@ -91,16 +93,18 @@ class Bench:
         self.slots = torch.empty(s, dtype=torch.int64, device=dev)
 
     def quant_append(self, *args):
-        (pa.kv_append_int8 if self.shape.cache_dtype == "i8" else pa.kv_append_fp8)(*args)
+        {"i8": pa.kv_append_int8, "fp8": pa.kv_append_fp8,
+         "i4": pa.kv_append_int4}[self.shape.cache_dtype](*args)
 
     def _quantize(self, c):
         nb, hkv, bs, d = c.k_cache.shape
         rows = lambda x: x.permute(0, 2, 1, 3).reshape(nb * bs, hkv, d).contiguous()
         slots = torch.arange(nb * bs, dtype=torch.int64, device=self.dev)
-        kq = torch.empty((nb, hkv, bs, d), dtype=W.TORCH_DTYPE[self.shape.cache_dtype],
-                         device=self.dev)
+        kq = torch.empty((nb, hkv, bs, d // 2 if self.int4 else d),
+                         dtype=W.TORCH_DTYPE[self.shape.cache_dtype], device=self.dev)
         vq = torch.empty_like(kq)
-        ks = torch.empty((nb, hkv, bs), dtype=torch.float16, device=self.dev)
+        ks = torch.empty((nb, hkv, bs) + ((d // W.INT4_GROUP,) if self.int4 else ()),
+                         dtype=torch.float16, device=self.dev)
         vs = torch.empty_like(ks)
         self.quant_append(rows(c.k_cache), rows(c.v_cache), slots, kq, vq, ks, vs)
         torch.cuda.synchronize()
@@ -140,7 +144,7 @@ class Bench:
         else:
             pa.decode_partitions(c.q, c.k_cache, c.v_cache, self.bt, self.ctx, sh.scale, out,
                                  self.part, self.ws, getattr(c, "k_scale", None),
-                                 getattr(c, "v_scale", None))
+                                 getattr(c, "v_scale", None), int4=self.int4)
 
     @property
     def fused_append(self) -> bool:
@@ -175,7 +179,7 @@ def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
     host = W.to_numpy_bits
     args = dict(k_scale=host(c.k_scale) if b.quant else None,
                 v_scale=host(c.v_scale) if b.quant else None,
-                bf16=b.shape.cache_dtype == "bf16")
+                bf16=b.shape.cache_dtype == "bf16", int4=b.int4)
     q, kc, vc = host(c.q), host(c.k_cache), host(c.v_cache)
     bt, ctx = host(lay.block_tables), host(lay.context_lens)
     threads = oracle.max_threads()

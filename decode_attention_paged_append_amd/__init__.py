@@ -20,7 +20,8 @@ __all__ = [
     "PagedAttnError", "library", "CacheDesc", "slot_mapping", "decode_slot_mapping",
     "kv_append", "kv_append_int8", "decode_workspace_bytes", "decode_partition_tokens",
     "paged_decode_attention", "paged_decode_attention_int8", "decode_step", "decode_partitions",
-    "kv_append_fp8", "paged_decode_attention_fp8",
+    "kv_append_fp8", "paged_decode_attention_fp8", "kv_append_int4",
+    "paged_decode_attention_int4", "int4_desc",
     "decode_step_partitions", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
     "BlockManager", "copy_blocks", "paged_prefill_attention", "paged_decode_attention_window",
     "decode_window_workspace_bytes",
@@ -85,9 +86,11 @@ def _declare(lib):
         "pa_kv_append": [P, P, P, i64, P, P, D, P],
         "pa_kv_append_int8": [P, P, P, i64, P, P, P, P, D, P],
         "pa_kv_append_fp8": [P, P, P, i64, P, P, P, P, D, P],
+        "pa_kv_append_int4": [P, P, P, i64, P, P, P, P, D, P],
         "pa_paged_decode_attention": [P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
         "pa_paged_decode_attention_int8": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
         "pa_paged_decode_attention_fp8": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
+        "pa_paged_decode_attention_int4": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
         "pa_decode_partitions": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D, P, sz, P],
         "pa_lse_merge": [P, sz, P, i32, i32, i32, i32, i32, i32, i32, P, P],
         "pa_decode_step": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
@@ -221,6 +224,39 @@ def kv_append_int8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scal
                               _stream(k_cache)), lib)
 
 
+INT4 = 5        # pa_dtype of an int4 cache
+INT4_GROUP = 32
+
+
+def int4_desc(k_cache) -> CacheDesc:
+    """Descriptor of an int4 pool held as uint8 [NB, Hkv, BS, D/2] (two codes
+    per byte; torch has no 4-bit type)."""
+    if k_cache.dtype != torch.uint8 or k_cache.dim() != 4:
+        raise ValueError("an int4 pool is a uint8 tensor [NB, Hkv, BS, D/2]")
+    nb, hkv, bs, half = k_cache.shape
+    return CacheDesc(nb, hkv, bs, 2 * half, INT4)
+
+
+def kv_append_int4(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale):
+    """Quantize fp16 rows [T, Hkv, D] to int4 codes (uint8 pools [NB, Hkv, BS,
+    D/2]) with fp16 scales per 32 dims ([NB, Hkv, BS, D/32])."""
+    lib = library()
+    desc = int4_desc(k_cache)
+    t = slot_mapping.numel()
+    if k_new.shape != (t, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{t}, {desc.num_kv_heads}, {desc.head_dim}]")
+    want = (*k_cache.shape[:3], desc.head_dim // INT4_GROUP)
+    if tuple(k_scale.shape) != want or tuple(v_scale.shape) != want:
+        raise ValueError(f"scales must be {want}")
+    _ok(lib.pa_kv_append_int4(_dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),
+                              _dev(slot_mapping, "slot_mapping", torch.int64), t,
+                              _dev(k_cache, "k_cache", torch.uint8, 4),
+                              _dev(v_cache, "v_cache", torch.uint8, 4),
+                              _dev(k_scale, "k_scale", torch.float16),
+                              _dev(v_scale, "v_scale", torch.float16), ctypes.byref(desc),
+                              _stream(k_cache)), lib)
+
+
 def kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale):
     """Quantize fp16 rows [T, Hkv, D] to fp8 E4M3 codes + fp16 scales."""
     lib = library()
@@ -260,13 +296,13 @@ def _workspace(ws, nbytes, device):
     return ws
 
 
-def _shapes(q, k_cache, block_tables, context_lens, out):
+def _shapes(q, k_cache, block_tables, context_lens, out, int4=False):
     s, hq, d = q.shape
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
     if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.numel() != s:
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
-    if k_cache.shape[3] != d:
+    if k_cache.shape[3] * (2 if int4 else 1) != d:
         raise ValueError("head_dim of q and cache differ")
     return s, hq, block_tables.shape[1]
 
@@ -325,6 +361,30 @@ def paged_decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tabl
     return out
 
 
+def paged_decode_attention_int4(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                context_lens, scale, out, workspace=None):
+    """Decode attention over an int4 cache (uint8 pools [NB, Hkv, BS, D/2],
+    fp16 scales [NB, Hkv, BS, D/32])."""
+    lib = library()
+    desc = int4_desc(k_cache)
+    s, hq, d = q.shape
+    if out.shape != q.shape or d != desc.head_dim:
+        raise ValueError("q and out must be [S, Hq, D] with the cache's D")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.numel() != s:
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    maxb = block_tables.shape[1]
+    need = decode_workspace_bytes(desc, s, hq, maxb)
+    ws = _workspace(workspace, need, q.device)
+    _ok(lib.pa_paged_decode_attention_int4(
+        _dev(q, "q", torch.float16, 3), _dev(k_cache, "k_cache", torch.uint8, 4),
+        _dev(v_cache, "v_cache", torch.uint8, 4), _dev(k_scale, "k_scale", torch.float16),
+        _dev(v_scale, "v_scale", torch.float16), _dev(block_tables, "block_tables", torch.int32),
+        maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
+        _dev(out, "out", torch.float16), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _stream(q)), lib)
+    return out
+
+
 def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
                 workspace=None):
     """One decode step: store each sequence's k_new/v_new [S, Hkv, D] rows at
@@ -348,12 +408,13 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, s
 
 
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, out,
-                      partition_tokens, workspace, k_scale=None, v_scale=None):
-    """Phase 1 with an explicit partition length (see pa_decode_partitions)."""
+                      partition_tokens, workspace, k_scale=None, v_scale=None, int4=False):
+    """Phase 1 with an explicit partition length (see pa_decode_partitions);
+    int4: uint8 pools [NB, Hkv, BS, D/2] hold int4 codes."""
     lib = library()
-    desc = CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
-    q_dtype = torch.float16 if k_cache.dtype in QUANTIZED else k_cache.dtype
+    desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out, int4)
+    q_dtype = torch.float16 if int4 or k_cache.dtype in QUANTIZED else k_cache.dtype
     _ok(lib.pa_decode_partitions(
         _dev(q, "q", q_dtype, 3), _dev(k_cache, "k_cache", ndim=4),
         _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(k_scale, "k_scale", torch.float16),
@@ -398,12 +459,13 @@ def lse_merge(workspace, context_lens, num_q_heads, head_dim, max_blocks, block_
 # ---------------------------------------------------------------- gather
 
 def gather_kv(k_cache, v_cache, block_tables, context_lens, k_out, v_out, k_scale=None,
-              v_scale=None, k_scale_out=None, v_scale_out=None):
-    """Un-page to dense [S, max_blocks*BS, Hkv, D]; rows past a length untouched."""
+              v_scale=None, k_scale_out=None, v_scale_out=None, int4=False):
+    """Un-page to dense [S, max_blocks*BS, Hkv, D] (int4: packed [..., D/2]);
+    rows past a length untouched."""
     lib = library()
-    desc = CacheDesc.of(k_cache)
+    desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
     s, maxb = block_tables.shape
-    want = (s, maxb * desc.block_size, desc.num_kv_heads, desc.head_dim)
+    want = (s, maxb * desc.block_size, desc.num_kv_heads, k_cache.shape[3])
     if tuple(k_out.shape) != want or tuple(v_out.shape) != want:
         raise ValueError(f"k_out/v_out must be {want}")
     _ok(lib.pa_gather_kv(_dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", k_cache.dtype, 4),
@@ -424,13 +486,13 @@ def decode_window_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks, wi
 
 
 def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_lens, scale, window,
-                                  out, k_scale=None, v_scale=None, workspace=None):
+                                  out, k_scale=None, v_scale=None, workspace=None, int4=False):
     """Decode attention over each sequence's last `window` positions (0: all);
     any cache format, scales for int8 / fp8 (see pa_paged_decode_attention_window)."""
     lib = library()
-    desc = CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
-    quant = k_cache.dtype in QUANTIZED
+    desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out, int4)
+    quant = int4 or k_cache.dtype in QUANTIZED
     q_dtype = torch.float16 if quant else k_cache.dtype
     need = decode_window_workspace_bytes(desc, s, hq, maxb, int(window))
     ws = _workspace(workspace, need, q.device)
@@ -564,7 +626,7 @@ class BlockManager:
         return self._lib.pa_bm_sequence_length(self._h, seq)
 
 
-def copy_blocks(k_cache, v_cache, block_pairs, k_scale=None, v_scale=None):
+def copy_blocks(k_cache, v_cache, block_pairs, k_scale=None, v_scale=None, int4=False):
     """Copy whole blocks (every KV head) from source to destination inside one
     pool; block_pairs is int32 [n, 2] (a host array is moved to the GPU)."""
     lib = library()
@@ -572,8 +634,8 @@ def copy_blocks(k_cache, v_cache, block_pairs, k_scale=None, v_scale=None):
         block_pairs = torch.as_tensor(np.ascontiguousarray(block_pairs, np.int32).reshape(-1, 2),
                                       device=k_cache.device)
     n = block_pairs.shape[0]
-    i8 = k_cache.dtype in QUANTIZED
-    desc = CacheDesc.of(k_cache)
+    i8 = int4 or k_cache.dtype in QUANTIZED
+    desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
     _ok(lib.pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(k_scale, "k_scale", torch.float16) if i8 else None,
                            _dev(v_scale, "v_scale", torch.float16) if i8 else None,

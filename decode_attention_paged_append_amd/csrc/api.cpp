@@ -45,12 +45,22 @@ int elem_bytes(int32_t dtype) {
     case PA_BF16: return 2;
     case PA_I8: return 1;
     case PA_FP8: return 1;
+    case PA_I4: return 1;  // two codes per byte: see row_bytes
     default: return 0;
   }
 }
 
-// int8 or fp8 (E4M3) codes with fp16 per-(token, head) scales
-bool quantized(int32_t dtype) { return dtype == PA_I8 || dtype == PA_FP8; }
+// int8 or fp8 (E4M3) codes with fp16 per-(token, head) scales, or int4
+// codes with a scale per group of 32 dims
+bool quantized(int32_t dtype) { return dtype == PA_I8 || dtype == PA_FP8 || dtype == PA_I4; }
+
+// Bytes of one cached (token, head) row, and fp16 scales per row.
+int32_t row_bytes(const pa_cache_desc* c) {
+  return c->dtype == PA_I4 ? c->head_dim / 2 : c->head_dim * elem_bytes(c->dtype);
+}
+int32_t scales_per_row(const pa_cache_desc* c) {
+  return c->dtype == PA_I4 ? c->head_dim / 32 : quantized(c->dtype) ? 1 : 0;
+}
 
 bool supported_block(int32_t bs) { return bs == 4 || bs == 8 || bs == 16 || bs == 32; }
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
@@ -137,14 +147,18 @@ pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_head
   // dense enough for the matrix cores (fp16 / bf16 / int8 caches, blocks of
   // 16 or 32).  Otherwise the vector-ALU kernel, up to 8 heads per workgroup.
   const int32_t gc_mfma = group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : 0;
-  if (c->dtype != PA_F32 && (c->block_size == 16 || c->block_size == 32) && gc_mfma >= 4) {
+  if (c->dtype != PA_F32 && c->dtype != PA_I4 && (c->block_size == 16 || c->block_size == 32) &&
+      gc_mfma >= 4) {
     p.mfma = true;
     p.gc = gc_mfma;
+  } else if (c->dtype == PA_I4) {  // 32 values per lane and head: at most 2 heads
+    p.gc = group % 2 == 0 ? 2 : 1;
   } else {
     p.gc = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
   }
   p.chunks = group / p.gc;
-  p.tile = pa::tile_tokens(elem_bytes(c->dtype), c->head_dim, c->block_size);
+  // positions per tile: a block, or enough rows for one 1 KiB wave-load
+  p.tile = std::max<int32_t>(c->block_size, 1024 / row_bytes(c));
   const int64_t max_tok = (int64_t)max_blocks * c->block_size;
   int64_t part;
   if (requested > 0) {
@@ -237,6 +251,7 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
     case PA_BF16: e = pa::launch_decode_bf16(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
     case PA_I8: e = pa::launch_decode_i8(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
     case PA_FP8: e = pa::launch_decode_fp8(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
+    case PA_I4: e = pa::launch_decode_i4(p, cache->head_dim, cache->block_size, plan.gc, num_seqs, stream); break;
     default: return fail(PA_ERR_UNSUPPORTED, "dtype %d", cache->dtype);
   }
   return hip_status(e, "decode partitions launch");
@@ -268,8 +283,10 @@ pa_status decode_common(const void* q, const void* k_cache, const void* v_cache,
     return fail(PA_ERR_UNSUPPORTED,
                 want_dtype == PA_I8    ? "the int8 entry point needs an int8 cache"
                 : want_dtype == PA_FP8 ? "the fp8 entry point needs an fp8 cache"
+                : want_dtype == PA_I4  ? "the int4 entry point needs an int4 cache"
                 : cache->dtype == PA_I8 ? "int8 cache: use pa_paged_decode_attention_int8"
-                                        : "fp8 cache: use pa_paged_decode_attention_fp8");
+                : cache->dtype == PA_FP8 ? "fp8 cache: use pa_paged_decode_attention_fp8"
+                                         : "int4 cache: use pa_paged_decode_attention_int4");
   if (num_seqs == 0) return PA_OK;
   st = run_partitions(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks,
                       context_lens, num_seqs, num_q_heads, scale, out, cache, plan, workspace,
@@ -361,8 +378,9 @@ pa_status kv_append_quantized(const void* k_new, const void* v_new, const int64_
   pa_status st = check_cache(cache);
   if (st != PA_OK) return st;
   if (cache->dtype != want)
-    return fail(PA_ERR_UNSUPPORTED, want == PA_I8 ? "pa_kv_append_int8 needs an int8 cache"
-                                                  : "pa_kv_append_fp8 needs an fp8 cache");
+    return fail(PA_ERR_UNSUPPORTED, want == PA_I8    ? "pa_kv_append_int8 needs an int8 cache"
+                                    : want == PA_FP8 ? "pa_kv_append_fp8 needs an fp8 cache"
+                                                     : "pa_kv_append_int4 needs an int4 cache");
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
@@ -371,7 +389,8 @@ pa_status kv_append_quantized(const void* k_new, const void* v_new, const int64_
                                                v_cache, k_scale, v_scale, cache->num_kv_heads,
                                                cache->block_size, cache->head_dim,
                                                (int64_t)cache->num_blocks * cache->block_size,
-                                               want == PA_FP8, stream),
+                                               want == PA_I8 ? 0 : want == PA_FP8 ? 1 : 2,
+                                               stream),
                     "quantizing append launch");
 }
 
@@ -456,6 +475,26 @@ pa_status pa_paged_decode_attention_window(const void* q, const void* k_cache,
                        context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
                        workspace_bytes, (hipStream_t)stream,
                        quantized(cache->dtype) ? cache->dtype : -1, nullptr, nullptr, window);
+}
+
+pa_status pa_kv_append_int4(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                            int64_t num_tokens, void* k_cache, void* v_cache, void* k_scale,
+                            void* v_scale, const pa_cache_desc* cache, pa_stream_t stream) {
+  return kv_append_quantized(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, k_scale,
+                             v_scale, cache, PA_I4, (hipStream_t)stream);
+}
+
+pa_status pa_paged_decode_attention_int4(const void* q, const void* k_cache,
+                                         const void* v_cache, const void* k_scale,
+                                         const void* v_scale, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, float scale, void* out,
+                                         const pa_cache_desc* cache, void* workspace,
+                                         size_t workspace_bytes, pa_stream_t stream) {
+  return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
+                       workspace_bytes, (hipStream_t)stream, PA_I4);
 }
 
 pa_status pa_paged_decode_attention_fp8(const void* q, const void* k_cache,
@@ -561,14 +600,15 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
   if (num_seqs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_tables || !context_lens || !k_out || !v_out)
     return fail(PA_ERR_INVALID_ARG, "NULL pointer");
-  const int32_t row_bytes = cache->head_dim * elem_bytes(cache->dtype);
+  const int32_t rbytes = row_bytes(cache);
   const bool i8 = quantized(cache->dtype);
   return hip_status(pa::launch_gather_kv(k_cache, v_cache, i8 ? k_scale : nullptr,
                                          i8 ? v_scale : nullptr, block_tables, max_blocks_per_seq,
                                          context_lens, num_seqs, k_out, v_out,
                                          i8 ? k_scale_out : nullptr, i8 ? v_scale_out : nullptr,
                                          cache->num_blocks, cache->num_kv_heads,
-                                         cache->block_size, row_bytes, (hipStream_t)stream),
+                                         cache->block_size, rbytes, scales_per_row(cache),
+                                         (hipStream_t)stream),
                     "gather launch");
 }
 
@@ -635,13 +675,14 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_sc
   const bool i8 = quantized(cache->dtype);
   if (!k_cache || !v_cache || !block_pairs || (i8 && (!k_scale || !v_scale)))
     return fail(PA_ERR_INVALID_ARG, "NULL pointer");
-  const int32_t row_bytes = cache->head_dim * elem_bytes(cache->dtype);
-  if ((int64_t)cache->num_kv_heads * cache->block_size * row_bytes > ((int64_t)1 << 29))
+  const int32_t rbytes = row_bytes(cache);
+  if ((int64_t)cache->num_kv_heads * cache->block_size * rbytes > ((int64_t)1 << 29))
     return fail(PA_ERR_UNSUPPORTED, "blocks above 512 MiB per tensor");
   return hip_status(pa::launch_copy_blocks(k_cache, v_cache, i8 ? k_scale : nullptr,
                                            i8 ? v_scale : nullptr, block_pairs, num_pairs,
                                            cache->num_blocks, cache->num_kv_heads,
-                                           cache->block_size, row_bytes, (hipStream_t)stream),
+                                           cache->block_size, rbytes, scales_per_row(cache),
+                                           (hipStream_t)stream),
                     "copy_blocks launch");
 }
 

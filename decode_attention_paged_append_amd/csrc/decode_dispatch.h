@@ -15,13 +15,25 @@ static hipError_t launch_one(const DecodeParams& p, int num_seqs, hipStream_t st
   return hipGetLastError();
 }
 
+// Heads per workgroup of the vector-ALU kernel: up to 8, int4 up to 2 (its
+// lanes hold 32 values per head, twice the others).
+template <Fmt F>
+constexpr int max_heads_per_workgroup() { return F == Fmt::I4 ? 2 : 8; }
+
 template <Fmt F, int D, int BS>
 static hipError_t launch_gc(const DecodeParams& p, int gc, int num_seqs, hipStream_t stream) {
+  if (gc > max_heads_per_workgroup<F>()) return hipErrorInvalidValue;
   switch (gc) {
     case 1: return launch_one<F, D, BS, 1>(p, num_seqs, stream);
     case 2: return launch_one<F, D, BS, 2>(p, num_seqs, stream);
-    case 4: return launch_one<F, D, BS, 4>(p, num_seqs, stream);
-    case 8: return launch_one<F, D, BS, 8>(p, num_seqs, stream);
+    case 4:
+      if constexpr (max_heads_per_workgroup<F>() >= 4)
+        return launch_one<F, D, BS, 4>(p, num_seqs, stream);
+      return hipErrorInvalidValue;
+    case 8:
+      if constexpr (max_heads_per_workgroup<F>() >= 8)
+        return launch_one<F, D, BS, 8>(p, num_seqs, stream);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -98,5 +110,7 @@ hipError_t launch_decode_i8(const DecodeParams& p, int head_dim, int bs, int gc,
                             hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                              hipStream_t stream);
+hipError_t launch_decode_i4(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                            hipStream_t stream);
 
 }  // namespace pa

@@ -257,6 +257,56 @@ template <> struct Frag<Fmt::FP8> {
   }
 };
 
+// int4 codes: 32 per fragment (8 per word, dim i of a word in nibble i, as
+// code + 8), dotted with 32 fp16 query values; a fragment is one scale group.
+// Nibbles k and k+4 of a word come out together: (w >> 4k) & 0x000F000F under
+// the exponent pattern 0x6400 is the half pair 1024 + code + 8, minus 1032
+// gives the codes exactly.  The query words are regrouped once (prep_q) into
+// the same (k, k+4) pairs.
+template <> struct Frag<Fmt::I4> {
+  static constexpr int VE = 32;
+  static constexpr int QW = 16;
+  __device__ static __forceinline__ h16x2 pair(uint32_t w, int k) {
+    const h16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+    return as_h2(((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - bias;
+  }
+  __device__ static __forceinline__ void prep_q(uint32_t* q) {
+    uint32_t r[QW];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // halves 8j+k and 8j+k+4 of the lane's 32 query values
+        const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+        r[4 * j + k] = __builtin_amdgcn_perm(q[4 * j + 2 + k / 2], q[4 * j + k / 2], sel);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < QW; ++i) q[i] = r[i];
+  }
+  __device__ static __forceinline__ float dot(const uint32_t* q, u32x4 k) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s = __builtin_amdgcn_fdot2(as_h2(q[4 * j + kk]), pair(k[j], kk), s, false);
+    }
+    return s;
+  }
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const h16x2 h = pair(v[j], kk);
+        f[8 * j + kk] = (float)h[0];
+        f[8 * j + kk + 4] = (float)h[1];
+      }
+    }
+  }
+};
+
 // Result of one workgroup for one query head row of one sequence: final when
 // the partition is the sequence's only one, else a partial (running max M in
 // log2 units, sum L, unnormalized output) for the log-sum-exp merge.
@@ -276,10 +326,12 @@ __device__ __forceinline__ void store_result(const DecodeParams& p, bool direct,
 }
 
 template <Fmt F, int D, int BS, int GC, int NW>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(GC == 1 ? 8 : GC == 2 ? 4 : 1, 8)))
+// Occupancy hint: int4 lanes hold 32 values per head (the others 16 or
+// fewer), so they get twice the registers.
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(
+    F == Fmt::I4 ? (GC == 1 ? 4 : 2) : GC == 1 ? 8 : GC == 2 ? 4 : 1, 8)))
 void decode_partition_kernel(const DecodeParams p) {
   using FR = Frag<F>;
-  constexpr int CB = FmtInfo<F>::bytes;       // bytes per cache element
   constexpr int QB = FmtInfo<F>::q_bytes;     // bytes per query element
   constexpr int VE = FR::VE;                  // elements per 16-byte fragment
   constexpr int LR = D / VE;                  // lanes per row
@@ -287,7 +339,9 @@ void decode_partition_kernel(const DecodeParams p) {
   constexpr int TT = BS > RPI ? BS : RPI;     // positions per tile
   constexpr int NJ = TT / RPI;                // fragments per lane per tile (K, and V)
   constexpr int BPT = TT / BS;                // blocks per tile
-  constexpr int ROWB = D * CB;                // bytes per cached row
+  constexpr int ROWB = LR * 16;               // bytes per cached row (D * CB, or D / 2)
+  constexpr bool kInt4 = F == Fmt::I4;
+  constexpr int SPR = kInt4 ? D / kInt4Group : 1;  // scales per cached row
   constexpr bool kQuant = FmtInfo<F>::quantized;
   static_assert(LR >= 1 && LR <= kWave && (kWave % LR) == 0, "row must split over lanes");
   static_assert(TT % RPI == 0 && TT % BS == 0, "tile must be whole loads and blocks");
@@ -343,6 +397,7 @@ void decode_partition_kernel(const DecodeParams p) {
                                            ((out_row0 + g) * D + (size_t)lcol * VE) * QB);
 #pragma unroll
     for (int w = 0; w < FR::QW; ++w) qf[g][w] = qp[w];
+    if constexpr (kInt4) FR::prep_q(qf[g]);
   }
 
   float m[GC], l[GC], acc[GC][VE];
@@ -405,8 +460,10 @@ void decode_partition_kernel(const DecodeParams p) {
       }
       if constexpr (kQuant) {
         constexpr float cs = FmtInfo<F>::code_scale;
-        ks[j] = valid ? (float)__builtin_bit_cast(_Float16, p.k_scale[row]) * cs : 0.0f;
-        vs[j] = valid ? (float)__builtin_bit_cast(_Float16, p.v_scale[row]) * cs : 0.0f;
+        // int4: the lane's 32 dims are scale group lcol of the row
+        const size_t si = kInt4 ? row * SPR + lcol : row;
+        ks[j] = valid ? (float)__builtin_bit_cast(_Float16, p.k_scale[si]) * cs : 0.0f;
+        vs[j] = valid ? (float)__builtin_bit_cast(_Float16, p.v_scale[si]) * cs : 0.0f;
       } else {
         ks[j] = 1.0f;
         vs[j] = 1.0f;
@@ -421,8 +478,14 @@ void decode_partition_kernel(const DecodeParams p) {
     for (int g = 0; g < GC; ++g) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const float d = group_sum<LR>(FR::dot(qf[g], kf[j]));
-        z[g][j] = kQuant ? d * (ks[j] * p.scale_log2) : d * p.scale_log2;
+        float z0;
+        if constexpr (kInt4) {  // each lane's group has its own scale
+          z0 = group_sum<LR>(FR::dot(qf[g], kf[j]) * ks[j]) * p.scale_log2;
+        } else {
+          const float d = group_sum<LR>(FR::dot(qf[g], kf[j]));
+          z0 = kQuant ? d * (ks[j] * p.scale_log2) : d * p.scale_log2;
+        }
+        z[g][j] = z0;
         if (PARTIAL && (j * RPI + lrow >= nvalid || j * RPI + lrow < nlow))
           z[g][j] = -__builtin_inff();
       }

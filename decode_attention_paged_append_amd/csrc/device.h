@@ -18,7 +18,10 @@ constexpr int kWave = 64;
 constexpr float kMaxInit = -1.0e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum class Fmt : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3, FP8 = 4 };
+enum class Fmt : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3, FP8 = 4, I4 = 5 };
+
+// int4 caches: one fp16 scale per group of this many dims of a row.
+constexpr int kInt4Group = 32;
 
 // bytes: cache element; q_bytes: query/output element.  Quantized caches
 // (int8, fp8 E4M3) hold codes with an fp16 scale per (token, head) and take
@@ -46,6 +49,13 @@ template <> struct FmtInfo<Fmt::FP8> {
   static constexpr int bytes = 1, q_bytes = 2;
   static constexpr bool quantized = true;
   static constexpr float code_scale = 256.0f;
+};
+// int4: two codes per byte (bytes = 0 marks the packed format; rows are D/2
+// bytes), a scale per kInt4Group dims.
+template <> struct FmtInfo<Fmt::I4> {
+  static constexpr int bytes = 0, q_bytes = 2;
+  static constexpr bool quantized = true;
+  static constexpr float code_scale = 1.0f;
 };
 
 __device__ __forceinline__ float bits_to_float(uint32_t u) { return __builtin_bit_cast(float, u); }

@@ -16,22 +16,22 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
                             int64_t num_tokens, void* k_cache, void* v_cache,
                             int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,
                             int64_t pool_slots, hipStream_t stream);
-// Quantizing append into an int8 (fp8 false) or fp8 E4M3 (fp8 true) cache.
+// Quantizing append into an int8 (kind 0), fp8 E4M3 (1) or int4 (2) cache.
 hipError_t launch_kv_append_quant(const void* k_new, const void* v_new, const int64_t* slots,
                                   int64_t num_tokens, void* k_cache, void* v_cache,
                                   void* k_scale, void* v_scale, int32_t num_kv_heads,
                                   int32_t block_size, int32_t head_dim, int64_t pool_slots,
-                                  bool fp8, hipStream_t stream);
+                                  int kind, hipStream_t stream);
 hipError_t launch_gather_kv(const void* k_cache, const void* v_cache, const void* k_scale,
                             const void* v_scale, const int32_t* tables, int32_t max_blocks,
                             const int32_t* context_lens, int32_t num_seqs, void* k_out,
                             void* v_out, void* k_scale_out, void* v_scale_out,
                             int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
-                            int32_t row_bytes, hipStream_t stream);
+                            int32_t row_bytes, int32_t scales_per_row, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,
                               const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
                               int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,
-                              hipStream_t stream);
+                              int32_t scales_per_row, hipStream_t stream);
 
 // Log-sum-exp merge of partition partials (lse_merge.hip).
 // window > 0: partials are stored by window slot (the partition holding the

@@ -89,20 +89,26 @@ __device__ __forceinline__ uint32_t e4m3_code(float r) {
   return code | (r < 0.0f && code != 0u ? 0x80u : 0u);
 }
 
-// Quantizing append, int8 or fp8 (E4M3) codes with one fp16 scale per
-// (token, head) row.  LQ = D/8 lanes hold one row of fp16 values, 8 each.
-//   a = max |x| over the row (exact);  s = fp16(a / R)  (IEEE fp32 divide,
-//   round to nearest even), R = 127 (int8) or 448 (E4M3 maximum);
+// Quantizing append.  LQ = D/8 lanes hold one (token, head) row of fp16
+// values, 8 each.  KIND 0: int8, 1: fp8 (E4M3), both with one fp16 scale per
+// row; KIND 2: int4, with one scale per group of kInt4Group dims (the 4
+// lanes of the group).  Over the row (int4: the group):
+//   a = max |x| (exact);  s = fp16(a / R) (IEEE fp32 divide, round to nearest
+//   even), R = 127, 448 or 7;
 //   int8: code = clamp(rint(x / s), -127, 127);  fp8: code = E4M3(x / s);
+//   int4: code = clamp(rint(x / s), -7, 7), stored as the nibble code + 8
+//   (dim 2i low, 2i + 1 high in byte i);
 //   codes are 0 when s == 0 (and for a NaN input).
-template <int D, bool FP8>
+template <int D, int KIND>
 __global__ __launch_bounds__(256) void kv_append_quant_kernel(
     const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
-    const int64_t* __restrict__ slots, int64_t num_tokens, u32x2* __restrict__ k_cache,
-    u32x2* __restrict__ v_cache, uint16_t* __restrict__ k_scale, uint16_t* __restrict__ v_scale,
+    const int64_t* __restrict__ slots, int64_t num_tokens, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, uint16_t* __restrict__ k_scale, uint16_t* __restrict__ v_scale,
     int32_t num_kv_heads, int32_t block_size, int64_t pool_slots) {
   constexpr int LQ = D / 8;  // lanes per row
-  constexpr float R = FP8 ? 448.0f : 127.0f;
+  constexpr bool kInt4 = KIND == 2;
+  constexpr int LG = kInt4 ? kInt4Group / 8 : LQ;  // lanes sharing a scale
+  constexpr float R = KIND == 1 ? 448.0f : KIND == 2 ? 7.0f : 127.0f;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / LQ;        // (token, head) row
   const int c = (int)(gid % LQ);       // 8-value piece of the row
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(256) void kv_append_quant_kernel(
     kx = k_new[row * LQ + c];
     vx = v_new[row * LQ + c];
   }
-  auto quantize = [&](u32x4 x, u32x2* cache, uint16_t* scales) {
+  auto quantize = [&](u32x4 x, uint8_t* cache, uint16_t* scales) {
     float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -128,29 +134,42 @@ __global__ __launch_bounds__(256) void kv_append_quant_kernel(
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
-    a = group_max<LQ>(a);
+    a = group_max<LG>(a);
     const _Float16 s16 = (_Float16)(a / R);
     const float s = (float)s16;
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint32_t code = 0u;
-      if (s != 0.0f) {
-        if constexpr (FP8) {
-          code = e4m3_code(f[i] / s);
+      if constexpr (KIND == 1) {
+        if (s != 0.0f) code = e4m3_code(f[i] / s);
+        packed[i / 4] |= code << (8 * (i % 4));
+      } else {
+        const float lim = kInt4 ? 7.0f : 127.0f;
+        float r = 0.0f;
+        if (s != 0.0f) {
+          r = rintf(f[i] / s);
+          r = r != r ? 0.0f : fminf(fmaxf(r, -lim), lim);
+        }
+        if constexpr (kInt4) {
+          packed[0] |= ((uint32_t)((int32_t)r + 8) & 0xfu) << (4 * i);
         } else {
-          const float r = rintf(f[i] / s);
-          code = (uint32_t)(int32_t)(r != r ? 0.0f : fminf(fmaxf(r, -127.0f), 127.0f)) & 0xffu;
+          packed[i / 4] |= ((uint32_t)(int32_t)r & 0xffu) << (8 * (i % 4));
         }
       }
-      packed[i / 4] |= code << (8 * (i % 4));
     }
     if (store) {
       const int64_t block = slot / block_size;
       const int64_t off = slot - block * block_size;
       const int64_t dst_row = (block * num_kv_heads + h) * block_size + off;
-      cache[dst_row * LQ + c] = u32x2{packed[0], packed[1]};
-      if (c == 0) scales[dst_row] = __builtin_bit_cast(uint16_t, s16);
+      if constexpr (kInt4) {
+        ((uint32_t*)cache)[dst_row * LQ + c] = packed[0];  // D/2 bytes per row
+        if (c % LG == 0)
+          scales[dst_row * (D / kInt4Group) + c / LG] = __builtin_bit_cast(uint16_t, s16);
+      } else {
+        ((u32x2*)cache)[dst_row * LQ + c] = u32x2{packed[0], packed[1]};
+        if (c == 0) scales[dst_row] = __builtin_bit_cast(uint16_t, s16);
+      }
     }
   };
   quantize(kx, k_cache, k_scale);
@@ -169,7 +188,8 @@ __global__ void gather_kv_kernel(const char* __restrict__ k_cache, const char* _
                                  char* __restrict__ k_out, char* __restrict__ v_out,
                                  uint16_t* __restrict__ k_scale_out,
                                  uint16_t* __restrict__ v_scale_out, int32_t num_blocks,
-                                 int32_t num_kv_heads, int32_t block_size, int32_t row_bytes) {
+                                 int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,
+                                 int32_t scales_per_row) {
   const int32_t pieces = row_bytes / 16;
   const int64_t cap = (int64_t)max_blocks * block_size;
   const int64_t total = (int64_t)num_seqs * cap * num_kv_heads * pieces;
@@ -190,8 +210,11 @@ __global__ void gather_kv_kernel(const char* __restrict__ k_cache, const char* _
         *(const u32x4*)(k_cache + src_row * row_bytes + c * 16);
     *(u32x4*)(v_out + dst_row * row_bytes + c * 16) =
         *(const u32x4*)(v_cache + src_row * row_bytes + c * 16);
-    if (c == 0 && k_scale && k_scale_out) k_scale_out[dst_row] = k_scale[src_row];
-    if (c == 0 && v_scale && v_scale_out) v_scale_out[dst_row] = v_scale[src_row];
+    // scales: one per row, or (int4) one per 16-byte piece = 32 dims
+    if (c < scales_per_row && k_scale && k_scale_out)
+      k_scale_out[dst_row * scales_per_row + c] = k_scale[src_row * scales_per_row + c];
+    if (c < scales_per_row && v_scale && v_scale_out)
+      v_scale_out[dst_row * scales_per_row + c] = v_scale[src_row * scales_per_row + c];
   }
 }
 
@@ -234,20 +257,23 @@ hipError_t launch_kv_append_quant(const void* k_new, const void* v_new, const in
                                   int64_t num_tokens, void* k_cache, void* v_cache,
                                   void* k_scale, void* v_scale, int32_t num_kv_heads,
                                   int32_t block_size, int32_t head_dim, int64_t pool_slots,
-                                  bool fp8, hipStream_t stream) {
+                                  int kind, hipStream_t stream) {
   const int64_t lanes = num_tokens * num_kv_heads * (head_dim / 8);
   const dim3 grid(blocks_for(lanes, 256));
-#define PA_APPEND_Q(D, FP8)                                                                    \
-  hipLaunchKernelGGL((kv_append_quant_kernel<D, FP8>), grid, dim3(256), 0, stream,              \
+#define PA_APPEND_Q(D, KIND)                                                                   \
+  hipLaunchKernelGGL((kv_append_quant_kernel<D, KIND>), grid, dim3(256), 0, stream,             \
                      (const u32x4*)k_new, (const u32x4*)v_new, slots, num_tokens,               \
-                     (u32x2*)k_cache, (u32x2*)v_cache, (uint16_t*)k_scale, (uint16_t*)v_scale, \
-                     num_kv_heads, block_size, pool_slots)
+                     (uint8_t*)k_cache, (uint8_t*)v_cache, (uint16_t*)k_scale,                  \
+                     (uint16_t*)v_scale, num_kv_heads, block_size, pool_slots)
+  if (kind < 0 || kind > 2) return hipErrorInvalidValue;
   if (head_dim == 64) {
-    if (fp8) PA_APPEND_Q(64, true);
-    else PA_APPEND_Q(64, false);
+    if (kind == 0) PA_APPEND_Q(64, 0);
+    else if (kind == 1) PA_APPEND_Q(64, 1);
+    else PA_APPEND_Q(64, 2);
   } else if (head_dim == 128) {
-    if (fp8) PA_APPEND_Q(128, true);
-    else PA_APPEND_Q(128, false);
+    if (kind == 0) PA_APPEND_Q(128, 0);
+    else if (kind == 1) PA_APPEND_Q(128, 1);
+    else PA_APPEND_Q(128, 2);
   } else {
     return hipErrorInvalidValue;
   }
@@ -260,7 +286,7 @@ hipError_t launch_gather_kv(const void* k_cache, const void* v_cache, const void
                             const int32_t* context_lens, int32_t num_seqs, void* k_out,
                             void* v_out, void* k_scale_out, void* v_scale_out,
                             int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
-                            int32_t row_bytes, hipStream_t stream) {
+                            int32_t row_bytes, int32_t scales_per_row, hipStream_t stream) {
   const int64_t total = (int64_t)num_seqs * max_blocks * block_size * num_kv_heads * (row_bytes / 16);
   const int64_t want = (total + 255) / 256;
   const unsigned grid = (unsigned)(want < 65536 ? (want > 0 ? want : 1) : 65536);
@@ -268,7 +294,7 @@ hipError_t launch_gather_kv(const void* k_cache, const void* v_cache, const void
                      (const char*)v_cache, (const uint16_t*)k_scale, (const uint16_t*)v_scale,
                      tables, max_blocks, context_lens, num_seqs, (char*)k_out, (char*)v_out,
                      (uint16_t*)k_scale_out, (uint16_t*)v_scale_out, num_blocks, num_kv_heads,
-                     block_size, row_bytes);
+                     block_size, row_bytes, scales_per_row);
   return hipGetLastError();
 }
 
@@ -312,12 +338,12 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,
                               const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
                               int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,
-                              hipStream_t stream) {
+                              int32_t scales_per_row, hipStream_t stream) {
   const int64_t block_pieces = (int64_t)num_kv_heads * block_size * (row_bytes / 16);
   const int32_t chunks = (int32_t)((block_pieces + kCopyChunkPieces - 1) / kCopyChunkPieces);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2 * chunks), dim3(256), 0, stream,
                      (u32x4*)k_cache, (u32x4*)v_cache, (uint16_t*)k_scale, (uint16_t*)v_scale,
-                     pairs, num_blocks, block_pieces, num_kv_heads * block_size, chunks);
+                     pairs, num_blocks, block_pieces, num_kv_heads * block_size * scales_per_row, chunks);
   return hipGetLastError();
 }
 

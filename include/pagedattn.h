@@ -23,7 +23,10 @@
  *                      one contiguous block_size x head_dim tile per
  *                      (block, KV head)
  *   k_scale, v_scale : [num_blocks][num_kv_heads][block_size] fp16, quantized
- *                      (int8, fp8) caches only
+ *                      (int8, fp8) caches only; int4: [...][block_size][head_dim/32]
+ *   int4 k/v_cache   : [num_blocks][num_kv_heads][block_size][head_dim/2] bytes,
+ *                      dim 2i in the low nibble of byte i, 2i+1 in the high
+ *                      nibble, each stored as code + 8 (code in [-7, 7])
  *   block_tables     : int32 [num_seqs][max_blocks_per_seq]; entry j of row s
  *                      is the pool block holding positions [j*BS, (j+1)*BS)
  *                      of sequence s.  Entries past ceil(ctx/BS) are never read.
@@ -37,8 +40,9 @@
  * memory").
  *
  * Supported: head_dim in {64, 128}; block_size in {4, 8, 16, 32}; element
- * formats fp32, fp16, bf16 (q, caches and out share one format), and int8 or
- * fp8 (E4M3) caches with fp16 q/out and per-(token, head) fp16 scales.
+ * formats fp32, fp16, bf16 (q, caches and out share one format), int8 or fp8
+ * (E4M3) caches with fp16 q/out and per-(token, head) fp16 scales, and int4
+ * caches with fp16 q/out and fp16 scales per (token, head, 32 dims).
  *
  * Errors: arguments are checked on the host before anything is enqueued.
  * A non-PA_OK status means nothing was enqueued (except PA_ERR_HIP, which
@@ -71,7 +75,8 @@ typedef enum {
   PA_F16 = 1,
   PA_BF16 = 2,
   PA_I8 = 3,
-  PA_FP8 = 4  /* OCP fp8 E4M3 codes (1 sign, 4 exponent bits of bias 7, 3 fraction bits) */
+  PA_FP8 = 4, /* OCP fp8 E4M3 codes (1 sign, 4 exponent bits of bias 7, 3 fraction bits) */
+  PA_I4 = 5   /* int4 codes, two per byte, a scale per 32 dims (layout below) */
 } pa_dtype;
 
 typedef enum {
@@ -156,6 +161,20 @@ pa_status pa_kv_append_fp8(const void* k_new, const void* v_new,
                            void* k_cache, void* v_cache, void* k_scale, void* v_scale,
                            const pa_cache_desc* cache, pa_stream_t stream);
 
+/* int4 cache (the 4-bit half of [viz] "What the page leaves out"'s "8-bit or
+ * 4-bit"; groups and rounding are this library's reading): for every group of
+ * 32 consecutive dims of a (token, head) row of fp16 values x,
+ *   a = max |x|,  s = fp16_rne(fp32(a / 7)),
+ *   code = clamp(rint_half_even(fp32(x / s)), -7, 7)   (0 when s == 0 or x is
+ *   NaN), stored as the nibble code + 8.
+ * Codes go to k_cache/v_cache (device bytes [NB][Hkv][BS][D/2],
+ * cache->dtype == PA_I4), the group scales to k_scale/v_scale (device fp16
+ * [NB][Hkv][BS][D/32]).  k_new, v_new: device fp16 [num_tokens][Hkv][D]. */
+pa_status pa_kv_append_int4(const void* k_new, const void* v_new,
+                            const int64_t* slot_mapping, int64_t num_tokens,
+                            void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                            const pa_cache_desc* cache, pa_stream_t stream);
+
 /* ---------------------------------------------------------------- attention */
 
 /* Workspace the decode entry points need for this shape: fp32 partial
@@ -215,6 +234,18 @@ pa_status pa_paged_decode_attention_fp8(const void* q, const void* k_cache,
                                         int32_t num_q_heads, float scale, void* out,
                                         const pa_cache_desc* cache, void* workspace,
                                         size_t workspace_bytes, pa_stream_t stream);
+
+/* The same over an int4 cache: keys and values are code * (the scale of the
+ * code's 32-dim group), exact in binary32; q and out fp16.  Runs on the
+ * vector-ALU kernel at any group size. */
+pa_status pa_paged_decode_attention_int4(const void* q, const void* k_cache,
+                                         const void* v_cache, const void* k_scale,
+                                         const void* v_scale, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, float scale, void* out,
+                                         const pa_cache_desc* cache, void* workspace,
+                                         size_t workspace_bytes, pa_stream_t stream);
 
 /* One decode step for a fp32 / fp16 / bf16 cache: store each
  * sequence's new K and V rows (k_new, v_new: device [S][Hkv][D] in the
@@ -412,7 +443,7 @@ int32_t pa_bm_sequence_length(const pa_block_manager* bm, int32_t seq); /* -1 if
  * one holder writes into it).  block_pairs: device int32 [num_pairs][2] of
  * (source, destination) block ids; every KV head's rows of the source block
  * are copied to the destination block, in k_cache and v_cache, and for an
- * int8 or fp8 cache also in k_scale and v_scale (NULL otherwise).  Pairs with an id
+ * int8, fp8 or int4 cache also in k_scale and v_scale (NULL otherwise).  Pairs with an id
  * outside [0, num_blocks) are skipped.  A destination must not be the source
  * or the destination of another pair in the same call. */
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,

@@ -23,15 +23,17 @@ import torch
 SEED_DATA, SEED_TABLES, SEED_LENGTHS = 0, 1, 2
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-               "i8": torch.int8, "fp8": torch.float8_e4m3fn}
+               "i8": torch.int8, "fp8": torch.float8_e4m3fn,
+               "i4": torch.uint8}   # int4: two codes per byte, [NB, Hkv, BS, D/2]
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "fp8": 1}
-QUANTIZED = ("i8", "fp8")   # codes + fp16 per-(token, head) scales
+QUANTIZED = ("i8", "fp8", "i4")   # codes + fp16 scales (i4: one per 32 dims)
+INT4_GROUP = 32
 
 
 @dataclasses.dataclass(frozen=True)
 class Shape:
     name: str
-    cache_dtype: str          # "f32" | "f16" | "bf16" | "i8" | "fp8"
+    cache_dtype: str          # "f32" | "f16" | "bf16" | "i8" | "fp8" | "i4"
     num_seqs: int
     num_q_heads: int
     num_kv_heads: int
@@ -75,8 +77,12 @@ LLAMA3_8B_WINDOW = Shape("llama3-8b-f16-window4k", "f16", 16, 32, 8, 128, 16, la
                                      "of 4096 positions, 32 layers",
                          window=4096)
 
+LLAMA3_8B_I4 = Shape("llama3-8b-int4kv", "i4", 64, 32, 8, 128, 16,
+                     description="Llama-3-8B layer, int4 KV + fp16 scales per 32 dims, "
+                                 "64 seqs x 8192")
+
 SHAPES = {s.name: s for s in (TINY, LLAMA3_8B, LLAMA2_7B, LLAMA2_70B, LLAMA3_8B_I8,
-                              LLAMA3_8B_FP8, LLAMA3_8B_WINDOW)}
+                              LLAMA3_8B_FP8, LLAMA3_8B_WINDOW, LLAMA3_8B_I4)}
 
 TINY_POOL_BLOCKS = 64
 PREFIX_GROUP = 8          # sequences per shared-prefix group (Llama-2-70B workload)
@@ -95,7 +101,7 @@ def context_lengths(shape: Shape) -> list[int]:
         return [3, 7, 16, 33]
     if shape.name in (LLAMA3_8B.name, LLAMA2_7B.name):
         return [4096] * shape.num_seqs
-    if shape.name in (LLAMA3_8B_I8.name, LLAMA3_8B_FP8.name):
+    if shape.name in (LLAMA3_8B_I8.name, LLAMA3_8B_FP8.name, LLAMA3_8B_I4.name):
         return [8192] * shape.num_seqs
     if shape.name == LLAMA3_8B_WINDOW.name:
         return [16384] * shape.num_seqs
@@ -262,6 +268,9 @@ def kv_bytes_per_layer_step(shape: Shape, ctx_lens) -> int:
     its whole context, shared blocks included, or its last `window` positions),
     plus the scale bytes of a quantized cache."""
     total = sum(min(int(c), shape.window) if shape.window > 0 else int(c) for c in ctx_lens)
+    if shape.cache_dtype == "i4":   # half a byte per value, a scale per 32 values
+        return total * shape.num_kv_heads * 2 * (shape.head_dim // 2 +
+                                                 2 * (shape.head_dim // INT4_GROUP))
     b = total * shape.num_kv_heads * shape.head_dim * 2 * ELEM_BYTES[shape.cache_dtype]
     if shape.cache_dtype in QUANTIZED:
         b += total * shape.num_kv_heads * 2 * 2
