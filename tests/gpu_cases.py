@@ -2,6 +2,8 @@
 the CPU oracle on the same seeded inputs, and compare."""
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -95,5 +97,12 @@ def quantize_blocks_oracle(src_k, src_v, blocks, fmt="i8"):
     ks = np.zeros((nb, hkv, bs), np.float16)
     vs = np.zeros_like(ks)
     append = oracle.kv_append_int8 if fmt == "i8" else oracle.kv_append_fp8
-    append(rows_k, rows_v, slots, kq, vq, ks, vs)
+    # chunks of whole blocks write disjoint slots: run them on host threads
+    # (the oracle's C routine runs without the interpreter lock)
+    n = rows_k.shape[0]
+    step = -(-max(n // bs, 1) // 8) * bs
+    spans = [(a, min(a + step, n)) for a in range(0, n, step)]
+    with ThreadPoolExecutor(len(spans)) as ex:
+        list(ex.map(lambda s: append(rows_k[s[0]:s[1]], rows_v[s[0]:s[1]], slots[s[0]:s[1]],
+                                     kq, vq, ks, vs), spans))
     return kq, vq, ks, vs, blocks

@@ -95,9 +95,8 @@ def test_fp8_full_size_sampled():
     print("fp8 full size", flush=True)
     kq, vq, ks, vs = quantize_pool_gpu(case.k_cache, case.v_cache, None, "fp8")
     rng = np.random.default_rng(6)
-    pairs = [(int(rng.integers(shape.num_seqs)), int(rng.integers(shape.num_q_heads)))
-             for _ in range(24)]
-    seqs = sorted({s for s, _ in pairs})
+    seqs = [0, 29, shape.num_seqs - 1]
+    pairs = [(s, int(rng.integers(shape.num_q_heads))) for s in seqs for _ in range(6)]
     blocks = lay.block_tables[seqs].flatten()
     okq, ovq, oks, ovs, used = quantize_blocks_oracle(case.k_cache, case.v_cache,
                                                       blocks[blocks >= 0], "fp8")
