@@ -83,9 +83,11 @@ class Bench:
             # the library plans a windowed call itself (partitions + merge)
             self.wws = torch.empty(max(pa.decode_window_workspace_bytes(
                 desc, s, hq, lay.max_blocks, self.window), 256), dtype=torch.uint8, device=dev)
-        # the library routes >= 4 query heads per KV head with 16/32 blocks to matrix cores
-        self.mfma = (shape.cache_dtype not in ("f32", "i4") and shape.block_size in (16, 32)
-                     and shape.group % 4 == 0)
+        # the library routes >= 4 query heads per KV head with 16/32 blocks to
+        # matrix cores (int4: at head_dim 128)
+        self.mfma = (shape.cache_dtype != "f32" and shape.block_size in (16, 32)
+                     and shape.group % 4 == 0
+                     and (shape.cache_dtype != "i4" or shape.head_dim == 128))
         self.nparts = -(-lay.max_blocks * shape.block_size // self.part)
         nbytes = pa.decode_workspace_bytes(desc, s, hq, lay.max_blocks, self.part)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
@@ -426,6 +428,41 @@ def prefill_bench(name, dev, steps, warmup, cpu: bool) -> dict:
     }
 
 
+def attention_launch_ms(b, layers, steps):
+    """Average duration of the dominant kernel: the same launches (every
+    layer, K times) back to back between two events on the stream they run
+    on.  They are captured once in a HIP graph and replayed, so that neither
+    per-launch events nor the binding's host work between launches (which a
+    short kernel would wait on) enter the figure; if capture fails, the
+    launches are issued directly."""
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def launches():
+        for _ in range(steps):
+            for layer in range(layers):
+                b.attend(layer)
+
+    try:
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            launches()
+        graph.replay()                      # first replay: untimed
+        torch.cuda.synchronize()
+        k0.record()
+        graph.replay()
+        k1.record()
+        how = "hip graph replay of the launches"
+    except RuntimeError:
+        torch.cuda.synchronize()
+        k0.record()
+        launches()
+        k1.record()
+        how = "launches issued back to back"
+    torch.cuda.synchronize()
+    return k0.elapsed_time(k1) / (steps * layers), how
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -488,18 +525,7 @@ def main():
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
 
-    # The dominant kernel's average launch duration: the same launches (every
-    # layer, K times) back to back between two events, so that per-launch
-    # event overhead does not inflate it.
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    k0.record()
-    for _ in range(args.steps):
-        for layer in range(layers):
-            b.attend(layer)
-    k1.record()
-    torch.cuda.synchronize()
-    kernel_ms = k0.elapsed_time(k1) / (args.steps * layers)
+    kernel_ms, kernel_timing = attention_launch_ms(b, layers, args.steps)
 
     kv_step = b.kv_bytes_per_layer() * layers
     value = kv_step / (ms_step / 1e3) / 1e9
@@ -539,7 +565,8 @@ def main():
         "kv_bytes_per_step": kv_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("decode_mfma_kernel" if b.mfma else "decode_partition_kernel")
+            "kernel": (("decode_mfma_i4_kernel" if b.int4 else "decode_mfma_kernel") if b.mfma
+                       else "decode_partition_kernel")
                       + (" + lse_merge_kernel (one windowed call)" if b.window else ""),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
@@ -548,6 +575,7 @@ def main():
             "traffic": traffic_block(io),
             "bytes_per_launch": io,
             "avg_launch_ms": round(kernel_ms, 5),
+            "timing": kernel_timing,
         },
         "cpu_baseline": None,
     }

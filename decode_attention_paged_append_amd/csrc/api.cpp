@@ -94,6 +94,7 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
       case PA_BF16: e = pa::launch_mfma_bf16(p, D, BS, plan.gc, num_seqs, stream); break;
       case PA_I8: e = pa::launch_mfma_i8(p, D, BS, plan.gc, num_seqs, stream); break;
       case PA_FP8: e = pa::launch_mfma_fp8(p, D, BS, plan.gc, num_seqs, stream); break;
+      case PA_I4: e = pa::launch_mfma_i4(p, D, BS, plan.gc, num_seqs, stream); break;
       default: return fail(PA_ERR_UNSUPPORTED, "dtype %d", cache->dtype);
     }
     return hip_status(e, "decode partitions launch");

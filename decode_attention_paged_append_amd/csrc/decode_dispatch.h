@@ -60,8 +60,9 @@ static hipError_t launch_fmt(const DecodeParams& p, int head_dim, int bs, int gc
   }
 }
 
-// ---- matrix-core kernel for grouped-query heads (fp16 / bf16 / int8 caches,
-// block size 16 or 32, 4..16 query heads per workgroup)
+// ---- matrix-core kernel for grouped-query heads (fp16 / bf16 / int8 / fp8
+// caches, int4 at head_dim 128; block size 16 or 32, 4..16 query heads per
+// workgroup)
 template <Fmt F, int D, int BS, int GC>
 static hipError_t launch_mfma_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_parts, (unsigned)(p.num_kv_heads * p.head_chunks),
@@ -99,6 +100,8 @@ hipError_t launch_mfma_i8(const DecodeParams& p, int head_dim, int bs, int gc, i
                           hipStream_t stream);
 hipError_t launch_mfma_fp8(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                            hipStream_t stream);
+hipError_t launch_mfma_i4(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
+                          hipStream_t stream);  // head_dim 128, 4 or 8 heads per workgroup
 
 hipError_t launch_decode_f32(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                              hipStream_t stream);

@@ -1,0 +1,383 @@
+// decode_mfma_i4.h -- grouped-query paged decode attention over an int4 cache
+// on the matrix cores (head_dim 128).
+//
+// Same computation and partials as the other decode kernels (phase 1 of the
+// decode: "KV cache: the engine behind fast LLM inference", "Concept" and
+// step 3; online softmax per "Flash attention: don't build the giant
+// matrix"), over a cache of 4-bit codes with an fp16 scale per 32 dims (the
+// 4-bit half of "What the page leaves out" on the KV-cache visualization
+// page).  A cached value is (nibble - 8) * scale of its group.
+//
+// An int4 tile carries a quarter of the bytes of an fp16 one, so the work of
+// widening codes decides the speed.  Both products take the codes exactly,
+// as fp16 subnormals: the byte 0x0n under a zero high byte is n * 2^-24.
+// One AND / shift splits a word into even and odd nibbles, one v_perm then
+// builds a pair of subnormals; the +8 of the stored nibbles is taken out
+// once per product, never per element.
+//
+//  * Scores.  One 16x16x32 MFMA contracts exactly one scale group (32 dims),
+//    so each group's product has its own accumulator, started at
+//    -8 * 2^-24 * sum(q over the group) to remove the bias, and the key
+//    scale multiplies it in fp32 (v_fma_mix on the fp16 scale).
+//  * Values.  O^T[dim][col] += V^T[dim][tok] . B[tok][col] with the sixteen
+//    columns taken as (head, scale group) pairs: column n is head n % 4 of
+//    the column set and group n / 4, and B = p * (value scale of that group),
+//    rounded to fp16 like the weights of the 16-bit caches.  Lane (g, n)'s
+//    rows are dims 8(4g+i)+e, all in group g, so the lanes with n / 4 == g
+//    hold the result: 2^24 * O^T - 8 * (column sum of B), the column sums
+//    kept beside the running sums.
+//  * Four heads per column set; the score MFMA repeats each head's query in
+//    all four groups of columns, so every lane already holds the weights of
+//    its column's head (its softmax runs four times over, in lanes that would
+//    otherwise be padding).  Eight heads per workgroup are two sets.
+//  * The rescale of the accumulators by alpha is a real branch: it runs only
+//    on tiles that raise some running max.
+//
+// Tiling, loads, the K tile in LDS and the cross-wave merge follow the
+// decode_mfma_kernel (decode_mfma.h).
+#pragma once
+
+#include "decode_mfma.h"
+
+namespace pa {
+
+// v_perm selectors: bytes k of the two sources become the low bytes of the
+// two halves of the result (high bytes zero): {lo.byte k, 0, hi.byte k, 0}.
+__device__ __forceinline__ constexpr uint32_t i4_sel(int k) {
+  return 0x0C000C00u | ((uint32_t)(4 + k) << 16) | (uint32_t)k;
+}
+constexpr uint32_t kNibbles = 0x0F0F0F0Fu;
+constexpr float kTwo24 = 16777216.0f;    // 2^24
+constexpr float kTwoM24 = 1.0f / kTwo24;
+
+template <int BS, int GC, int NW>
+__global__ __launch_bounds__(NW * kWave)
+__attribute__((amdgpu_waves_per_eu(GC == 4 ? 3 : 2, 8)))
+void decode_mfma_i4_kernel(const DecodeParams p) {
+  constexpr int D = 128;
+  constexpr int TT = 16;                  // positions per tile
+  constexpr int ROWB = D / 2;             // cache bytes per row
+  constexpr int KG = D / kInt4Group;      // scale groups per row = score MFMAs
+  constexpr int VE = D / 16;              // value MFMAs per column set
+  constexpr int CS = GC / 4;              // column sets
+  constexpr int CHUNKS = D / 8;           // 16-byte chunks per fp16 row in LDS
+  constexpr int K_LPR = ROWB / 16;        // lanes per row in a K load
+  constexpr int TPI = GC == 4 ? 2 : 1;    // tiles fetched per loop iteration
+  static_assert(GC == 4 || GC == 8, "four or eight heads per workgroup");
+  static_assert(BS % TT == 0, "a tile lies inside one block");
+  static_assert(TT * ROWB == kWave * 16, "one K tile = one 16-byte load per lane");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const WgCoord wc = wg_coord();
+  const int slot = wc.part;
+  const int kvh = wc.y / p.head_chunks;
+  const int chunk = wc.y - kvh * p.head_chunks;
+  const int s = wc.s;
+  const int h0 = kvh * p.group + chunk * GC;
+  const size_t out_row0 = (size_t)s * p.num_q_heads + h0;
+
+  const int ctx = p.context_lens[s];
+  const bool single = p.num_parts == 1;
+  const int tok0 = partition_of_slot(p, slot, ctx) * p.part_tokens;
+  const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
+  if (bad_ctx || tok0 >= ctx) {
+    if (single) {
+      const float fill = bad_ctx ? __builtin_nanf("") : 0.0f;
+      for (int i = threadIdx.x; i < GC * D; i += NW * kWave)
+        store_out<Fmt::I4>(p.out, out_row0 * D + i, fill);
+    }
+    return;
+  }
+  const int tok_end = min(ctx, tok0 + p.part_tokens);
+  const int start = window_start(p, ctx);
+  if (tok_end <= start) {  // wholly before the window (never the only partition)
+    for (int i = threadIdx.x; i < GC * D; i += NW * kWave)
+      store_result<Fmt::I4, D>(p, false, out_row0 + i / D, slot, i % D, kMaxInit, 0.0f, 0.0f);
+    return;
+  }
+  const int ntiles = (tok_end - tok0 + TT - 1) / TT;
+  const int t_first = (max(tok0, start) - tok0) / TT;
+  const bool low_cut = start > tok0 + t_first * TT;
+  const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
+
+  // Query of column n's head (4 sigma + n % 4), dims 32c + 8g .. +8: the B
+  // operand of score MFMA c; the accumulator start removes the code bias.
+  u32x4 qb[CS][KG];
+  float qbias[CS][KG];
+#pragma unroll
+  for (int cs = 0; cs < CS; ++cs) {
+#pragma unroll
+    for (int c = 0; c < KG; ++c) {
+      qb[cs][c] = *(const u32x4*)((const char*)p.q +
+                                  ((out_row0 + 4 * cs + (n & 3)) * D + 32 * c + 8 * g) * 2);
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) t += f16_lo(qb[cs][c][w]) + f16_hi(qb[cs][c][w]);
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+      qbias[cs][c] = -8.0f * kTwoM24 * t;
+    }
+  }
+
+  float m[CS], lsum[CS], corr[CS];  // per column: running max, sum, sum of B
+  f32x4 o[CS][VE];                  // O^T * 2^-24 (biased codes): rows 8(4g+i)+e
+#pragma unroll
+  for (int cs = 0; cs < CS; ++cs) {
+    m[cs] = kMaxInit;
+    lsum[cs] = corr[cs] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) o[cs][e] = f32x4{0, 0, 0, 0};
+  }
+  bool bad_block = false;
+
+  constexpr int KTILE_BYTES = TT * D * 2;
+  constexpr int ACC_BYTES = GC * D * 4;
+  constexpr int REGION = KTILE_BYTES > ACC_BYTES ? KTILE_BYTES : ACC_BYTES;
+  __shared__ __attribute__((aligned(16))) char s_mem[NW * REGION];
+  __shared__ float s_ml[NW][GC][2];
+  u32x4* const ktile = (u32x4*)(s_mem + wave * REGION);
+
+  const char* __restrict__ kbase = (const char*)p.k_cache;
+  const char* __restrict__ vbase = (const char*)p.v_cache;
+  const int blk0 = tok0 / BS;
+  const int nblk = (tok_end + BS - 1) / BS - blk0;
+  int ids = 0;
+  int ids_base = -kWave;
+
+  struct Raw {
+    u32x4 k;           // 32 codes: row lane / 4, dims 32 (lane % 4) ..
+    uint32_t v[4];     // 8 codes: token 4g+j, dims 8n ..
+    uint32_t ks[8];    // fp16 key scales, tokens 4g..4g+3 x KG groups
+    uint32_t vs[2];    // fp16 value scales, tokens 4g+j (j = 2w, 2w+1), group n / 4
+    int nvalid;        // rows of the tile inside the partition
+    int nlow;          // rows below this one are before the window
+  };
+
+  auto fetch = [&](const int t, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    Raw raw;
+    const int ttok = tok0 + t * TT;
+    const int nvalid = tok_end - ttok;
+    const int nlow = start - ttok;
+    raw.nvalid = nvalid;
+    raw.nlow = nlow;
+    const int rel = ttok / BS - blk0;
+    if (rel >= ids_base + kWave) {
+      ids_base = rel & ~(kWave - 1);
+      const int bi = ids_base + lane;
+      ids = bi < nblk ? table[blk0 + bi] : 0;
+    }
+    int phys = __builtin_amdgcn_readlane(ids, rel - ids_base);
+    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    bad_block |= !ok;
+    phys = ok ? phys : 0;
+    const size_t row0 = ((size_t)phys * p.num_kv_heads + kvh) * BS + ttok % BS;
+    const char* kt = kbase + row0 * ROWB;
+    const char* vt = vbase + row0 * ROWB;
+
+    const int kr = lane / K_LPR;
+    raw.k = u32x4{0, 0, 0, 0};
+    if (!PARTIAL || (kr >= nlow && kr < nvalid)) raw.k = load16_stream(kt + lane * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * g + j;
+      const bool valid = !PARTIAL || (r >= nlow && r < nvalid);
+      raw.v[j] = valid ? __builtin_nontemporal_load((const uint32_t*)(vt + (size_t)r * ROWB + 4 * n))
+                       : 0u;
+    }
+    const size_t srow = row0 + 4 * g;
+    const bool any = !PARTIAL || (4 * g < nvalid && 4 * g + 3 >= nlow);
+    const u32x4* ksrc = (const u32x4*)(p.k_scale + srow * KG);
+    const u32x4 a = any ? ksrc[0] : u32x4{0, 0, 0, 0};
+    const u32x4 b = any ? ksrc[1] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      raw.ks[w] = a[w];
+      raw.ks[4 + w] = b[w];
+    }
+    uint32_t vsh[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // rows outside [nlow, nvalid) get a zero value scale: their B is 0
+      const bool valid = !PARTIAL || (4 * g + j >= nlow && 4 * g + j < nvalid);
+      vsh[j] = valid ? p.v_scale[(srow + j) * KG + (n >> 2)] : 0u;
+    }
+    raw.vs[0] = vsh[0] | (vsh[1] << 16);
+    raw.vs[1] = vsh[2] | (vsh[3] << 16);
+    return raw;
+  };
+
+  auto consume = [&](const Raw& raw, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    const int nvalid = raw.nvalid;
+    const int nlow = raw.nlow;
+
+    // ---- K tile -> LDS as subnormal codes, chunk c of row r at c ^ (r % CHUNKS)
+    {
+      const int r = lane / K_LPR;
+      const int c0 = 4 * (lane % K_LPR);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = raw.k[w];
+        const uint32_t lo = x & kNibbles, hi = (x >> 4) & kNibbles;
+        ktile[r * CHUNKS + ((c0 + w) ^ (r % CHUNKS))] =
+            u32x4{__builtin_amdgcn_perm(hi, lo, i4_sel(0)), __builtin_amdgcn_perm(hi, lo, i4_sel(1)),
+                  __builtin_amdgcn_perm(hi, lo, i4_sel(2)), __builtin_amdgcn_perm(hi, lo, i4_sel(3))};
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- value A operands: dim 8n+e of tokens 4g..4g+3 (shared by the sets)
+    u32x2 va[VE];
+    {
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo[j] = raw.v[j] & kNibbles;
+        hi[j] = (raw.v[j] >> 4) & kNibbles;
+      }
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const uint32_t* src = (e & 1) ? hi : lo;
+        va[e] = u32x2{__builtin_amdgcn_perm(src[1], src[0], i4_sel(e >> 1)),
+                      __builtin_amdgcn_perm(src[3], src[2], i4_sel(e >> 1))};
+      }
+    }
+
+    u32x4 ka[KG];
+#pragma unroll
+    for (int c = 0; c < KG; ++c) ka[c] = ktile[n * CHUNKS + ((4 * c + g) ^ (n % CHUNKS))];
+
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      // ---- scores: one accumulator per scale group, scaled in fp32
+      float sacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < KG; ++c) {
+        const float b0 = qbias[cs][c];
+        const f32x4 sc = Mfma<Fmt::F16>::qk(ka[c], qb[cs][c], f32x4{b0, b0, b0, b0});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = raw.ks[(i * KG + c) >> 1];
+          sacc[i] = fmaf(sc[i], (c & 1) ? f16_hi(w) : f16_lo(w), sacc[i]);
+        }
+      }
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = sacc[i] * (p.scale_log2 * kTwo24);
+        if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) z[i] = -__builtin_inff();
+      }
+      float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m[cs], mt);
+      const bool moved = mn > m[cs];
+      const float alpha = fast_exp2(m[cs] - mn);
+      m[cs] = mn;
+      float pw[4];
+      float ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[i] = fast_exp2(z[i] - mn);
+        ps += pw[i];
+      }
+      lsum[cs] = fmaf(lsum[cs], alpha, ps);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(moved) != 0, 0)) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) o[cs][e] *= alpha;
+        corr[cs] *= alpha;
+      }
+      // ---- values: B = p * value scale of column n's group, fp16
+      const u32x2 pb = {Mfma<Fmt::F16>::pack(pw[0] * f16_lo(raw.vs[0]), pw[1] * f16_hi(raw.vs[0])),
+                        Mfma<Fmt::F16>::pack(pw[2] * f16_lo(raw.vs[1]), pw[3] * f16_hi(raw.vs[1]))};
+      corr[cs] = Mfma<Fmt::F16>::sum2(pb[1], Mfma<Fmt::F16>::sum2(pb[0], corr[cs]));
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[cs][e] = Mfma<Fmt::F16>::pv(va[e], pb, o[cs][e]);
+    }
+  };
+
+  const int nfull = (tok_end - tok0) / TT;
+  int t = t_first + wave;
+  if (low_cut && wave == 0) {
+    const Raw a = fetch(t, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    consume(a, std::true_type{});
+    t += NW;
+  }
+  if constexpr (TPI == 2) {
+    for (; t + NW < nfull; t += 2 * NW) {
+      const Raw a = fetch(t, std::false_type{});
+      const Raw b = fetch(t + NW, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      consume(a, std::false_type{});
+      consume(b, std::false_type{});
+    }
+  }
+  for (; t < ntiles; t += NW) {
+    if (t < nfull) {
+      const Raw a = fetch(t, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      consume(a, std::false_type{});
+    } else {
+      const Raw a = fetch(t, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      consume(a, std::true_type{});
+    }
+  }
+
+  // ---- merge: the lanes' shares of l and of the column sums, then the
+  // waves through LDS
+#pragma unroll
+  for (int cs = 0; cs < CS; ++cs) {
+    lsum[cs] += __shfl_xor(lsum[cs], 16);
+    lsum[cs] += __shfl_xor(lsum[cs], 32);
+    corr[cs] += __shfl_xor(corr[cs], 16);
+    corr[cs] += __shfl_xor(corr[cs], 32);
+  }
+  __syncthreads();  // every wave is done with its K tile region
+  float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][D]
+  if ((n >> 2) == g) {  // column group n / 4 is the group of this lane's rows
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      const int hh = 4 * cs + (n & 3);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_acc[hh * D + 32 * g + 8 * i + e] = fmaf(o[cs][e][i], kTwo24, -8.0f * corr[cs]);
+      }
+    }
+  }
+  if (g == 0 && n < 4) {
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      s_ml[wave][4 * cs + n][0] = m[cs];
+      s_ml[wave][4 * cs + n][1] = lsum[cs];
+    }
+  }
+  const bool bad = __syncthreads_or(bad_block ? 1 : 0) != 0;
+  for (int i = threadIdx.x; i < GC * D; i += NW * kWave) {
+    const int h = i / D;
+    const int d = i - h * D;
+    float M = s_ml[0][h][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h][0]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float a = fast_exp2(s_ml[w][h][0] - M);
+      L = fmaf(a, s_ml[w][h][1], L);
+      acc = fmaf(a, ((const float*)(s_mem + w * REGION))[h * D + d], acc);
+    }
+    if (bad) M = L = acc = __builtin_nanf("");
+    store_result<Fmt::I4, D>(p, single, out_row0 + h, slot, d, M, L, acc);
+  }
+}
+
+}  // namespace pa

@@ -1,8 +1,9 @@
 """int4 caches on the GPU against the oracle (needs an MI355X): the
 quantizing append bit-exact (packed codes and group scales), decode
-attention over the same codes and scales within tolerance (vector-ALU kernel,
-one or two query heads per workgroup), windowed decode, the gather and the
-block copy, and a full-size case."""
+attention over the same codes and scales within tolerance (the vector-ALU
+kernel at one or two query heads per KV head, head_dim 64 or block 4; the
+matrix-core kernel at 4, 8 and 16 with head_dim 128 and blocks of 16 or 32),
+windowed decode, the gather and the block copy, and a full-size case."""
 import numpy as np
 import pytest
 import torch
@@ -78,7 +79,7 @@ def test_kv_append_int4_bit_exact(d):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bs", [4, 16, 32])
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (32, 2)])
 def test_int4_decode_matches_oracle(d, bs, hq, hkv, orc):
     ctx = [1, bs + 3, 200, 513]
     shape, lay, case = make("f16", hq, hkv, d, bs, ctx, seed=5, spare_blocks=2)
