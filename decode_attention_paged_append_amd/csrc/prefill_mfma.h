@@ -133,191 +133,209 @@ void prefill_mfma_kernel(const PrefillParams p) {
   const char* __restrict__ vbase = (const char*)p.v_cache;
   bool bad_block = false;
 
-  // Cooperative tile load: chunk idx = row * CH + c of the tile.  K/V rows
-  // are fetched two tiles ahead of their use (two register stages), and a
-  // tile's block ids one tile ahead of its rows, so neither the table nor the
-  // cache rows are waited for while there is math to do.
+  // Cooperative tile loads: chunk idx = row * CH + c of a tile.  Stage s of
+  // the pipeline is {K of tile s, V of tile s-1}: the value product of a tile
+  // runs one step after its scores.  Stages are fetched two steps ahead of
+  // their use (two register stages), a tile's block ids one step ahead of its
+  // rows, so neither the table nor the cache rows are waited for while there
+  // is math to do.
   struct Stage {
     u32x4 k[PER_THREAD], v[PER_THREAD];
   };
-  int ids_next[PER_THREAD];
   auto load_ids = [&](const int t, int (&ids)[PER_THREAD]) {
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
       const int idx = j * NW * kWave + threadIdx.x;
       const int row = idx / CH;
       const int pos = t * TT + row;
-      ids[j] = (EVEN || idx < TILE_CHUNKS) && pos < ctx ? table[pos / BS] : 0;
+      ids[j] = (EVEN || idx < TILE_CHUNKS) && t < ntiles && pos < ctx ? table[pos / BS] : 0;
     }
   };
-  auto load_tile = [&](const int t, const int (&ids)[PER_THREAD], Stage& st) {
+  auto load_rows = [&](const char* base_ptr, const int t, const int (&ids)[PER_THREAD],
+                       u32x4 (&dst)[PER_THREAD]) {
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
       const int idx = j * NW * kWave + threadIdx.x;
       const int row = idx / CH;
       const int c = idx - row * CH;
       const int pos = t * TT + row;
-      st.k[j] = st.v[j] = u32x4{0, 0, 0, 0};
-      if ((EVEN || idx < TILE_CHUNKS) && pos < ctx) {
+      dst[j] = u32x4{0, 0, 0, 0};
+      if ((EVEN || idx < TILE_CHUNKS) && t >= 0 && t < ntiles && pos < ctx) {
         int blk = ids[j];
         const bool ok = (unsigned)blk < (unsigned)p.num_blocks;
         bad_block |= !ok;
         blk = ok ? blk : 0;
         const size_t off = ((((size_t)blk * p.num_kv_heads + kvh) * BS + pos % BS) * CH + c) * 16;
-        st.k[j] = load16(kbase + off);
-        st.v[j] = load16(vbase + off);
+        dst[j] = load16(base_ptr + off);
       }
     }
   };
-  auto store_tile = [&](const int buf, const Stage& st) {
+  auto store_stage = [&](const int s, const Stage& st) {
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
       const int idx = j * NW * kWave + threadIdx.x;
       const int row = idx / CH;
       const int c = idx - row * CH;
       if (!EVEN && idx >= TILE_CHUNKS) continue;
-      s_k[buf][row * CH + (c ^ (row % CH))] = st.k[j];
-      s_v[buf][idx] = st.v[j];
+      if (s < ntiles) s_k[s & 1][row * CH + (c ^ (row % CH))] = st.k[j];
+      if (s >= 1) s_v[(s - 1) & 1][idx] = st.v[j];
     }
   };
 
-  Stage sa, sb;
-  {
-    int ids[PER_THREAD];
-    load_ids(0, ids);
-    load_tile(0, ids, sa);
-    if (ntiles > 1) {
-      load_ids(1, ids);
-      load_tile(1, ids, sb);
+  // ---- the three pieces of a tile's math
+  auto tile_live = [&](const int t) { return wave_live && t >= 0 && t < ntiles && t * TT <= wave_qmax; };
+
+  // S^T = K . Q^T for the wave's row groups, two 16-token halves
+  auto scores = [&](const int t, f32x4 (&sacc)[2][NR]) {
+    const int buf = t & 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int krow = 16 * h + n;
+      u32x4 a[QKS];
+#pragma unroll
+      for (int c = 0; c < QKS; ++c) a[c] = s_k[buf][krow * CH + ((4 * c + g) ^ (krow % CH))];
+      // chunk outer, row group inner: NR independent accumulation chains
+#pragma unroll
+      for (int r = 0; r < NR; ++r) sacc[h][r] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < QKS; ++c) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) sacc[h][r] = MM::qk(a[c], qb[r][c], sacc[h][r]);
+      }
     }
+  };
+
+  // Online softmax of a score tile into the fp16/bf16 weights pb.  Scores
+  // stay raw (the scale is positive, so maxima commute with it); a weight is
+  // exp2(s * scale_log2 - m) in one FMA and one v_exp.  The accumulators hold
+  // the tiles before this one when it rescales them.
+  auto softmax = [&](const int t, const f32x4 (&sacc)[2][NR], u32x4 (&pb)[NR]) {
+    const int t0 = t * TT;
+    auto body = [&](auto diag_tag) {
+      constexpr bool DIAG = decltype(diag_tag)::value;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float sv[2][4];
+        float mt = -__builtin_inff();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sv[h][i] = sacc[h][r][i];
+            if (DIAG && t0 + 16 * h + 4 * g + i > qpos[r]) sv[h][i] = -__builtin_inff();
+          }
+          mt = fmaxf(mt, fmaxf(fmaxf(sv[h][0], sv[h][1]), fmaxf(sv[h][2], sv[h][3])));
+        }
+        // The reference max m of a row moves only when one of its scores
+        // exceeds it by more than kLazyRescale.  The result is the same for
+        // any reference (it cancels in the normalisation); weights stay
+        // <= 2^kLazyRescale, far inside the operand formats' range; and on
+        // almost every tile neither the row-wide max (two cross-lane steps)
+        // nor the accumulator rescale is needed.
+        float mn = m[r];
+        float alpha = 1.0f;
+        const bool need = mt * p.scale_log2 > m[r] + kLazyRescale;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+          mt = fmaxf(mt, __shfl_xor(mt, 16));
+          mt = fmaxf(mt, __shfl_xor(mt, 32));
+          mt *= p.scale_log2;
+          if (mt > m[r] + kLazyRescale) mn = mt;  // same decision on the row's 4 lanes
+          alpha = fast_exp2(m[r] - mn);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) o[r][e] *= alpha;
+          m[r] = mn;
+        }
+        float pw[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pw[h][i] = fast_exp2(fmaf(sv[h][i], p.scale_log2, -mn));
+        }
+        pb[r] = u32x4{MM::pack(pw[0][0], pw[0][1]), MM::pack(pw[0][2], pw[0][3]),
+                      MM::pack(pw[1][0], pw[1][1]), MM::pack(pw[1][2], pw[1][3])};
+        // the row sum of the rounded weights, the ones the value product uses
+        float ps = lsum[r] * alpha;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ps = MM::sum2(pb[r][w], ps);
+        lsum[r] = ps;
+      }
+    };
+    if (t0 + TT - 1 > wave_qmin)  // some (row, token) pair is masked
+      body(std::true_type{});
+    else
+      body(std::false_type{});
+  };
+
+  // O^T += V^T . P^T
+  auto values = [&](const int t, const u32x4 (&pb)[NR]) {
+    const int buf = t & 1;
+    uint32_t vh[8][VE / 2];  // token rows {4g+j, 16+4g+j}, dims n*VE..
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int vrow = (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+      if constexpr (VE == 8) {
+        const u32x4 w = s_v[buf][vrow * CH + n];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vh[j][k] = w[k];
+      } else {
+        const u32x2 w = ((const u32x2*)&s_v[buf][0])[vrow * (CH * 2) + n];
+        vh[j][0] = w[0];
+        vh[j][1] = w[1];
+      }
+    }
+    // V^T operand of value MFMA e: the 8 token rows' values at dim n*VE + e,
+    // built just before its MFMAs
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const int w = e >> 1;
+      const u32x4 va = {__builtin_amdgcn_perm(vh[1][w], vh[0][w], sel),
+                        __builtin_amdgcn_perm(vh[3][w], vh[2][w], sel),
+                        __builtin_amdgcn_perm(vh[5][w], vh[4][w], sel),
+                        __builtin_amdgcn_perm(vh[7][w], vh[6][w], sel)};
+#pragma unroll
+      for (int r = 0; r < NR; ++r) o[r][e] = MM::qk(va, pb[r], o[r][e]);
+    }
+  };
+
+  // ---- pipeline.  Step t holds K of tile t and V of tile t-1 in LDS: a wave
+  // runs the value product of t-1 and the scores of t back to back on the
+  // matrix cores (32 MFMAs at NR = 2), then the softmax of t on the vector ALU.
+  // Measured on MI355X this beats scores, softmax and values of one tile in a
+  // row (+7 % whole prompts, +12 % chunks), and beats splitting the waves of
+  // each SIMD into two groups in opposite phases (a second barrier per tile).
+  f32x4 sacc[2][NR];
+  u32x4 pb[NR];
+  Stage st;
+  int ids_next[PER_THREAD], ids_last[PER_THREAD];
+  {
+    load_ids(0, ids_last);
+    load_rows(kbase, 0, ids_last, st.k);        // stage 0: K(0)
+    load_ids(1, ids_next);
   }
-  if (ntiles > 2) load_ids(2, ids_next);
-  store_tile(0, sa);
+  store_stage(0, st);
   __syncthreads();
 
-  // One tile: start the loads of tile t+2 into `into`, do tile t's math from
-  // LDS, then move tile t+1 (loaded an iteration ago) from `from` to LDS.
-  auto step = [&](const int t, Stage& into, const Stage& from) {
-    const int buf = t & 1;
-    if (t + 2 < ntiles) {
-      int ids[PER_THREAD];
+  auto step = [&](const int t) {
+    if (t + 1 <= ntiles) {  // stage t+1: K(t+1) (ids one step ahead), V(t)
+      int idk[PER_THREAD];
 #pragma unroll
-      for (int j = 0; j < PER_THREAD; ++j) ids[j] = ids_next[j];
-      if (t + 3 < ntiles) load_ids(t + 3, ids_next);
-      load_tile(t + 2, ids, into);
+      for (int j = 0; j < PER_THREAD; ++j) idk[j] = ids_next[j];
+      load_rows(kbase, t + 1, idk, st.k);
+      load_rows(vbase, t, ids_last, st.v);
+#pragma unroll
+      for (int j = 0; j < PER_THREAD; ++j) ids_last[j] = idk[j];
+      load_ids(t + 2, ids_next);
     }
-    const int t0 = t * TT;
-    if (wave_live && t0 <= wave_qmax) {
-      const bool diag = t0 + TT - 1 > wave_qmin;  // some (row, token) pair is masked
-      // ---- scores: two 16-token halves
-      f32x4 sacc[2][NR];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int krow = 16 * h + n;
-        u32x4 a[QKS];
-#pragma unroll
-        for (int c = 0; c < QKS; ++c) a[c] = s_k[buf][krow * CH + ((4 * c + g) ^ (krow % CH))];
-        // chunk outer, row group inner: NR independent accumulation chains
-#pragma unroll
-        for (int r = 0; r < NR; ++r) sacc[h][r] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < QKS; ++c) {
-#pragma unroll
-          for (int r = 0; r < NR; ++r) sacc[h][r] = MM::qk(a[c], qb[r][c], sacc[h][r]);
-        }
-      }
-      // ---- V^T operands (shared by the NR row groups)
-      uint32_t vh[8][VE / 2];  // token rows {4g+j, 16+4g+j}, dims n*VE..
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int vrow = (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
-        if constexpr (VE == 8) {
-          const u32x4 w = s_v[buf][vrow * CH + n];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) vh[j][k] = w[k];
-        } else {
-          const u32x2 w = ((const u32x2*)&s_v[buf][0])[vrow * (CH * 2) + n];
-          vh[j][0] = w[0];
-          vh[j][1] = w[1];
-        }
-      }
-      // V^T operand of value MFMA e: the 8 token rows' values at dim n*VE + e
-      u32x4 va[VE];
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const int w = e >> 1;
-        va[e] = u32x4{__builtin_amdgcn_perm(vh[1][w], vh[0][w], sel),
-                      __builtin_amdgcn_perm(vh[3][w], vh[2][w], sel),
-                      __builtin_amdgcn_perm(vh[5][w], vh[4][w], sel),
-                      __builtin_amdgcn_perm(vh[7][w], vh[6][w], sel)};
-      }
-      // ---- online softmax and values, per row group.  Scores stay raw (the
-      // scale is positive, so maxima commute with it); a weight is
-      // exp2(s * scale_log2 - m) in one FMA and one v_exp.
-      auto softmax_values = [&](auto diag_tag) {
-        constexpr bool DIAG = decltype(diag_tag)::value;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          float sv[2][4];
-          float mt = -__builtin_inff();
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              sv[h][i] = sacc[h][r][i];
-              if (DIAG && t0 + 16 * h + 4 * g + i > qpos[r]) sv[h][i] = -__builtin_inff();
-            }
-            mt = fmaxf(mt, fmaxf(fmaxf(sv[h][0], sv[h][1]), fmaxf(sv[h][2], sv[h][3])));
-          }
-          // The reference max m of a row moves only when one of its scores
-          // exceeds it by more than kLazyRescale.  The result is the same
-          // for any reference (it cancels in the normalisation); weights stay
-          // <= 2^kLazyRescale, far inside the operand formats' range; and
-          // on almost every tile neither the row-wide max (two cross-lane
-          // steps) nor the accumulator rescale is needed.
-          float mn = m[r];
-          float alpha = 1.0f;
-          const bool need = mt * p.scale_log2 > m[r] + kLazyRescale;
-          if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            mt *= p.scale_log2;
-            if (mt > m[r] + kLazyRescale) mn = mt;  // same decision on the row's 4 lanes
-            alpha = fast_exp2(m[r] - mn);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) o[r][e] *= alpha;
-            m[r] = mn;
-          }
-          float pw[2][4];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pw[h][i] = fast_exp2(fmaf(sv[h][i], p.scale_log2, -mn));
-          }
-          const u32x4 pb = {MM::pack(pw[0][0], pw[0][1]), MM::pack(pw[0][2], pw[0][3]),
-                            MM::pack(pw[1][0], pw[1][1]), MM::pack(pw[1][2], pw[1][3])};
-          // the row sum of the rounded weights, the ones the value product uses
-          float ps = lsum[r] * alpha;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) ps = MM::sum2(pb[w], ps);
-          lsum[r] = ps;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) o[r][e] = MM::qk(va[e], pb, o[r][e]);
-        }
-      };
-      if (diag)
-        softmax_values(std::true_type{});
-      else
-        softmax_values(std::false_type{});
+    if (tile_live(t - 1)) values(t - 1, pb);
+    if (tile_live(t)) {
+      scores(t, sacc);
+      softmax(t, sacc, pb);
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1, from);
+    if (t + 1 <= ntiles) store_stage(t + 1, st);
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < ntiles) step(t + 1, sb, sa);
-  }
+  for (int t = 0; t <= ntiles; ++t) step(t);
 
   // ---- normalise and store: lane (g, n) holds dims (4g+i)*VE + e of row n
   const bool bad = __syncthreads_or(bad_block ? 1 : 0) != 0;
