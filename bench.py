@@ -172,6 +172,32 @@ class Bench:
         return self.kv_bytes_per_layer() + qo + tables + new_rows
 
 
+READ_PROBE_BYTES = 4 << 30   # 16x the 256 MiB last-level cache
+
+
+def read_probe(dev, launches: int = 10) -> dict:
+    """The library's HBM read-rate probe (pa_hbm_read_probe) over a 4 GiB
+    buffer, timed between HIP events: the practical read bandwidth the
+    attention kernels' rates are compared with."""
+    src = torch.empty(READ_PROBE_BYTES // 4, dtype=torch.int32, device=dev)
+    src.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        pa.hbm_read_probe(src, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(launches):
+        pa.hbm_read_probe(src, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    gbs = READ_PROBE_BYTES / (ms / 1e3) / 1e9
+    del src
+    return {"GB/s": round(gbs, 1), "bytes": READ_PROBE_BYTES, "ms_per_launch": round(ms, 4),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
     """The CPU oracle, as it stands, over layer 0 of the same workload."""
     import oracle
@@ -479,6 +505,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-kernel", type=int, default=0,
                     help="only run N copies of a 1 GiB tensor (counter calibration) and exit")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only time the HBM read-rate probe over 4 GiB and exit")
+    ap.add_argument("--no-read-probe", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -494,6 +523,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": src.numel() * 2, "copies": args.copy_kernel}))
+        return
+
+    if args.read_probe:
+        print(json.dumps({"hbm_read_probe": read_probe(dev)}))
         return
 
     if args.workload == "block-pool":
@@ -579,6 +612,10 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_read_probe:
+        probe = read_probe(dev)
+        probe["kernel_frac_of_probe"] = round(achieved / probe["GB/s"], 4)
+        result["hbm_read_probe"] = probe
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(result))

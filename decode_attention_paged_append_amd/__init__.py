@@ -23,6 +23,7 @@ __all__ = [
     "kv_append_fp8", "paged_decode_attention_fp8", "kv_append_int4",
     "paged_decode_attention_int4", "int4_desc",
     "decode_step_partitions", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
+    "hbm_read_probe",
     "BlockManager", "copy_blocks", "paged_prefill_attention", "paged_decode_attention_window",
     "decode_window_workspace_bytes",
 ]
@@ -98,6 +99,7 @@ def _declare(lib):
                                       P],
         "pa_gather_kv": [P, P, P, P, P, i32, P, i32, P, P, P, P, D, P],
         "pa_copy_blocks": [P, P, P, P, P, i32, D, P],
+        "pa_hbm_read_probe": [P, sz, P, P],
         "pa_paged_prefill_attention": [P, P, P, P, i32, P, P, i32, i32, i32, f32, P, D, P],
         "pa_paged_decode_attention_window": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D,
                                              P, sz, P],
@@ -624,6 +626,19 @@ class BlockManager:
 
     def length(self, seq: int) -> int:
         return self._lib.pa_bm_sequence_length(self._h, seq)
+
+
+def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read every byte of the contiguous device tensor src once (see
+    pa_hbm_read_probe); sink: a device int32/uint32 tensor of one element or
+    more, written only for an improbable data value."""
+    lib = library()
+    if not src.is_contiguous() or src.device.type != "cuda":
+        raise ValueError("src must be a contiguous device tensor")
+    if sink.device != src.device or sink.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("sink must be an int32 tensor on src's device")
+    _ok(lib.pa_hbm_read_probe(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                              ctypes.c_void_p(sink.data_ptr()), _stream(src)), lib)
 
 
 def copy_blocks(k_cache, v_cache, block_pairs, k_scale=None, v_scale=None, int4=False):

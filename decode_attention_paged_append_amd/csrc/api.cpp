@@ -466,6 +466,15 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
                     "gather launch");
 }
 
+pa_status pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, pa_stream_t stream) {
+  if (!src || !sink) return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  if (bytes == 0 || bytes % 16 != 0 || ((uintptr_t)src & 15) != 0)
+    return fail(PA_ERR_INVALID_ARG, "probe buffer of %zu bytes must be a positive multiple of 16, "
+                "16-byte aligned", bytes);
+  return hip_status(pa::launch_hbm_read_probe(src, bytes, sink, (hipStream_t)stream),
+                    "read probe launch");
+}
+
 pa_status pa_paged_prefill_attention(const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                                      const int32_t* query_start, const int32_t* context_lens,

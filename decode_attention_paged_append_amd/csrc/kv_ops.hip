@@ -7,6 +7,8 @@
 // KV-cache visualization page).  A decode step appends the new token's K and
 // V rows at its slot ("KV cache: the engine behind fast LLM inference",
 // "What happens at each decoding step", step 4).
+#include <algorithm>
+
 #include "kv_ops.h"
 
 namespace pa {
@@ -344,6 +346,41 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void*
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2 * chunks), dim3(256), 0, stream,
                      (u32x4*)k_cache, (u32x4*)v_cache, (uint16_t*)k_scale, (uint16_t*)v_scale,
                      pairs, num_blocks, block_pieces, num_kv_heads * block_size * scales_per_row, chunks);
+  return hipGetLastError();
+}
+
+// ---- HBM read-rate probe: each thread folds U 16-byte words per pass of a
+// grid-stride loop; a store that depends on the data keeps the loads alive.
+constexpr int kProbeThreads = 256;
+constexpr int kProbeUnroll = 8;
+constexpr uint32_t kProbeNever = 0x9E3779B9u;
+
+__global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(
+    const u32x4* __restrict__ src, int64_t words, uint32_t* sink) {
+  const int64_t per_pass = (int64_t)gridDim.x * kProbeThreads * kProbeUnroll;
+  uint32_t acc = 0;
+  for (int64_t base = (int64_t)blockIdx.x * kProbeThreads * kProbeUnroll; base < words;
+       base += per_pass) {
+    u32x4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      const int64_t i = base + (int64_t)u * kProbeThreads + threadIdx.x;
+      v[u] = i < words ? __builtin_nontemporal_load(src + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  if (acc == kProbeNever) sink[0] = acc;
+}
+
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
+                                 hipStream_t stream) {
+  const int64_t words = (int64_t)(bytes / 16);
+  // 16 workgroups of 4 waves per CU on 256 CUs, or fewer for a small buffer
+  const int64_t per_wg = (int64_t)kProbeThreads * kProbeUnroll;
+  const int64_t wgs = std::min<int64_t>(4096, (words + per_wg - 1) / per_wg);
+  hipLaunchKernelGGL(hbm_read_probe_kernel, dim3((unsigned)wgs), dim3(kProbeThreads), 0, stream,
+                     (const u32x4*)src, words, sink);
   return hipGetLastError();
 }
 

@@ -321,6 +321,18 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
                        int32_t num_seqs, void* k_out, void* v_out, void* k_scale_out,
                        void* v_scale_out, const pa_cache_desc* cache, pa_stream_t stream);
 
+/* ---------------------------------------------------------------- measurement */
+
+/* HBM read-rate probe (a measurement export, not part of attention): every
+ * 16-byte word of src (device, `bytes` a positive multiple of 16, 16-byte
+ * aligned) is read once with non-temporal loads by a full-chip grid.  The
+ * loaded words are folded into one value per thread, which is stored to
+ * sink[0] (device uint32) only if it equals a fixed improbable constant, so
+ * that the reads cannot be elided.  Timing a launch gives the practical
+ * read bandwidth that the attention kernels' rates can be compared with.
+ * PA_ERR_INVALID_ARG for a NULL pointer or a bad size. */
+pa_status pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, pa_stream_t stream);
+
 /* ---------------------------------------------------------------- sliding window */
 
 /* Sliding-window decode attention ([viz] "What the page leaves out" names

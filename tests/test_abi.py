@@ -130,3 +130,16 @@ def test_workspace_and_plan(lib, dtype, d, bs, tile):
         assert ws == a256(ml) + s * hq * nparts * d * 4
     # an explicit partition covering the whole table needs no workspace
     assert lib.pa_decode_workspace_bytes(ctypes.byref(dd), s, hq, maxb, maxb * bs) == 0
+
+
+def test_read_probe_argument_checks(lib):
+    """Rejected on the host: NULL pointers, a size that is zero or not a
+    multiple of 16, a source that is not 16-byte aligned (the pointers here
+    are never dereferenced)."""
+    src, sink = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    assert lib.pa_hbm_read_probe(None, 16, sink, None) == INVALID
+    assert lib.pa_hbm_read_probe(src, 16, None, None) == INVALID
+    assert lib.pa_hbm_read_probe(src, 0, sink, None) == INVALID
+    assert lib.pa_hbm_read_probe(src, 24, sink, None) == INVALID
+    assert lib.pa_hbm_read_probe(ctypes.c_void_p(4104), 32, sink, None) == INVALID
+    assert b"multiple of 16" in lib.pa_last_error()

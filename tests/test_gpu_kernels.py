@@ -380,3 +380,15 @@ def test_library_plan_many_partitions_reused_workspace(dtype, hq, hkv):
         assert (out[3] == 0).all()
         outs.append(out)
     assert torch.equal(outs[0].view(torch.uint8), outs[1].view(torch.uint8))
+
+
+def test_read_probe_runs_and_leaves_sink():
+    """The HBM read probe reads a buffer (ragged against its grid) without
+    error and stores nothing for ordinary data."""
+    src = torch.ones((1 << 20) + 12, dtype=torch.int32, device=dev())
+    sink = torch.full((1,), 7, dtype=torch.int32, device=dev())
+    pa.hbm_read_probe(src, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    with pytest.raises(ValueError):
+        pa.hbm_read_probe(src.cpu(), sink)
