@@ -177,25 +177,31 @@ READ_PROBE_BYTES = 4 << 30   # 16x the 256 MiB last-level cache
 
 def read_probe(dev, launches: int = 10) -> dict:
     """The library's HBM read-rate probe (pa_hbm_read_probe) over a 4 GiB
-    buffer, timed between HIP events: the practical read bandwidth the
-    attention kernels' rates are compared with."""
+    buffer, timed between HIP events: 4 KiB chunks read in sequence, and in a
+    seeded random order (the access pattern of the attention kernels' block
+    gather).  These are the practical read bandwidths the attention kernels'
+    rates are compared with."""
     src = torch.empty(READ_PROBE_BYTES // 4, dtype=torch.int32, device=dev)
     src.fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(2):
-        pa.hbm_read_probe(src, sink)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(launches):
-        pa.hbm_read_probe(src, sink)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / launches
-    gbs = READ_PROBE_BYTES / (ms / 1e3) / 1e9
-    del src
-    return {"GB/s": round(gbs, 1), "bytes": READ_PROBE_BYTES, "ms_per_launch": round(ms, 4),
-            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    chunks = READ_PROBE_BYTES // 4096
+    gen = torch.Generator().manual_seed(3)
+    order = torch.randperm(chunks, generator=gen).to(torch.int32).to(dev)
+    result = {"bytes": READ_PROBE_BYTES, "chunk_bytes": 4096}
+    for name, o in (("sequential", None), ("random_chunks", order)):
+        for _ in range(2):
+            pa.hbm_read_probe(src, sink, o)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(launches):
+            pa.hbm_read_probe(src, sink, o)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        result[name + "_GB/s"] = round(READ_PROBE_BYTES / (ms / 1e3) / 1e9, 1)
+    del src, order
+    return result
 
 
 def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
@@ -614,7 +620,8 @@ def main():
     }
     if not args.no_read_probe:
         probe = read_probe(dev)
-        probe["kernel_frac_of_probe"] = round(achieved / probe["GB/s"], 4)
+        probe["kernel_frac_of_sequential"] = round(achieved / probe["sequential_GB/s"], 4)
+        probe["kernel_frac_of_random_chunks"] = round(achieved / probe["random_chunks_GB/s"], 4)
         result["hbm_read_probe"] = probe
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)

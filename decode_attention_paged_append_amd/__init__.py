@@ -99,7 +99,7 @@ def _declare(lib):
                                       P],
         "pa_gather_kv": [P, P, P, P, P, i32, P, i32, P, P, P, P, D, P],
         "pa_copy_blocks": [P, P, P, P, P, i32, D, P],
-        "pa_hbm_read_probe": [P, sz, P, P],
+        "pa_hbm_read_probe": [P, sz, P, P, P],
         "pa_paged_prefill_attention": [P, P, P, P, i32, P, P, i32, i32, i32, f32, P, D, P],
         "pa_paged_decode_attention_window": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D,
                                              P, sz, P],
@@ -628,16 +628,22 @@ class BlockManager:
         return self._lib.pa_bm_sequence_length(self._h, seq)
 
 
-def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
-    """Read every byte of the contiguous device tensor src once (see
-    pa_hbm_read_probe); sink: a device int32/uint32 tensor of one element or
-    more, written only for an improbable data value."""
+def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, chunk_order=None) -> None:
+    """Read every byte of the contiguous device tensor src once, as 4 KiB
+    chunks in sequence or in the order of the device int32 tensor
+    chunk_order (see pa_hbm_read_probe); sink: a device int32 tensor of one
+    element or more, written only for an improbable data value."""
     lib = library()
     if not src.is_contiguous() or src.device.type != "cuda":
         raise ValueError("src must be a contiguous device tensor")
     if sink.device != src.device or sink.dtype not in (torch.int32, torch.uint32):
         raise ValueError("sink must be an int32 tensor on src's device")
-    _ok(lib.pa_hbm_read_probe(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+    nbytes = src.numel() * src.element_size()
+    if chunk_order is not None and (chunk_order.device != src.device or chunk_order.dtype !=
+                                    torch.int32 or chunk_order.numel() != nbytes // 4096):
+        raise ValueError("chunk_order must be an int32 device tensor of bytes // 4096 entries")
+    _ok(lib.pa_hbm_read_probe(ctypes.c_void_p(src.data_ptr()), nbytes,
+                              None if chunk_order is None else ctypes.c_void_p(chunk_order.data_ptr()),
                               ctypes.c_void_p(sink.data_ptr()), _stream(src)), lib)
 
 

@@ -466,12 +466,13 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
                     "gather launch");
 }
 
-pa_status pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, pa_stream_t stream) {
+pa_status pa_hbm_read_probe(const void* src, size_t bytes, const int32_t* chunk_order,
+                            uint32_t* sink, pa_stream_t stream) {
   if (!src || !sink) return fail(PA_ERR_INVALID_ARG, "NULL pointer");
-  if (bytes == 0 || bytes % 16 != 0 || ((uintptr_t)src & 15) != 0)
-    return fail(PA_ERR_INVALID_ARG, "probe buffer of %zu bytes must be a positive multiple of 16, "
+  if (bytes == 0 || bytes % 4096 != 0 || ((uintptr_t)src & 15) != 0)
+    return fail(PA_ERR_INVALID_ARG, "probe buffer of %zu bytes must be a positive multiple of 4096, "
                 "16-byte aligned", bytes);
-  return hip_status(pa::launch_hbm_read_probe(src, bytes, sink, (hipStream_t)stream),
+  return hip_status(pa::launch_hbm_read_probe(src, bytes, chunk_order, sink, (hipStream_t)stream),
                     "read probe launch");
 }
 

@@ -28,8 +28,8 @@ hipError_t launch_gather_kv(const void* k_cache, const void* v_cache, const void
                             void* v_out, void* k_scale_out, void* v_scale_out,
                             int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                             int32_t row_bytes, int32_t scales_per_row, hipStream_t stream);
-hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
-                                 hipStream_t stream);
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, const int32_t* chunk_order,
+                                 uint32_t* sink, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void* v_scale,
                               const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
                               int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,

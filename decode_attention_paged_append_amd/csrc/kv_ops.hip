@@ -349,38 +349,41 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void*
   return hipGetLastError();
 }
 
-// ---- HBM read-rate probe: each thread folds U 16-byte words per pass of a
-// grid-stride loop; a store that depends on the data keeps the loads alive.
+// ---- HBM read-rate probe: each wave reads whole 4 KiB chunks (4 loads of
+// 16 bytes per lane) in a grid-stride loop over the chunk order; a store that
+// depends on the data keeps the loads alive.
 constexpr int kProbeThreads = 256;
-constexpr int kProbeUnroll = 8;
+constexpr int kProbeChunkWords = 4096 / 16;
 constexpr uint32_t kProbeNever = 0x9E3779B9u;
 
 __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(
-    const u32x4* __restrict__ src, int64_t words, uint32_t* sink) {
-  const int64_t per_pass = (int64_t)gridDim.x * kProbeThreads * kProbeUnroll;
+    const u32x4* __restrict__ src, const int32_t* __restrict__ order, int64_t chunks,
+    uint32_t* sink) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = (int64_t)gridDim.x * (kProbeThreads / kWave);
   uint32_t acc = 0;
-  for (int64_t base = (int64_t)blockIdx.x * kProbeThreads * kProbeUnroll; base < words;
-       base += per_pass) {
-    u32x4 v[kProbeUnroll];
+  for (int64_t c = (int64_t)blockIdx.x * (kProbeThreads / kWave) + threadIdx.x / kWave; c < chunks;
+       c += waves) {
+    int64_t ch = order ? order[c] : c;
+    ch = (uint64_t)ch < (uint64_t)chunks ? ch : 0;
+    const u32x4* p = src + ch * kProbeChunkWords + lane;
+    u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) {
-      const int64_t i = base + (int64_t)u * kProbeThreads + threadIdx.x;
-      v[u] = i < words ? __builtin_nontemporal_load(src + i) : u32x4{0, 0, 0, 0};
-    }
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p + u * kWave);
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   if (acc == kProbeNever) sink[0] = acc;
 }
 
-hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
-                                 hipStream_t stream) {
-  const int64_t words = (int64_t)(bytes / 16);
-  // 16 workgroups of 4 waves per CU on 256 CUs, or fewer for a small buffer
-  const int64_t per_wg = (int64_t)kProbeThreads * kProbeUnroll;
-  const int64_t wgs = std::min<int64_t>(4096, (words + per_wg - 1) / per_wg);
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, const int32_t* chunk_order,
+                                 uint32_t* sink, hipStream_t stream) {
+  const int64_t chunks = (int64_t)(bytes / 4096);
+  // 4 workgroups of 4 waves per CU on 256 CUs (measured best for both
+  // orders), or fewer for a small buffer
+  const int64_t wgs = std::min<int64_t>(1024, (chunks + 3) / 4);
   hipLaunchKernelGGL(hbm_read_probe_kernel, dim3((unsigned)wgs), dim3(kProbeThreads), 0, stream,
-                     (const u32x4*)src, words, sink);
+                     (const u32x4*)src, chunk_order, chunks, sink);
   return hipGetLastError();
 }
 

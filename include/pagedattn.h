@@ -323,15 +323,20 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_s
 
 /* ---------------------------------------------------------------- measurement */
 
-/* HBM read-rate probe (a measurement export, not part of attention): every
- * 16-byte word of src (device, `bytes` a positive multiple of 16, 16-byte
- * aligned) is read once with non-temporal loads by a full-chip grid.  The
- * loaded words are folded into one value per thread, which is stored to
- * sink[0] (device uint32) only if it equals a fixed improbable constant, so
- * that the reads cannot be elided.  Timing a launch gives the practical
- * read bandwidth that the attention kernels' rates can be compared with.
- * PA_ERR_INVALID_ARG for a NULL pointer or a bad size. */
-pa_status pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, pa_stream_t stream);
+/* HBM read-rate probe (a measurement export, not part of attention): src
+ * (device, 16-byte aligned, `bytes` a positive multiple of 4096) is read once
+ * as 4 KiB chunks -- the size of one fp16 (block, head) tile at block 16 and
+ * head_dim 128 -- each by one wave with 16-byte non-temporal loads, in the
+ * order chunk_order gives (device int32 [bytes / 4096], a permutation of the
+ * chunk indices; entries outside the range are read as chunk 0) or in
+ * sequence when chunk_order is NULL.  The loaded words are folded into one
+ * value per thread, stored to sink[0] (device uint32) only if it equals a
+ * fixed improbable constant, so that the reads cannot be elided.  Timing a
+ * launch gives the practical read bandwidth of a sequential stream, or of a
+ * random gather of tiles, that the attention kernels' rates can be compared
+ * with.  PA_ERR_INVALID_ARG for a NULL src or sink or a bad size. */
+pa_status pa_hbm_read_probe(const void* src, size_t bytes, const int32_t* chunk_order,
+                            uint32_t* sink, pa_stream_t stream);
 
 /* ---------------------------------------------------------------- sliding window */
 

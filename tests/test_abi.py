@@ -133,13 +133,13 @@ def test_workspace_and_plan(lib, dtype, d, bs, tile):
 
 
 def test_read_probe_argument_checks(lib):
-    """Rejected on the host: NULL pointers, a size that is zero or not a
-    multiple of 16, a source that is not 16-byte aligned (the pointers here
+    """Rejected on the host: NULL src or sink, a size that is zero or not a
+    multiple of 4096, a source that is not 16-byte aligned (the pointers here
     are never dereferenced)."""
     src, sink = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
-    assert lib.pa_hbm_read_probe(None, 16, sink, None) == INVALID
-    assert lib.pa_hbm_read_probe(src, 16, None, None) == INVALID
-    assert lib.pa_hbm_read_probe(src, 0, sink, None) == INVALID
-    assert lib.pa_hbm_read_probe(src, 24, sink, None) == INVALID
-    assert lib.pa_hbm_read_probe(ctypes.c_void_p(4104), 32, sink, None) == INVALID
-    assert b"multiple of 16" in lib.pa_last_error()
+    assert lib.pa_hbm_read_probe(None, 4096, None, sink, None) == INVALID
+    assert lib.pa_hbm_read_probe(src, 4096, None, None, None) == INVALID
+    assert lib.pa_hbm_read_probe(src, 0, None, sink, None) == INVALID
+    assert lib.pa_hbm_read_probe(src, 4112, None, sink, None) == INVALID
+    assert lib.pa_hbm_read_probe(ctypes.c_void_p(4104), 8192, None, sink, None) == INVALID
+    assert b"multiple of 4096" in lib.pa_last_error()

@@ -383,12 +383,18 @@ def test_library_plan_many_partitions_reused_workspace(dtype, hq, hkv):
 
 
 def test_read_probe_runs_and_leaves_sink():
-    """The HBM read probe reads a buffer (ragged against its grid) without
-    error and stores nothing for ordinary data."""
-    src = torch.ones((1 << 20) + 12, dtype=torch.int32, device=dev())
+    """The HBM read probe reads a buffer in sequence and in a permuted chunk
+    order (one entry out of range, read as chunk 0) without error, and stores
+    nothing for ordinary data."""
+    src = torch.ones(37 * 1024, dtype=torch.int32, device=dev())    # 37 chunks of 4 KiB
     sink = torch.full((1,), 7, dtype=torch.int32, device=dev())
+    order = torch.randperm(37, generator=W.generator(5)).to(torch.int32)
+    order[3] = 1 << 30
     pa.hbm_read_probe(src, sink)
+    pa.hbm_read_probe(src, sink, order.to(dev()))
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
     with pytest.raises(ValueError):
         pa.hbm_read_probe(src.cpu(), sink)
+    with pytest.raises(ValueError):
+        pa.hbm_read_probe(src, sink, order[:5].to(dev()))
