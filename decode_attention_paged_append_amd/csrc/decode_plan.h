@@ -72,8 +72,9 @@ inline constexpr int32_t kTargetWorkgroupsMfma = 256;
 inline constexpr int32_t kTargetWorkgroupsMfmaInt8 = 2048;
 inline constexpr int32_t kMinPartitionTokens = 256;
 // A windowed plan: workgroups over the window only (measured on a 4096-token
-// window: 512 beat 256, 1024 and 2048 with the neutral-partition grid).
-inline constexpr int32_t kTargetWorkgroupsWindow = 512;
+// window of 16 sequences x 8 KV heads, partitions launched by slot: 1024
+// beat 512, 2048 and 256 by 4-7 %).
+inline constexpr int32_t kTargetWorkgroupsWindow = 1024;
 
 struct Plan {
   bool mfma = false;      // matrix-core kernel (grouped-query heads)
