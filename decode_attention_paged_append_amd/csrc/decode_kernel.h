@@ -224,14 +224,16 @@ template <> struct Frag<Fmt::I8> {
 };
 
 // fp8 E4M3 codes: 16 per fragment, dotted with 16 fp16 query values.  Codes
-// are widened to binary16 exactly as value * 2^-8 (e4m3_pair_to_f16); the
-// key/value scales carry the 2^8 (FmtInfo<FP8>::code_scale).
+// are widened to their binary16 values exactly by the hardware conversion
+// (e4m3x4_to_f16), two instructions per four codes.
 template <> struct Frag<Fmt::FP8> {
   static constexpr int VE = 16;
   static constexpr int QW = 8;
   __device__ static __forceinline__ void codes_to_half2(uint32_t w, h16x2& lo, h16x2& hi) {
-    lo = as_h2(e4m3_pair_to_f16(w, kE4m3Lo));
-    hi = as_h2(e4m3_pair_to_f16(w, kE4m3Hi));
+    uint32_t a, b;
+    e4m3x4_to_f16(w, a, b);
+    lo = as_h2(a);
+    hi = as_h2(b);
   }
   __device__ static __forceinline__ float dot(const uint32_t* q, u32x4 k) {
     float s = 0.0f;
@@ -459,11 +461,10 @@ void decode_partition_kernel(const DecodeParams p) {
         vf[j] = u32x4{0, 0, 0, 0};
       }
       if constexpr (kQuant) {
-        constexpr float cs = FmtInfo<F>::code_scale;
         // int4: the lane's 32 dims are scale group lcol of the row
         const size_t si = kInt4 ? row * SPR + lcol : row;
-        ks[j] = valid ? (float)__builtin_bit_cast(_Float16, p.k_scale[si]) * cs : 0.0f;
-        vs[j] = valid ? (float)__builtin_bit_cast(_Float16, p.v_scale[si]) * cs : 0.0f;
+        ks[j] = valid ? (float)__builtin_bit_cast(_Float16, p.k_scale[si]) : 0.0f;
+        vs[j] = valid ? (float)__builtin_bit_cast(_Float16, p.v_scale[si]) : 0.0f;
       } else {
         ks[j] = 1.0f;
         vs[j] = 1.0f;

@@ -251,11 +251,10 @@ void decode_mfma_kernel(const DecodeParams p) {
       const bool any = !PARTIAL || (4 * g < nvalid && 4 * g + 3 >= nlow);
       const u32x2 kw = any ? *(const u32x2*)(p.k_scale + srow) : u32x2{0, 0};
       const u32x2 vw = any ? *(const u32x2*)(p.v_scale + srow) : u32x2{0, 0};
-      constexpr float cs = FmtInfo<F>::code_scale;
-      ksc[0] = f16_lo(kw[0]) * cs; ksc[1] = f16_hi(kw[0]) * cs;
-      ksc[2] = f16_lo(kw[1]) * cs; ksc[3] = f16_hi(kw[1]) * cs;
-      vsc[0] = f16_lo(vw[0]) * cs; vsc[1] = f16_hi(vw[0]) * cs;
-      vsc[2] = f16_lo(vw[1]) * cs; vsc[3] = f16_hi(vw[1]) * cs;
+      ksc[0] = f16_lo(kw[0]); ksc[1] = f16_hi(kw[0]);
+      ksc[2] = f16_lo(kw[1]); ksc[3] = f16_hi(kw[1]);
+      vsc[0] = f16_lo(vw[0]); vsc[1] = f16_hi(vw[0]);
+      vsc[2] = f16_lo(vw[1]); vsc[3] = f16_hi(vw[1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // rows outside [nlow, nvalid) never contribute (their weight is 0)

@@ -24,9 +24,9 @@ enum class Fmt : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3, FP8 = 4, I4 = 5 };
 constexpr int kInt4Group = 32;
 
 // bytes: cache element; q_bytes: query/output element.  Quantized caches
-// (int8, fp8 E4M3) hold codes with an fp16 scale per (token, head) and take
-// fp16 queries; their codes are widened to fp16 exactly, as the stored value
-// times 1/code_scale (the kernels multiply the scales by code_scale).
+// (int8, fp8 E4M3) hold codes with an fp16 scale per (token, head), int4 one
+// per 32 dims, and take fp16 queries; their codes are widened to fp16
+// exactly.
 template <Fmt F> struct FmtInfo;
 template <> struct FmtInfo<Fmt::F32> {
   static constexpr int bytes = 4, q_bytes = 4;
@@ -43,19 +43,16 @@ template <> struct FmtInfo<Fmt::BF16> {
 template <> struct FmtInfo<Fmt::I8> {
   static constexpr int bytes = 1, q_bytes = 2;
   static constexpr bool quantized = true;
-  static constexpr float code_scale = 1.0f;
 };
 template <> struct FmtInfo<Fmt::FP8> {
   static constexpr int bytes = 1, q_bytes = 2;
   static constexpr bool quantized = true;
-  static constexpr float code_scale = 256.0f;
 };
 // int4: two codes per byte (bytes = 0 marks the packed format; rows are D/2
 // bytes), a scale per kInt4Group dims.
 template <> struct FmtInfo<Fmt::I4> {
   static constexpr int bytes = 0, q_bytes = 2;
   static constexpr bool quantized = true;
-  static constexpr float code_scale = 1.0f;
 };
 
 __device__ __forceinline__ float bits_to_float(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -137,17 +134,14 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 
 namespace pa {
 
-// Two OCP E4M3 codes (bytes `b` and `b+1` of w, picked by the v_perm
-// selector) -> two binary16 values equal to the codes' values times 2^-8,
-// exactly: the sign moves to bit 15 and the 7 exponent/fraction bits to bits
-// 13..7, so an E4M3 exponent field e (bias 7) becomes a binary16 exponent
-// field e (bias 15) and subnormals stay subnormal.  The NaN code is never
-// stored by the quantizer.
-__device__ __forceinline__ uint32_t e4m3_pair_to_f16(uint32_t w, uint32_t sel) {
-  const uint32_t x = __builtin_amdgcn_perm(0u, w, sel);  // codes in bits 15..8 and 31..24
-  return ((x >> 1) & 0x3F803F80u) | (x & 0x80008000u);
+// Four OCP E4M3 codes (bytes 0..3 of w) -> binary16 pairs (byte 0, byte 1)
+// and (byte 2, byte 3), exactly: every E4M3 value, subnormals included, is a
+// binary16 value, and v_cvt_scalef32_pk_f16_fp8 with scale 1 converts each
+// code to it (checked on MI355X for all 256 codes in every byte position,
+// signed zeros kept).  The NaN code is never stored by the quantizer.
+__device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
-constexpr uint32_t kE4m3Lo = 0x010C000Cu;  // bytes 0, 1
-constexpr uint32_t kE4m3Hi = 0x030C020Cu;  // bytes 2, 3
 
 }  // namespace pa
