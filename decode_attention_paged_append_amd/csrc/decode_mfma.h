@@ -29,9 +29,14 @@
 //    a per-lane multiply; it is skipped when no running max moved.
 //  * P is rounded to the operand format (fp16 / bf16) for the value product;
 //    the running sum uses the fp32 weights.
-//  * int8 caches: codes become fp16 exactly (byte + 1024 under the exponent
-//    0x64, minus 1152); the key scale multiplies the score and the value
-//    scale the weight of its token.
+//  * int8 caches: a code c enters both products as the fp16 subnormal
+//    (c + 128) * 2^-24, exactly (its byte with the sign bit flipped, under a
+//    zero high byte: one XOR and a v_perm per two codes).  The +128 comes out
+//    once per product: the score MFMAs start from -128 * 2^-24 * sum(q), and
+//    the value result drops 128 * (column sum of the weights), kept beside
+//    the running sums.  The key scale multiplies the score, the value scale
+//    the weight of its token.
+//  * fp8 caches: codes become fp16 exactly (v_cvt_scalef32_pk_f16_fp8).
 #pragma once
 
 #include "decode_kernel.h"
@@ -83,19 +88,27 @@ template <> struct Mfma<Fmt::BF16> {
   }
 };
 
-// Four 8-bit codes -> four exact fp16 values (two words, element order kept).
+// Four 8-bit codes -> four exact fp16 values (two words, element order kept);
+// int8 codes as the biased subnormals (c + 128) * 2^-24.
 template <Fmt F>
 __device__ __forceinline__ u32x2 codes4_to_f16(uint32_t w) {
-  h16x2 lo, hi;
-  Frag<F>::codes_to_half2(w, lo, hi);
-  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  if constexpr (F == Fmt::I8) {
+    const uint32_t u = w ^ 0x80808080u;
+    return u32x2{__builtin_amdgcn_perm(0u, u, 0x0C010C00u), __builtin_amdgcn_perm(0u, u, 0x0C030C02u)};
+  } else {
+    h16x2 lo, hi;
+    Frag<F>::codes_to_half2(w, lo, hi);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  }
 }
+constexpr float kSub = 16777216.0f;  // 2^24: scale of the int8 subnormal codes
 
 // Heads per workgroup (GC, padded to 16 in the MFMA) x NW waves.
 template <Fmt F, int D, int BS, int GC, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void decode_mfma_kernel(const DecodeParams p) {
   constexpr bool kQuant = FmtInfo<F>::quantized;
+  constexpr bool kBias = F == Fmt::I8;          // codes biased by +128 (subnormals)
   constexpr Fmt OF = kQuant ? Fmt::F16 : F;     // MFMA operand format
   using MM = Mfma<OF>;
   constexpr int EB = FmtInfo<F>::bytes;         // cache element bytes
@@ -162,9 +175,22 @@ void decode_mfma_kernel(const DecodeParams p) {
     if (n < GC)
       qb[c] = *(const u32x4*)((const char*)p.q + ((out_row0 + n) * D + 32 * c + 8 * g) * 2);
   }
+  // int8: start of the score accumulation, -128 * 2^-24 * sum of head n's q
+  float qbias = 0.0f;
+  if constexpr (kBias) {
+#pragma unroll
+    for (int c = 0; c < QKS; ++c) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qbias += f16_lo(qb[c][w]) + f16_hi(qb[c][w]);
+    }
+    qbias += __shfl_xor(qbias, 16);
+    qbias += __shfl_xor(qbias, 32);
+    qbias *= -128.0f / kSub;
+  }
 
   float m = kMaxInit;  // running max of head n (log2 units), same in all g
   float lsum = 0.0f;   // this lane's share of head n's running sum
+  float corr = 0.0f;   // int8: this lane's share of head n's sum of fp16 weights
   f32x4 o[VE];         // O^T: rows dim (D/16)*(4g+i) + e, column head n
 #pragma unroll
   for (int e = 0; e < VE; ++e) o[e] = f32x4{0, 0, 0, 0};
@@ -293,16 +319,17 @@ void decode_mfma_kernel(const DecodeParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- scores: S^T = K . Q^T, lane (g, n): tokens 4g+i of head n
-    f32x4 sacc = {0, 0, 0, 0};
+    f32x4 sacc = {qbias, qbias, qbias, qbias};
 #pragma unroll
     for (int c = 0; c < QKS; ++c) {
       const u32x4 a = ktile[n * CHUNKS + ((4 * c + g) ^ (n % CHUNKS))];
       sacc = MM::qk(a, qb[c], sacc);
     }
+    constexpr float zs = kBias ? kSub : 1.0f;
     float z[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = kQuant ? sacc[i] * (ksc[i] * p.scale_log2) : sacc[i] * p.scale_log2;
+      z[i] = kQuant ? sacc[i] * (ksc[i] * (p.scale_log2 * zs)) : sacc[i] * p.scale_log2;
       if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) z[i] = -__builtin_inff();
     }
     float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -320,15 +347,19 @@ void decode_mfma_kernel(const DecodeParams p) {
       ps += pw[i];
     }
     lsum = fmaf(lsum, alpha, ps);
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+    // a real branch (the hint keeps the compiler from if-converting it): the
+    // rescale runs only on tiles that raise some running max
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(moved) != 0, 0)) {
 #pragma unroll
       for (int e = 0; e < VE; ++e) o[e] *= alpha;
+      corr *= alpha;
     }
     if constexpr (kQuant) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) pw[i] *= vsc[i];
     }
     const u32x2 pb = {MM::pack(pw[0], pw[1]), MM::pack(pw[2], pw[3])};
+    if constexpr (kBias) corr = MM::sum2(pb[1], MM::sum2(pb[0], corr));
 
     // ---- values: O^T += V^T . P^T, MFMA e uses dim (D/16)*row + e
     uint32_t vh[4][VE / 2];  // fp16/bf16 words of tokens 4g+j, dims of lane n
@@ -390,13 +421,19 @@ void decode_mfma_kernel(const DecodeParams p) {
   // ---- merge: sum the lanes' shares of l, then the waves through LDS
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
+  if constexpr (kBias) {
+    corr += __shfl_xor(corr, 16);
+    corr += __shfl_xor(corr, 32);
+  }
   __syncthreads();  // every wave is done with its K tile region
   float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][D]
   if (n < GC) {
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_acc[n * D + (D / 16) * (4 * g + i) + e] = o[e][i];
+      for (int i = 0; i < 4; ++i)
+        s_acc[n * D + (D / 16) * (4 * g + i) + e] =
+            kBias ? fmaf(o[e][i], kSub, -128.0f * corr) : o[e][i];
     }
     if (g == 0) {
       s_ml[wave][n][0] = m;
