@@ -519,7 +519,9 @@ pa_status pa_paged_prefill_attention(const void* q, const void* k_cache, const v
   const int64_t rows = (int64_t)max_query_len * p.group;
   const pa::PrefillShape shape = pa::prefill_shape(cache->head_dim, rows);
   const int64_t row_tiles = (rows + shape.rows() - 1) / shape.rows();
-  if (row_tiles > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "chunk too long");
+  if (row_tiles > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "chunk of %d tokens x %d heads per KV head needs %lld row "
+                "tiles, more than 65535", max_query_len, p.group, (long long)row_tiles);
   const hipError_t e =
       cache->dtype == PA_F16
           ? pa::launch_prefill_f16(p, cache->head_dim, cache->block_size, shape, (int)row_tiles,

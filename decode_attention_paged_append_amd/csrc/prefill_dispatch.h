@@ -22,7 +22,7 @@ template <Fmt F, int D, int BS, int NR, int NW>
 static hipError_t launch_prefill_one(const PrefillParams& p, int row_tiles, int num_seqs,
                                      hipStream_t stream) {
   hipLaunchKernelGGL((prefill_mfma_kernel<F, D, BS, NR, NW>),
-                     dim3(row_tiles, p.num_kv_heads, num_seqs), dim3(NW * kWave), 0, stream, p);
+                     dim3(p.num_kv_heads, num_seqs, row_tiles), dim3(NW * kWave), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -67,13 +67,17 @@ void prefill_mfma_kernel(const PrefillParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4;
   const int n = lane & 15;
-  const int s = blockIdx.z;
-  const int kvh = blockIdx.y;
+  // grid (KV head, sequence, row tile): the KV head runs fastest, so every
+  // row tile of a (sequence, KV head) lands on the same XCD (the one whose L2
+  // holds its K/V), and the row tile slowest, so all the longest tiles of the
+  // launch are dispatched first
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
   const int G = p.group;
   const int q0 = p.query_start[s];
   const int T = p.query_start[s + 1] - q0;
   const int ctx = p.context_lens[s];
-  const int R0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * RWG;  // late rows (most work) first
+  const int R0 = ((int)gridDim.z - 1 - (int)blockIdx.z) * RWG;  // late rows (most work) first
   if (R0 >= T * G) return;
   const int Hq = p.num_q_heads;
 

@@ -382,7 +382,9 @@ pa_status pa_paged_decode_attention_window(const void* q, const void* k_cache,
  *   context_lens   : device int32 [num_seqs], each >= its chunk length
  *   max_query_len  : host bound on every T_s (sizes the grid); tokens of a
  *                    longer chunk are not computed
- * Only fp16 and bf16 caches (head_dim 64 or 128, any supported block size).
+ * Only fp16 and bf16 caches (head_dim 64 or 128, any supported block size);
+ * PA_ERR_UNSUPPORTED when max_query_len * (num_q_heads / num_kv_heads) query
+ * rows need more than 65535 row tiles of 256 (16.7 M rows).
  * A sequence whose context length is below its chunk length or above
  * max_blocks_per_seq * block_size gets NaN rows, as does one whose needed
  * table entries name a block outside the pool. */
