@@ -22,13 +22,17 @@
 // Lane l = 16g + n.  The two 16-token halves of a score tile leave lane (g, n)
 // holding tokens {4g..4g+3, 16+4g..16+4g+3} of row n, which is the B operand
 // P^T of the value product when its 32 k-slots are mapped to those tokens;
-// the A operand V^T is read from LDS as the same 8 token rows at the lane's
-// dims n*VE.. and packed with v_perm (row r of value MFMA e = dim r*VE + e).
+// the A operand V^T comes straight from LDS through transposing reads
+// (ds_read_b64_tr_b16): dim 16e + n of those 8 tokens for value MFMA e.
 #pragma once
 
 #include "decode_mfma.h"
 
 namespace pa {
+
+struct VtOperand {  // the two transposed reads of a value MFMA's A operand
+  i16x4 lo, hi;
+};
 
 struct PrefillParams {
   const void* q;            // [total][Hq][D]
@@ -182,7 +186,7 @@ void prefill_mfma_kernel(const PrefillParams p) {
       const int c = idx - row * CH;
       if (!EVEN && idx >= TILE_CHUNKS) continue;
       if (s < ntiles) s_k[s & 1][row * CH + (c ^ (row % CH))] = st.k[j];
-      if (s >= 1) s_v[(s - 1) & 1][idx] = st.v[j];
+      if (s >= 1) s_v[(s - 1) & 1][row * CH + (c ^ (row & 7))] = st.v[j];
     }
   };
 
@@ -273,30 +277,26 @@ void prefill_mfma_kernel(const PrefillParams p) {
   // O^T += V^T . P^T
   auto values = [&](const int t, const u32x4 (&pb)[NR]) {
     const int buf = t & 1;
-    uint32_t vh[8][VE / 2];  // token rows {4g+j, 16+4g+j}, dims n*VE..
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int vrow = (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
-      if constexpr (VE == 8) {
-        const u32x4 w = s_v[buf][vrow * CH + n];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) vh[j][k] = w[k];
-      } else {
-        const u32x2 w = ((const u32x2*)&s_v[buf][0])[vrow * (CH * 2) + n];
-        vh[j][0] = w[0];
-        vh[j][1] = w[1];
-      }
-    }
-    // V^T operand of value MFMA e: the 8 token rows' values at dim n*VE + e,
-    // built just before its MFMAs
+    const _Float16* vt = (const _Float16*)&s_v[buf][0];
+    // Transposing LDS reads (ds_read_b64_tr_b16): within each 16-lane group,
+    // lane 4q + j receives half j of the 8 bytes that lanes 4k + q (k = 0..3)
+    // point at.  Lane (g, 4k + q) points at token row 4g + k, dims 16e + 4q
+    // .. +3, so lane (g, n) receives dim 16e + n of tokens 4g .. 4g+3: the A
+    // operand V^T of value MFMA e (row n = dim 16e + n), with a second read
+    // for tokens 16 + 4g .. (the k-slots 4..7 of the lane's weights).  V's
+    // 16-byte chunks sit XOR-swizzled by row & 7 (measured on MI355X: 1 %
+    // ahead of row % 16 at head_dim 128, and 4-6 % ahead of row-major rows
+    // read whole and regrouped with v_perm).
+    const int k = n >> 2, q = n & 3;
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const int w = e >> 1;
-      const u32x4 va = {__builtin_amdgcn_perm(vh[1][w], vh[0][w], sel),
-                        __builtin_amdgcn_perm(vh[3][w], vh[2][w], sel),
-                        __builtin_amdgcn_perm(vh[5][w], vh[4][w], sel),
-                        __builtin_amdgcn_perm(vh[7][w], vh[6][w], sel)};
+      const int chunk = 2 * e + (q >> 1);
+      auto read = [&](const int row) {
+        const int off = row * D + (chunk ^ (row & 7)) * 8 + (q & 1) * 4;
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vt + off));
+      };
+      const u32x4 va = __builtin_bit_cast(u32x4, VtOperand{read(4 * g + k), read(16 + 4 * g + k)});
 #pragma unroll
       for (int r = 0; r < NR; ++r) o[r][e] = MM::qk(va, pb[r], o[r][e]);
     }
@@ -341,7 +341,7 @@ void prefill_mfma_kernel(const PrefillParams p) {
   };
   for (int t = 0; t <= ntiles; ++t) step(t);
 
-  // ---- normalise and store: lane (g, n) holds dims (4g+i)*VE + e of row n
+  // ---- normalise and store: lane (g, n) holds dims 16e + 4g + i of row n
   const bool bad = __syncthreads_or(bad_block ? 1 : 0) != 0;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -354,19 +354,11 @@ void prefill_mfma_kernel(const PrefillParams p) {
     if (tok >= T) continue;
     const size_t orow = (size_t)(q0 + tok) * Hq + kvh * G + rr % G;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t off = orow * D + (4 * g + i) * VE;
-      if constexpr (VE == 8) {
-        const u32x4 w = {MM::pack(o[r][0][i] * inv, o[r][1][i] * inv),
-                         MM::pack(o[r][2][i] * inv, o[r][3][i] * inv),
-                         MM::pack(o[r][4][i] * inv, o[r][5][i] * inv),
-                         MM::pack(o[r][6][i] * inv, o[r][7][i] * inv)};
-        *(u32x4*)((char*)p.out + off * 2) = w;
-      } else {
-        const u32x2 w = {MM::pack(o[r][0][i] * inv, o[r][1][i] * inv),
-                         MM::pack(o[r][2][i] * inv, o[r][3][i] * inv)};
-        *(u32x2*)((char*)p.out + off * 2) = w;
-      }
+    for (int e = 0; e < VE; ++e) {
+      const size_t off = orow * D + 16 * e + 4 * g;
+      const u32x2 w = {MM::pack(o[r][e][0] * inv, o[r][e][1] * inv),
+                       MM::pack(o[r][e][2] * inv, o[r][e][3] * inv)};
+      *(u32x2*)((char*)p.out + off * 2) = w;
     }
   }
 }
