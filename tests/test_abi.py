@@ -143,3 +143,19 @@ def test_read_probe_argument_checks(lib):
     assert lib.pa_hbm_read_probe(src, 4112, None, sink, None) == INVALID
     assert lib.pa_hbm_read_probe(ctypes.c_void_p(4104), 8192, None, sink, None) == INVALID
     assert b"multiple of 4096" in lib.pa_last_error()
+
+
+def test_prefill_argument_checks_on_host(lib):
+    """Prefill rejects bad shapes before any launch: a non-16-bit cache, a
+    non-positive scale, heads that do not divide, and a chunk whose query
+    rows need more than 65535 row tiles of the grid."""
+    d = desc(hkv=2)
+    call = lambda maxq, hq=16, scale=0.1, desc_=d: lib.pa_paged_prefill_attention(
+        FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 4, maxq, hq, scale, FAKE, ctypes.byref(desc_),
+        None)
+    assert call(8, desc_=desc(dtype=0)) == UNSUPPORTED          # fp32 cache
+    assert call(8, scale=0.0) == INVALID
+    assert call(8, hq=3) == INVALID
+    assert call(0) == OK                                         # nothing to do
+    assert call(1 << 24) == UNSUPPORTED                          # 2^27 rows: 524288 tiles
+    assert b"65535" in lib.pa_last_error()

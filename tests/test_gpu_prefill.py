@@ -190,3 +190,16 @@ def test_full_size_sampled_rows(orc):
     assert np.isfinite(got).all()
     ok, err = within(g, ref, "f16", vmax_of(vp, "f16"))
     assert ok, err
+
+
+def test_tokens_past_max_query_len_are_not_written():
+    """max_query_len bounds the grid: a longer chunk's first max_query_len
+    tokens are computed exactly as in a full call, the rest of its rows keep
+    what out held (the documented contract)."""
+    rng = np.random.default_rng(11)
+    kp, vp, bt, qs, ctx_a, q = make_batch(rng, "f16", [300, 70], [40, 10], 16, 2, 128, 16)
+    full = run_gpu("f16", kp, vp, bt, qs, ctx_a, q, 0.1)
+    part = run_gpu("f16", kp, vp, bt, qs, ctx_a, q, 0.1, max_query_len=16)
+    assert np.array_equal(part[:16], full[:16])          # sequence 0, tokens 0..15
+    assert np.isnan(part[16:40]).all()                   # past the bound: untouched (NaN fill)
+    assert np.array_equal(part[40:], full[40:])          # sequence 1 fits the bound
