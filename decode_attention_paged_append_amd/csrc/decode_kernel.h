@@ -327,11 +327,25 @@ __device__ __forceinline__ void store_result(const DecodeParams& p, bool direct,
   }
 }
 
+// Occupancy hint of the vector-ALU kernel (minimum waves per SIMD): 8, 4
+// or 1 for 1, 2 or 8 heads per workgroup; int4 lanes hold 32 values per head
+// (the others 16 or fewer), so they get twice the registers.  A block of
+// one head's rows of 8 KiB or more (counting int8 codes, which are widened to
+// fp32 on the fly, as 4 bytes) halves it and 16 KiB quarters it: at the full
+// hint those instances spilled 40-400 VGPRs, spill-free at the reduced one.
+template <Fmt F, int D, int BS, int GC>
+constexpr int valu_waves_per_simd() {
+  if constexpr (F == Fmt::I4) return GC == 1 ? 4 : 2;
+  const int base = GC == 1 ? 8 : GC == 2 ? 4 : 1;
+  const int eb = F == Fmt::F32 || F == Fmt::I8 ? 4 : 2;
+  const int block_bytes = BS * D * eb;
+  const int div = block_bytes >= 16384 ? 4 : block_bytes >= 8192 ? 2 : 1;
+  return base / div > 0 ? base / div : 1;
+}
+
 template <Fmt F, int D, int BS, int GC, int NW>
-// Occupancy hint: int4 lanes hold 32 values per head (the others 16 or
-// fewer), so they get twice the registers.
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(
-    F == Fmt::I4 ? (GC == 1 ? 4 : 2) : GC == 1 ? 8 : GC == 2 ? 4 : 1, 8)))
+__global__ __launch_bounds__(NW * kWave)
+__attribute__((amdgpu_waves_per_eu(valu_waves_per_simd<F, D, BS, GC>(), 8)))
 void decode_partition_kernel(const DecodeParams p) {
   using FR = Frag<F>;
   constexpr int QB = FmtInfo<F>::q_bytes;     // bytes per query element
