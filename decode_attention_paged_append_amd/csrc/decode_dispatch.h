@@ -101,7 +101,7 @@ hipError_t launch_mfma_i8(const DecodeParams& p, int head_dim, int bs, int gc, i
 hipError_t launch_mfma_fp8(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                            hipStream_t stream);
 hipError_t launch_mfma_i4(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
-                          hipStream_t stream);  // head_dim 128, 4 or 8 heads per workgroup
+                          hipStream_t stream);  // head_dim 128, 4 heads per workgroup
 
 hipError_t launch_decode_f32(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                              hipStream_t stream);

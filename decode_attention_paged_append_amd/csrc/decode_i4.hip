@@ -22,11 +22,9 @@ static hipError_t launch_mfma_i4_one(const DecodeParams& p, int num_seqs, hipStr
 
 hipError_t launch_mfma_i4(const DecodeParams& p, int head_dim, int bs, int gc, int num_seqs,
                           hipStream_t stream) {
-  if (head_dim != 128) return hipErrorInvalidValue;
-  if (bs == 16 && gc == 4) return launch_mfma_i4_one<16, 4>(p, num_seqs, stream);
-  if (bs == 16 && gc == 8) return launch_mfma_i4_one<16, 8>(p, num_seqs, stream);
-  if (bs == 32 && gc == 4) return launch_mfma_i4_one<32, 4>(p, num_seqs, stream);
-  if (bs == 32 && gc == 8) return launch_mfma_i4_one<32, 8>(p, num_seqs, stream);
+  if (head_dim != 128 || gc != 4) return hipErrorInvalidValue;
+  if (bs == 16) return launch_mfma_i4_one<16, 4>(p, num_seqs, stream);
+  if (bs == 32) return launch_mfma_i4_one<32, 4>(p, num_seqs, stream);
   return hipErrorInvalidValue;
 }
 

@@ -29,7 +29,9 @@
 //  * Four heads per column set; the score MFMA repeats each head's query in
 //    all four groups of columns, so every lane already holds the weights of
 //    its column's head (its softmax runs four times over, in lanes that would
-//    otherwise be padding).  Eight heads per workgroup are two sets.
+//    otherwise be padding).  Eight heads per workgroup would be two sets; at
+//    two waves per SIMD that instance spilled 28 VGPRs and ran 1.7x slower
+//    than two four-head workgroups per KV head, so only GC = 4 is launched.
 //  * The rescale of the accumulators by alpha is a real branch: it runs only
 //    on tiles that raise some running max.
 //
