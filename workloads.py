@@ -81,17 +81,19 @@ LLAMA3_8B_I4 = Shape("llama3-8b-int4kv", "i4", 64, 32, 8, 128, 16,
                      description="Llama-3-8B layer, int4 KV + fp16 scales per 32 dims, "
                                  "64 seqs x 8192")
 
-# the headline layer with blocks of 32, and with an int8 cache (one query head
-# per KV head: the vector-ALU kernel at those block sizes)
+# the headline layer with blocks of 32, in bf16, and with an int8 cache (one
+# query head per KV head: the vector-ALU kernel)
 LLAMA2_7B_BS32 = Shape("llama2-7b-f16-bs32", "f16", 16, 32, 32, 128, 32, layers=8,
                        description="Llama-2-7B MHA layer, fp16, block 32, 16 seqs x 4096, 8 layers")
+LLAMA2_7B_BF16 = Shape("llama2-7b-bf16", "bf16", 16, 32, 32, 128, 16, layers=8,
+                       description="Llama-2-7B MHA layer, bf16, 16 seqs x 4096, 8 layers")
 LLAMA2_7B_I8 = Shape("llama2-7b-int8kv", "i8", 16, 32, 32, 128, 16, layers=8,
                      description="Llama-2-7B MHA layer, int8 KV + fp16 scales, 16 seqs x 4096, "
                                  "8 layers")
 
 SHAPES = {s.name: s for s in (TINY, LLAMA3_8B, LLAMA2_7B, LLAMA2_70B, LLAMA3_8B_I8,
                               LLAMA3_8B_FP8, LLAMA3_8B_WINDOW, LLAMA3_8B_I4, LLAMA2_7B_BS32,
-                              LLAMA2_7B_I8)}
+                              LLAMA2_7B_BF16, LLAMA2_7B_I8)}
 
 TINY_POOL_BLOCKS = 64
 PREFIX_GROUP = 8          # sequences per shared-prefix group (Llama-2-70B workload)
@@ -108,7 +110,8 @@ def context_lengths(shape: Shape) -> list[int]:
     """Context length of every sequence, counting the token being decoded."""
     if shape.name == TINY.name:
         return [3, 7, 16, 33]
-    if shape.name in (LLAMA3_8B.name, LLAMA2_7B.name, LLAMA2_7B_BS32.name, LLAMA2_7B_I8.name):
+    if shape.name in (LLAMA3_8B.name, LLAMA2_7B.name, LLAMA2_7B_BS32.name, LLAMA2_7B_BF16.name,
+                      LLAMA2_7B_I8.name):
         return [4096] * shape.num_seqs
     if shape.name in (LLAMA3_8B_I8.name, LLAMA3_8B_FP8.name, LLAMA3_8B_I4.name):
         return [8192] * shape.num_seqs
