@@ -604,7 +604,8 @@ def main():
         "kv_bytes_per_step": kv_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": (("decode_mfma_i4_kernel" if b.int4 else "decode_mfma_kernel") if b.mfma
+            "kernel": (("decode_mfma_kernel" if not b.int4 else "decode_mfma_i4h_kernel"
+                        if shape.group % 8 == 0 else "decode_mfma_i4_kernel") if b.mfma
                        else "decode_partition_kernel")
                       + (" + lse_merge_kernel (one windowed call)" if b.window else ""),
             "achieved": round(achieved, 2),

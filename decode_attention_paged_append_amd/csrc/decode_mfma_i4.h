@@ -32,6 +32,8 @@
 //    otherwise be padding).  Eight heads per workgroup would be two sets; at
 //    two waves per SIMD that instance spilled 28 VGPRs and ran 1.7x slower
 //    than two four-head workgroups per KV head, so only GC = 4 is launched.
+//    Groups of eight or more heads take decode_mfma_i4h_kernel below, which
+//    widens a tile once for sixteen heads.
 //  * The rescale of the accumulators by alpha is a real branch: it runs only
 //    on tiles that raise some running max.
 //
@@ -376,6 +378,358 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
       const float a = fast_exp2(s_ml[w][h][0] - M);
       L = fmaf(a, s_ml[w][h][1], L);
       acc = fmaf(a, ((const float*)(s_mem + w * REGION))[h * D + d], acc);
+    }
+    if (bad) M = L = acc = __builtin_nanf("");
+    store_result<Fmt::I4, D>(p, single, out_row0 + h, slot, d, M, L, acc);
+  }
+}
+
+// Eight or sixteen query heads per workgroup, one head per column: the
+// matrix-core path for int4 caches with GQA groups of 8 or more.  With
+// (head, group) columns a workgroup holds 4 heads and every further four
+// fetch and widen the same tile again; here a tile is fetched and widened
+// once for all GC heads.
+//
+//  * Scores as in decode_mfma_i4_kernel (one MFMA and accumulator per scale
+//    group), with column n standing for head n % GC: at GC = 8 the second
+//    eight columns repeat the first and are not stored.
+//  * Values per scale group c: O^T[dim][head] += V^T[dim][tok] . B_c[tok][head]
+//    over the 32 dims of group c (two MFMAs of 16 rows), B_c = p * (value
+//    scale of group c at tok), rounded to fp16.  Every row of an MFMA lies
+//    in one group, so its B operand carries that group's scale.  The rows of
+//    value MFMA e are dims 16e .. 16e+15, which no lane's 16-byte load holds
+//    for four tokens at once: V goes through a per-wave LDS tile as the same
+//    subnormal codes as K, and transposing reads (ds_read_b64_tr_b16) give
+//    lane (g, n) dim 16e + n of tokens 4g .. 4g+3.
+//  * S^T comes out with lane (g, n) holding tokens 4g .. 4g+3 of head n,
+//    which is the B operand layout: the weights never move, and the running
+//    max, sum and column sums of B are per lane.  Lane (g, n) ends with dims
+//    16e + 4g + i of head n; the result is 2^24 * O^T - 8 * (column sum of
+//    B_c) per group.
+template <int BS, int GC, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void decode_mfma_i4h_kernel(const DecodeParams p) {
+  constexpr int D = 128;
+  constexpr int TT = 16;                  // positions per tile
+  constexpr int ROWB = D / 2;             // cache bytes per row
+  constexpr int KG = D / kInt4Group;      // scale groups per row = score MFMAs
+  constexpr int VE = D / 16;              // value MFMAs (two per group)
+  constexpr int CHUNKS = D / 8;           // 16-byte chunks per fp16 row in LDS
+  constexpr int K_LPR = ROWB / 16;        // lanes per row in a K or V load
+  constexpr int ACC_STRIDE = D + 4;       // floats per head row of the merge buffer
+  constexpr int TPI = 2;                  // tiles fetched per loop iteration
+  constexpr int SC_WORDS = TT * KG / 2;   // words of one tile's key (or value) scales
+  static_assert(GC == 8 || GC == 16, "eight or sixteen heads per workgroup");
+  static_assert(BS % TT == 0, "a tile lies inside one block");
+  static_assert(TT * ROWB == kWave * 16, "one K or V tile = one 16-byte load per lane");
+  static_assert(VE == 2 * KG, "two value MFMAs per scale group");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int head = n % GC;  // this lane's column
+  const WgCoord wc = wg_coord();
+  const int slot = wc.part;
+  const int kvh = wc.y / p.head_chunks;
+  const int chunk = wc.y - kvh * p.head_chunks;
+  const int s = wc.s;
+  const int h0 = kvh * p.group + chunk * GC;
+  const size_t out_row0 = (size_t)s * p.num_q_heads + h0;
+
+  const int ctx = p.context_lens[s];
+  const bool single = p.num_parts == 1;
+  const int tok0 = partition_of_slot(p, slot, ctx) * p.part_tokens;
+  const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
+  if (bad_ctx || tok0 >= ctx) {
+    if (single) {
+      const float fill = bad_ctx ? __builtin_nanf("") : 0.0f;
+      for (int i = threadIdx.x; i < GC * D; i += NW * kWave)
+        store_out<Fmt::I4>(p.out, out_row0 * D + i, fill);
+    }
+    return;
+  }
+  const int tok_end = min(ctx, tok0 + p.part_tokens);
+  const int start = window_start(p, ctx);
+  if (tok_end <= start) {  // wholly before the window (never the only partition)
+    for (int i = threadIdx.x; i < GC * D; i += NW * kWave)
+      store_result<Fmt::I4, D>(p, false, out_row0 + i / D, slot, i % D, kMaxInit, 0.0f, 0.0f);
+    return;
+  }
+  const int ntiles = (tok_end - tok0 + TT - 1) / TT;
+  const int t_first = (max(tok0, start) - tok0) / TT;
+  const bool low_cut = start > tok0 + t_first * TT;
+  const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
+
+  // Query of column n's head, dims 32c + 8g .. +8: the B operand of score
+  // MFMA c; the accumulator start removes the code bias.
+  u32x4 qb[KG];
+  float qbias[KG];
+#pragma unroll
+  for (int c = 0; c < KG; ++c) {
+    qb[c] = *(const u32x4*)((const char*)p.q + ((out_row0 + head) * D + 32 * c + 8 * g) * 2);
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) t += f16_lo(qb[c][w]) + f16_hi(qb[c][w]);
+    t += __shfl_xor(t, 16);
+    t += __shfl_xor(t, 32);
+    qbias[c] = -8.0f * kTwoM24 * t;
+  }
+
+  float m = kMaxInit, lsum = 0.0f;
+  float corr[KG];  // column sums of B_c (this lane's tokens)
+  f32x4 o[VE];     // O^T * 2^-24 (biased codes): dims 16e + 4g + i, head n
+#pragma unroll
+  for (int c = 0; c < KG; ++c) corr[c] = 0.0f;
+#pragma unroll
+  for (int e = 0; e < VE; ++e) o[e] = f32x4{0, 0, 0, 0};
+  bool bad_block = false;
+
+  constexpr int TILE_BYTES = TT * D * 2;           // one tile of fp16 codes
+  constexpr int TILES_BYTES = 2 * TILE_BYTES + 2 * SC_WORDS * 4;
+  constexpr int ACC_BYTES = GC * ACC_STRIDE * 4;
+  constexpr int REGION = TILES_BYTES > ACC_BYTES ? TILES_BYTES : ACC_BYTES;
+  static_assert(2 * SC_WORDS == kWave, "one scale word per lane");
+  __shared__ __attribute__((aligned(16))) char s_mem[NW * REGION];
+  __shared__ float s_ml[NW][GC][2];
+  u32x4* const ktile = (u32x4*)(s_mem + wave * REGION);
+  u32x4* const vtile = ktile + TT * CHUNKS;
+  uint32_t* const stile = (uint32_t*)(vtile + TT * CHUNKS);  // key, then value scales
+
+  const char* __restrict__ kbase = (const char*)p.k_cache;
+  const char* __restrict__ vbase = (const char*)p.v_cache;
+  const int blk0 = tok0 / BS;
+  const int nblk = (tok_end + BS - 1) / BS - blk0;
+  int ids = 0;
+  int ids_base = -kWave;
+
+  // The tile's scales arrive as one word per lane (lanes 0..31 the key
+  // scales, 32..63 the value scales, each [row][group] in order) and are
+  // spread through LDS: fetched whole by every lane, they took two thirds
+  // of the registers of a tile in flight.
+  struct Raw {
+    u32x4 k, v;        // 32 codes each: row lane / 4, dims 32 (lane % 4) ..
+    uint32_t sc;       // scale word lane % 32 of the tile (zero on masked rows)
+    int nvalid;        // rows of the tile inside the partition
+    int nlow;          // rows below this one are before the window
+  };
+
+  auto fetch = [&](const int t, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    Raw raw;
+    const int ttok = tok0 + t * TT;
+    const int nvalid = tok_end - ttok;
+    const int nlow = start - ttok;
+    raw.nvalid = nvalid;
+    raw.nlow = nlow;
+    const int rel = ttok / BS - blk0;
+    if (rel >= ids_base + kWave) {
+      ids_base = rel & ~(kWave - 1);
+      const int bi = ids_base + lane;
+      ids = bi < nblk ? table[blk0 + bi] : 0;
+    }
+    int phys = __builtin_amdgcn_readlane(ids, rel - ids_base);
+    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    bad_block |= !ok;
+    phys = ok ? phys : 0;
+    const size_t row0 = ((size_t)phys * p.num_kv_heads + kvh) * BS + ttok % BS;
+
+    const int r = lane / K_LPR;
+    raw.k = u32x4{0, 0, 0, 0};
+    raw.v = u32x4{0, 0, 0, 0};
+    if (!PARTIAL || (r >= nlow && r < nvalid)) {
+      raw.k = load16_stream(kbase + row0 * ROWB + lane * 16);
+      raw.v = load16_stream(vbase + row0 * ROWB + lane * 16);
+    }
+    // rows outside [nlow, nvalid) get zero scales: their B is 0
+    const int sw = lane & (SC_WORDS - 1);
+    const int sr = sw / (KG / 2);
+    const uint32_t* ssrc = (const uint32_t*)(lane < SC_WORDS ? p.k_scale : p.v_scale);
+    raw.sc = (!PARTIAL || (sr >= nlow && sr < nvalid)) ? ssrc[row0 * (KG / 2) + sw] : 0u;
+    return raw;
+  };
+
+  auto consume = [&](const Raw& raw, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    const int nvalid = raw.nvalid;
+    const int nlow = raw.nlow;
+
+    // ---- K and V tiles -> LDS as subnormal codes.  K's 16-byte chunk c of
+    // row r sits at c ^ (r % CHUNKS) (read whole rows), V's at c ^ (r & 7)
+    // (read transposed).
+    {
+      const int r = lane / K_LPR;
+      const int c0 = 4 * (lane % K_LPR);
+      stile[lane] = raw.sc;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t xk = raw.k[w];
+        const uint32_t klo = xk & kNibbles, khi = (xk >> 4) & kNibbles;
+        ktile[r * CHUNKS + ((c0 + w) ^ (r % CHUNKS))] =
+            u32x4{__builtin_amdgcn_perm(khi, klo, i4_sel(0)), __builtin_amdgcn_perm(khi, klo, i4_sel(1)),
+                  __builtin_amdgcn_perm(khi, klo, i4_sel(2)), __builtin_amdgcn_perm(khi, klo, i4_sel(3))};
+        const uint32_t xv = raw.v[w];
+        const uint32_t vlo = xv & kNibbles, vhi = (xv >> 4) & kNibbles;
+        vtile[r * CHUNKS + ((c0 + w) ^ (r & 7))] =
+            u32x4{__builtin_amdgcn_perm(vhi, vlo, i4_sel(0)), __builtin_amdgcn_perm(vhi, vlo, i4_sel(1)),
+                  __builtin_amdgcn_perm(vhi, vlo, i4_sel(2)), __builtin_amdgcn_perm(vhi, vlo, i4_sel(3))};
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    u32x4 ka[KG];
+#pragma unroll
+    for (int c = 0; c < KG; ++c) ka[c] = ktile[n * CHUNKS + ((4 * c + g) ^ (n % CHUNKS))];
+    // scales of tokens 4g .. 4g+3 x KG groups (one address per 16 lanes)
+    uint32_t ks[8], vs[8];
+    {
+      const u32x4* s4 = (const u32x4*)stile;
+      const u32x4 k0 = s4[2 * g], k1 = s4[2 * g + 1];
+      const u32x4 v0 = s4[8 + 2 * g], v1 = s4[8 + 2 * g + 1];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        ks[w] = k0[w];
+        ks[4 + w] = k1[w];
+        vs[w] = v0[w];
+        vs[4 + w] = v1[w];
+      }
+    }
+
+    // ---- scores: one accumulator per scale group, scaled in fp32
+    float sacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < KG; ++c) {
+      const float b0 = qbias[c];
+      const f32x4 sc = Mfma<Fmt::F16>::qk(ka[c], qb[c], f32x4{b0, b0, b0, b0});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = ks[(i * KG + c) >> 1];
+        sacc[i] = fmaf(sc[i], (c & 1) ? f16_hi(w) : f16_lo(w), sacc[i]);
+      }
+    }
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = sacc[i] * (p.scale_log2 * kTwo24);
+      if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) z[i] = -__builtin_inff();
+    }
+    float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const bool moved = mn > m;
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    float pw[4];
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] = fast_exp2(z[i] - mn);
+      ps += pw[i];
+    }
+    lsum = fmaf(lsum, alpha, ps);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(moved) != 0, 0)) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[e] *= alpha;
+#pragma unroll
+      for (int c = 0; c < KG; ++c) corr[c] *= alpha;
+    }
+
+    // ---- values: B_c = p * value scale of group c, fp16; A = V^T read
+    // transposed: within each 16-lane group, lane 4a + b receives half b of
+    // the 8 bytes that lanes 4k + a (k = 0..3) point at, and lane (g, 4k + a)
+    // points at token row 4g + k, dims 16e + 4a .. +3.
+    const _Float16* vt = (const _Float16*)vtile;
+    const int vrow = 4 * g + (n >> 2);
+    const int vq = n & 3;
+#pragma unroll
+    for (int c = 0; c < KG; ++c) {
+      auto vsc = [&](int i) {
+        const uint32_t w = vs[(i * KG + c) >> 1];
+        return (c & 1) ? f16_hi(w) : f16_lo(w);
+      };
+      const u32x2 pb = {Mfma<Fmt::F16>::pack(pw[0] * vsc(0), pw[1] * vsc(1)),
+                        Mfma<Fmt::F16>::pack(pw[2] * vsc(2), pw[3] * vsc(3))};
+      corr[c] = Mfma<Fmt::F16>::sum2(pb[1], Mfma<Fmt::F16>::sum2(pb[0], corr[c]));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = 2 * c + h;
+        const int ch = 2 * e + (vq >> 1);
+        const int off = vrow * D + (ch ^ (vrow & 7)) * 8 + (vq & 1) * 4;
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vt + off));
+        o[e] = Mfma<Fmt::F16>::pv(__builtin_bit_cast(u32x2, va), pb, o[e]);
+      }
+    }
+  };
+
+  const int nfull = (tok_end - tok0) / TT;
+  int t = t_first + wave;
+  if (low_cut && wave == 0) {
+    const Raw a = fetch(t, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    consume(a, std::true_type{});
+    t += NW;
+  }
+  for (; t + (TPI - 1) * NW < nfull; t += TPI * NW) {
+    Raw r[TPI];
+#pragma unroll
+    for (int i = 0; i < TPI; ++i) r[i] = fetch(t + i * NW, std::false_type{});
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TPI; ++i) consume(r[i], std::false_type{});
+  }
+  for (; t < ntiles; t += NW) {
+    if (t < nfull) {
+      const Raw a = fetch(t, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      consume(a, std::false_type{});
+    } else {
+      const Raw a = fetch(t, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      consume(a, std::true_type{});
+    }
+  }
+
+  // ---- merge: the lanes' shares of l and of the column sums, then the
+  // waves through LDS (head rows padded by 4 floats: conflict-free stores)
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+#pragma unroll
+  for (int c = 0; c < KG; ++c) {
+    corr[c] += __shfl_xor(corr[c], 16);
+    corr[c] += __shfl_xor(corr[c], 32);
+  }
+  __syncthreads();  // every wave is done with its tile region
+  float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][ACC_STRIDE]
+  if (n < GC) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const float b = -8.0f * corr[e / 2];
+      *(f32x4*)(s_acc + n * ACC_STRIDE + 16 * e + 4 * g) =
+          f32x4{fmaf(o[e][0], kTwo24, b), fmaf(o[e][1], kTwo24, b), fmaf(o[e][2], kTwo24, b),
+                fmaf(o[e][3], kTwo24, b)};
+    }
+    if (g == 0) {
+      s_ml[wave][n][0] = m;
+      s_ml[wave][n][1] = lsum;
+    }
+  }
+  const bool bad = __syncthreads_or(bad_block ? 1 : 0) != 0;
+  for (int i = threadIdx.x; i < GC * D; i += NW * kWave) {
+    const int h = i / D;
+    const int d = i - h * D;
+    float M = s_ml[0][h][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h][0]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float a = fast_exp2(s_ml[w][h][0] - M);
+      L = fmaf(a, s_ml[w][h][1], L);
+      acc = fmaf(a, ((const float*)(s_mem + w * REGION))[h * ACC_STRIDE + d], acc);
     }
     if (bad) M = L = acc = __builtin_nanf("");
     store_result<Fmt::I4, D>(p, single, out_row0 + h, slot, d, M, L, acc);

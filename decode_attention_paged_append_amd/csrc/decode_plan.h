@@ -122,13 +122,14 @@ inline pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num
   const int32_t group = num_q_heads / c->num_kv_heads;
   // Four or more query heads per KV head: the score and value products are
   // dense enough for the matrix cores (fp16 / bf16 / int8 / fp8 caches, and
-  // int4 at head_dim 128, 4 heads per workgroup; blocks of 16 or 32).
-  // Otherwise the vector-ALU kernel, up to 8 heads per workgroup (int4: 2).
+  // int4 at head_dim 128; blocks of 16 or 32), 4, 8 or 16 heads per
+  // workgroup.  Otherwise the vector-ALU kernel, up to 8 heads per workgroup
+  // (int4: 2).
   const int32_t gc_mfma = group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : 0;
   if (c->dtype != PA_F32 && (c->dtype != PA_I4 || c->head_dim == 128) &&
       (c->block_size == 16 || c->block_size == 32) && gc_mfma >= 4) {
     p.mfma = true;
-    p.gc = c->dtype == PA_I4 ? 4 : gc_mfma;  // int4: 4 (eight spill and ran 1.7x slower)
+    p.gc = gc_mfma;
   } else if (c->dtype == PA_I4) {  // 32 values per lane and head: at most 2 heads
     p.gc = group % 2 == 0 ? 2 : 1;
   } else {

@@ -2,8 +2,10 @@
 quantizing append bit-exact (packed codes and group scales), decode
 attention over the same codes and scales within tolerance (the vector-ALU
 kernel at one or two query heads per KV head, head_dim 64 or block 4; the
-matrix-core kernel at 4, 8 and 16 with head_dim 128 and blocks of 16 or 32),
-windowed decode, the gather and the block copy, and a full-size case."""
+matrix-core kernels at 4, 8, 16 and 32 with head_dim 128 and blocks of 16 or
+32: four heads per workgroup as (head, group) columns, eight or sixteen as one
+head per column), windowed decode on both, the gather and the block copy, and
+full-size cases."""
 import numpy as np
 import pytest
 import torch
@@ -79,7 +81,7 @@ def test_kv_append_int4_bit_exact(d):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bs", [4, 16, 32])
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (32, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (32, 2), (64, 2)])
 def test_int4_decode_matches_oracle(d, bs, hq, hkv, orc):
     ctx = [1, bs + 3, 200, 513]
     shape, lay, case = make("f16", hq, hkv, d, bs, ctx, seed=5, spare_blocks=2)
@@ -158,6 +160,32 @@ def test_int4_window_gather_copy(orc):
         assert host(g).tobytes() == w.tobytes()
 
 
+@pytest.mark.parametrize("hq,bs", [(16, 16), (32, 32)])
+def test_int4_window_head_columns(hq, bs, orc):
+    """Windowed decode with eight or sixteen query heads per KV head (one head
+    per column), windows cutting tiles and partitions mid-way."""
+    hkv, d = 2, 128
+    ctx = [40, 300, 1029, 2100]
+    shape, lay, case = make("f16", hq, hkv, d, bs, ctx, seed=8, spare_blocks=2)
+    src_k = case.k_cache.nan_to_num(0.0).to(dev())
+    src_v = case.v_cache.nan_to_num(0.0).to(dev())
+    kq, vq, ks, vs = quantize_all_gpu(src_k, src_v)
+    okq, ovq, oks, ovs = quantize_all_oracle(src_k, src_v)
+    q, bt, ctx_t = to_dev(case.q, lay.block_tables, lay.context_lens)
+    for window in (7, 100, 1000):
+        print(f"int4 window hq={hq} bs={bs} window={window}", flush=True)
+        out = torch.empty_like(q)
+        pa.paged_decode_attention_window(q, kq, vq, bt, ctx_t, shape.scale, window, out, ks, vs,
+                                         int4=True)
+        torch.cuda.synchronize()
+        ref = oracle.paged_decode_attention_window(host(case.q), okq, ovq,
+                                                   host(lay.block_tables), host(lay.context_lens),
+                                                   shape.scale, window, k_scale=oks, v_scale=ovs,
+                                                   int4=True, lib=orc)
+        assert torch.isfinite(out).all()
+        assert max_abs_err(out, ref) <= TOL_I4, window
+
+
 def test_int4_full_size_sampled(orc):
     """Llama-3-8B layer, 32 sequences x 8192 positions in int4, the library's
     own plan, on sampled (sequence, head) rows."""
@@ -173,6 +201,33 @@ def test_int4_full_size_sampled(orc):
     rng = np.random.default_rng(7)
     seqs = [0, 13, 31]
     pairs = [(s_, int(rng.integers(32))) for s_ in seqs for _ in range(4)]
+    used = lay.block_tables[seqs].flatten()
+    okq, ovq, oks, ovs = quantize_all_oracle(case.k_cache, case.v_cache,
+                                             used[used >= 0].tolist())
+    ref = oracle.paged_decode_attention(host(case.q), okq, ovq, host(lay.block_tables),
+                                        host(lay.context_lens), shape.scale, k_scale=oks,
+                                        v_scale=ovs, pairs=pairs, int4=True, num_threads=8,
+                                        lib=orc)
+    assert torch.isfinite(out).all()
+    assert max_abs_err(out, ref, pairs) <= TOL_I4
+
+
+def test_int4_full_size_head_columns_sampled(orc):
+    """Llama-3-70B layer (64 query / 8 KV heads), 16 sequences x 8192
+    positions in int4: the one-head-per-column kernel under the library's own
+    plan, on sampled (sequence, head) rows."""
+    shape = W.Shape("llama3-70b-int4kv-test", "f16", 16, 64, 8, 128, 16)
+    lay = W.carve_layout([8192] * 16, 16, num_blocks=16 * 512, seed=3)
+    case = W.make_case(shape, lay, device=dev(), poison=False)
+    print("int4 full size, head columns", flush=True)
+    kq, vq, ks, vs = quantize_all_gpu(case.k_cache, case.v_cache)
+    bt, ctx = lay.block_tables.to(dev()), lay.context_lens.to(dev())
+    out = torch.empty_like(case.q)
+    pa.paged_decode_attention_int4(case.q, kq, vq, ks, vs, bt, ctx, shape.scale, out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    seqs = [0, 15]
+    pairs = [(s_, int(rng.integers(64))) for s_ in seqs for _ in range(4)]
     used = lay.block_tables[seqs].flatten()
     okq, ovq, oks, ovs = quantize_all_oracle(case.k_cache, case.v_cache,
                                              used[used >= 0].tolist())

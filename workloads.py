@@ -81,6 +81,10 @@ LLAMA3_8B_I4 = Shape("llama3-8b-int4kv", "i4", 64, 32, 8, 128, 16,
                      description="Llama-3-8B layer, int4 KV + fp16 scales per 32 dims, "
                                  "64 seqs x 8192")
 
+LLAMA3_70B_I4 = Shape("llama3-70b-int4kv", "i4", 32, 64, 8, 128, 16, layers=4,
+                      description="Llama-3-70B layer (64 q / 8 KV heads), int4 KV + fp16 scales "
+                                  "per 32 dims, 32 seqs x 8192, 4 layers")
+
 # the headline layer with blocks of 32, in bf16, and with an int8 cache (one
 # query head per KV head: the vector-ALU kernel)
 LLAMA2_7B_BS32 = Shape("llama2-7b-f16-bs32", "f16", 16, 32, 32, 128, 32, layers=8,
@@ -93,7 +97,7 @@ LLAMA2_7B_I8 = Shape("llama2-7b-int8kv", "i8", 16, 32, 32, 128, 16, layers=8,
 
 SHAPES = {s.name: s for s in (TINY, LLAMA3_8B, LLAMA2_7B, LLAMA2_70B, LLAMA3_8B_I8,
                               LLAMA3_8B_FP8, LLAMA3_8B_WINDOW, LLAMA3_8B_I4, LLAMA2_7B_BS32,
-                              LLAMA2_7B_BF16, LLAMA2_7B_I8)}
+                              LLAMA2_7B_BF16, LLAMA2_7B_I8, LLAMA3_70B_I4)}
 
 TINY_POOL_BLOCKS = 64
 PREFIX_GROUP = 8          # sequences per shared-prefix group (Llama-2-70B workload)
@@ -113,7 +117,8 @@ def context_lengths(shape: Shape) -> list[int]:
     if shape.name in (LLAMA3_8B.name, LLAMA2_7B.name, LLAMA2_7B_BS32.name, LLAMA2_7B_BF16.name,
                       LLAMA2_7B_I8.name):
         return [4096] * shape.num_seqs
-    if shape.name in (LLAMA3_8B_I8.name, LLAMA3_8B_FP8.name, LLAMA3_8B_I4.name):
+    if shape.name in (LLAMA3_8B_I8.name, LLAMA3_8B_FP8.name, LLAMA3_8B_I4.name,
+                      LLAMA3_70B_I4.name):
         return [8192] * shape.num_seqs
     if shape.name == LLAMA3_8B_WINDOW.name:
         return [16384] * shape.num_seqs
