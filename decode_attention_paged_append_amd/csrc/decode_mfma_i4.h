@@ -25,7 +25,9 @@
 //    rounded to fp16 like the weights of the 16-bit caches.  Lane (g, n)'s
 //    rows are dims 8(4g+i)+e, all in group g, so the lanes with n / 4 == g
 //    hold the result: 2^24 * O^T - 8 * (column sum of B), the column sums
-//    kept beside the running sums.
+//    kept beside the running sums.  Odd dims enter as 16 * code (the high
+//    nibble masked in place, no shift), and their rows drop the 16 with the
+//    2^24.
 //  * Four heads per column set; the score MFMA repeats each head's query in
 //    all four groups of columns, so every lane already holds the weights of
 //    its column's head (its softmax runs four times over, in lanes that would
@@ -239,11 +241,12 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     // ---- value A operands: dim 8n+e of tokens 4g..4g+3 (shared by the sets)
     u32x2 va[VE];
     {
+      // odd dims (odd e) as 16 x code: high nibbles masked in place
       uint32_t lo[4], hi[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         lo[j] = raw.v[j] & kNibbles;
-        hi[j] = (raw.v[j] >> 4) & kNibbles;
+        hi[j] = raw.v[j] & (kNibbles << 4);
       }
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
@@ -298,8 +301,11 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
         corr[cs] *= alpha;
       }
       // ---- values: B = p * value scale of column n's group, fp16
-      const u32x2 pb = {Mfma<Fmt::F16>::pack(pw[0] * f16_lo(raw.vs[0]), pw[1] * f16_hi(raw.vs[0])),
-                        Mfma<Fmt::F16>::pack(pw[2] * f16_lo(raw.vs[1]), pw[3] * f16_hi(raw.vs[1]))};
+      // p * scale as one mixed-precision FMA each (fp16 scale, fp32 product)
+      const u32x2 pb = {Mfma<Fmt::F16>::pack(fmaf(pw[0], f16_lo(raw.vs[0]), 0.0f),
+                                             fmaf(pw[1], f16_hi(raw.vs[0]), 0.0f)),
+                        Mfma<Fmt::F16>::pack(fmaf(pw[2], f16_lo(raw.vs[1]), 0.0f),
+                                             fmaf(pw[3], f16_hi(raw.vs[1]), 0.0f))};
       corr[cs] = Mfma<Fmt::F16>::sum2(pb[1], Mfma<Fmt::F16>::sum2(pb[0], corr[cs]));
 #pragma unroll
       for (int e = 0; e < VE; ++e) o[cs][e] = Mfma<Fmt::F16>::pv(va[e], pb, o[cs][e]);
@@ -352,9 +358,10 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
       const int hh = 4 * cs + (n & 3);
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
+        const float f = (e & 1) ? kTwo24 / 16.0f : kTwo24;  // odd e: 16 x code
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          s_acc[hh * D + 32 * g + 8 * i + e] = fmaf(o[cs][e][i], kTwo24, -8.0f * corr[cs]);
+          s_acc[hh * D + 32 * g + 8 * i + e] = fmaf(o[cs][e][i], f, -8.0f * corr[cs]);
       }
     }
   }
@@ -400,7 +407,9 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
 //    value MFMA e are dims 16e .. 16e+15, which no lane's 16-byte load holds
 //    for four tokens at once: V goes through a per-wave LDS tile as the same
 //    subnormal codes as K, and transposing reads (ds_read_b64_tr_b16) give
-//    lane (g, n) dim 16e + n of tokens 4g .. 4g+3.
+//    lane (g, n) dim 16e + n of tokens 4g .. 4g+3.  Odd dims enter as
+//    16 * code, the high nibble masked in place (one instruction fewer per
+//    word); their output rows drop the 16 with the 2^24.
 //  * S^T comes out with lane (g, n) holding tokens 4g .. 4g+3 of head n,
 //    which is the B operand layout: the weights never move, and the running
 //    max, sum and column sums of B are per lane.  Lane (g, n) ends with dims
@@ -568,8 +577,10 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
         ktile[r * CHUNKS + ((c0 + w) ^ (r % CHUNKS))] =
             u32x4{__builtin_amdgcn_perm(khi, klo, i4_sel(0)), __builtin_amdgcn_perm(khi, klo, i4_sel(1)),
                   __builtin_amdgcn_perm(khi, klo, i4_sel(2)), __builtin_amdgcn_perm(khi, klo, i4_sel(3))};
+        // V: odd dims as 16 x code (high nibbles masked in place), taken out
+        // again with the 2^24 of the epilogue
         const uint32_t xv = raw.v[w];
-        const uint32_t vlo = xv & kNibbles, vhi = (xv >> 4) & kNibbles;
+        const uint32_t vlo = xv & kNibbles, vhi = xv & (kNibbles << 4);
         vtile[r * CHUNKS + ((c0 + w) ^ (r & 7))] =
             u32x4{__builtin_amdgcn_perm(vhi, vlo, i4_sel(0)), __builtin_amdgcn_perm(vhi, vlo, i4_sel(1)),
                   __builtin_amdgcn_perm(vhi, vlo, i4_sel(2)), __builtin_amdgcn_perm(vhi, vlo, i4_sel(3))};
@@ -646,12 +657,12 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     const int vq = n & 3;
 #pragma unroll
     for (int c = 0; c < KG; ++c) {
-      auto vsc = [&](int i) {
+      // p * scale as one mixed-precision FMA (fp16 scale, fp32 product)
+      auto wt = [&](int i) {
         const uint32_t w = vs[(i * KG + c) >> 1];
-        return (c & 1) ? f16_hi(w) : f16_lo(w);
+        return fmaf(pw[i], (c & 1) ? f16_hi(w) : f16_lo(w), 0.0f);
       };
-      const u32x2 pb = {Mfma<Fmt::F16>::pack(pw[0] * vsc(0), pw[1] * vsc(1)),
-                        Mfma<Fmt::F16>::pack(pw[2] * vsc(2), pw[3] * vsc(3))};
+      const u32x2 pb = {Mfma<Fmt::F16>::pack(wt(0), wt(1)), Mfma<Fmt::F16>::pack(wt(2), wt(3))};
       corr[c] = Mfma<Fmt::F16>::sum2(pb[1], Mfma<Fmt::F16>::sum2(pb[0], corr[c]));
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -705,12 +716,13 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   __syncthreads();  // every wave is done with its tile region
   float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][ACC_STRIDE]
   if (n < GC) {
+    constexpr float kOdd = kTwo24 / 16.0f;  // rows of odd dims hold 16 x code
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       const float b = -8.0f * corr[e / 2];
       *(f32x4*)(s_acc + n * ACC_STRIDE + 16 * e + 4 * g) =
-          f32x4{fmaf(o[e][0], kTwo24, b), fmaf(o[e][1], kTwo24, b), fmaf(o[e][2], kTwo24, b),
-                fmaf(o[e][3], kTwo24, b)};
+          f32x4{fmaf(o[e][0], kTwo24, b), fmaf(o[e][1], kOdd, b), fmaf(o[e][2], kTwo24, b),
+                fmaf(o[e][3], kOdd, b)};
     }
     if (g == 0) {
       s_ml[wave][n][0] = m;
