@@ -25,6 +25,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -236,15 +238,17 @@ def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
                       f"{dt:.1f} s on {threads} threads"}
 
 
-def traffic_block(io_bytes: int):
+def traffic_block(workload: str, default_launch: bool):
     """HBM bytes per launch measured with rocprofv3 counters, if they were taken
-    on the current kernel sources (else null)."""
+    on this workload's default launch and the current kernel sources (else
+    null)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_hash():
+    if (not default_launch or t.get("bench_workload") != workload
+            or t.get("kernel_source_sha256") != kernel_source_hash()):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -495,6 +499,17 @@ def attention_launch_ms(b, layers, steps):
     return k0.elapsed_time(k1) / (steps * layers), how
 
 
+def unique_bytes_report(b, layers, ms_step, kv_step) -> dict:
+    """For a pool whose blocks are shared between tables (a common prefix):
+    the distinct bytes a step reads, and the rate on those alone."""
+    if b.window or int(b.layout.owners.max()) <= 1:
+        return {}
+    uniq = W.unique_kv_bytes_per_layer_step(b.shape, b.layout) * layers
+    return {"unique_kv_bytes_per_step": uniq,
+            "unique_GBps": round(uniq / (ms_step / 1e3) / 1e9, 2),
+            "unique_fraction_of_logical": round(uniq / kv_step, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -554,15 +569,17 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: K whole steps, bracketed by events on torch's current
-    # stream, which is the stream the binding hands to every launch.
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # stream, which is the stream the binding hands to every launch; an event
+    # after every step gives the spread of single steps.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         b.step()
-    end.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
 
     kernel_ms, kernel_timing = attention_launch_ms(b, layers, args.steps)
 
@@ -578,6 +595,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": {"median": round(float(np.median(per_step)), 4),
+                    "p10": round(float(np.percentile(per_step, 10)), 4),
+                    "p90": round(float(np.percentile(per_step, 90)), 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -600,6 +620,7 @@ def main():
                {"partition_tokens": b.part, "partitions": b.nparts}),
         },
         "seq_steps_per_s": round(shape.num_seqs * 1e3 / ms_step, 2),
+        **unique_bytes_report(b, layers, ms_step, kv_step),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": kv_step,
         "roofline": {
@@ -612,7 +633,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_block(io),
+            "traffic": traffic_block(shape.name, not (args.separate or args.partition_tokens)),
             "bytes_per_launch": io,
             "avg_launch_ms": round(kernel_ms, 5),
             "timing": kernel_timing,

@@ -280,6 +280,20 @@ def to_numpy_bits(t: torch.Tensor):
     return t.numpy()
 
 
+def unique_kv_bytes_per_layer_step(shape: Shape, layout: "Layout") -> int:
+    """K+V bytes of the distinct pool rows one decode step of one layer reads:
+    a block named by several tables counts once, with the most rows any of
+    them uses (no window)."""
+    rows = {}
+    bs = layout.block_size
+    for s, c in enumerate(layout.context_lens.tolist()):
+        for j in range(blocks_needed(int(c), bs)):
+            phys = int(layout.block_tables[s, j])
+            rows[phys] = max(rows.get(phys, 0), min(bs, int(c) - j * bs))
+    n = sum(rows.values())
+    return kv_bytes_per_layer_step(dataclasses.replace(shape, window=0), [n])
+
+
 def kv_bytes_per_layer_step(shape: Shape, ctx_lens) -> int:
     """Logical K+V bytes one decode step of one layer reads (every sequence reads
     its whole context, shared blocks included, or its last `window` positions),
