@@ -231,11 +231,41 @@ def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
         if time.perf_counter() - t0 >= min_seconds:
             break
     dt = time.perf_counter() - t0
+    # one thread over every head of sequence 0 (at least 3 s)
+    pairs = [(0, h) for h in range(b.shape.num_q_heads)]
+    one = W.kv_bytes_per_layer_step(b.shape, [int(lay.context_lens[0])])
+    reps1, t1 = 0, time.perf_counter()
+    while True:
+        if b.window:
+            oracle.paged_decode_attention_window(q, kc, vc, bt, ctx, b.shape.scale, b.window,
+                                                 pairs=pairs, num_threads=1, **args)
+        else:
+            oracle.paged_decode_attention(q, kc, vc, bt, ctx, b.shape.scale, pairs=pairs,
+                                          num_threads=1, **args)
+        reps1 += 1
+        if time.perf_counter() - t1 >= 3.0:
+            break
+    dt1 = time.perf_counter() - t1
     return {"value": round(b.kv_bytes_per_layer() * reps / dt / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": f"layer 0 of {b.layers}: all {b.shape.num_seqs} seqs x "
                       f"{b.shape.num_q_heads} heads, fp64 oracle run {reps} time(s) in "
-                      f"{dt:.1f} s on {threads} threads"}
+                      f"{dt:.1f} s on {threads} threads",
+            "single_thread": {"value": round(one * reps1 / dt1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"layer 0, sequence 0 (all {b.shape.num_q_heads} "
+                                        f"heads), {reps1} time(s) in {dt1:.1f} s"},
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def traffic_block(workload: str, default_launch: bool):
