@@ -215,7 +215,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   struct Raw {
     u32x4 k[K_LOADS];
     uint32_t v[4][VW / 4];
-    float ks[4], vs[4];
+    uint32_t ks[2], vs[2];  // fp16 scales of tokens 4g..4g+3 (quantized caches)
     int nvalid;  // rows of the tile inside the partition
     int nlow;    // rows below this one are before the window
   };
@@ -269,22 +269,22 @@ void decode_mfma_kernel(const DecodeParams p) {
         vraw[j][0] = valid ? __builtin_nontemporal_load((const uint32_t*)src) : 0u;
       }
     }
-    float* const ksc = raw.ks;
-    float* const vsc = raw.vs;
     if constexpr (kQuant) {
-      // scales of tokens 4g..4g+3: 8 contiguous bytes
+      // scales of tokens 4g..4g+3: 8 contiguous bytes, kept as fp16 pairs
       const size_t srow = row0 + 4 * g;
       const bool any = !PARTIAL || (4 * g < nvalid && 4 * g + 3 >= nlow);
       const u32x2 kw = any ? *(const u32x2*)(p.k_scale + srow) : u32x2{0, 0};
       const u32x2 vw = any ? *(const u32x2*)(p.v_scale + srow) : u32x2{0, 0};
-      ksc[0] = f16_lo(kw[0]); ksc[1] = f16_hi(kw[0]);
-      ksc[2] = f16_lo(kw[1]); ksc[3] = f16_hi(kw[1]);
-      vsc[0] = f16_lo(vw[0]); vsc[1] = f16_hi(vw[0]);
-      vsc[2] = f16_lo(vw[1]); vsc[3] = f16_hi(vw[1]);
+      raw.ks[0] = kw[0]; raw.ks[1] = kw[1];
+      raw.vs[0] = vw[0]; raw.vs[1] = vw[1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // rows outside [nlow, nvalid) never contribute (their weight is 0)
-        if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) ksc[i] = vsc[i] = 0.0f;
+        if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) {
+          const uint32_t keep = (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          raw.ks[i >> 1] &= keep;
+          raw.vs[i >> 1] &= keep;
+        }
       }
     }
     return raw;
@@ -296,8 +296,8 @@ void decode_mfma_kernel(const DecodeParams p) {
     const int nlow = raw.nlow;
     const u32x4* const kraw = raw.k;
     const uint32_t (*const vraw)[VW / 4] = raw.v;
-    const float* const ksc = raw.ks;
-    const float* const vsc = raw.vs;
+    // scale of token 4g+i as the f16 operand of a v_fma_mix
+    auto scale_of = [](const uint32_t* w, int i) { return (i & 1) ? f16_hi(w[i >> 1]) : f16_lo(w[i >> 1]); };
 
     // ---- K tile -> LDS (fp16/bf16 halves), chunk c of row r at c ^ (r % CHUNKS)
 #pragma unroll
@@ -329,7 +329,8 @@ void decode_mfma_kernel(const DecodeParams p) {
     float z[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = kQuant ? sacc[i] * (ksc[i] * (p.scale_log2 * zs)) : sacc[i] * p.scale_log2;
+      z[i] = kQuant ? fmaf(sacc[i], scale_of(raw.ks, i), 0.0f) * (p.scale_log2 * zs)
+                    : sacc[i] * p.scale_log2;
       if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) z[i] = -__builtin_inff();
     }
     float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -356,7 +357,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
     if constexpr (kQuant) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] *= vsc[i];
+      for (int i = 0; i < 4; ++i) pw[i] = fmaf(pw[i], scale_of(raw.vs, i), 0.0f);
     }
     const u32x2 pb = {MM::pack(pw[0], pw[1]), MM::pack(pw[2], pw[3])};
     if constexpr (kBias) corr = MM::sum2(pb[1], MM::sum2(pb[0], corr));
