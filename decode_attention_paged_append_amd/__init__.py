@@ -22,7 +22,7 @@ __all__ = [
     "paged_decode_attention", "paged_decode_attention_int8", "decode_step", "decode_partitions",
     "kv_append_fp8", "paged_decode_attention_fp8", "kv_append_int4",
     "paged_decode_attention_int4", "int4_desc",
-    "decode_step_partitions", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
+    "decode_step_partitions", "decode_step_quant", "decode_step_partitions_quant", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
     "hbm_read_probe",
     "BlockManager", "copy_blocks", "paged_prefill_attention", "paged_decode_attention_window",
     "decode_window_workspace_bytes",
@@ -97,6 +97,9 @@ def _declare(lib):
         "pa_decode_step": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
         "pa_decode_step_partitions": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D, P, sz,
                                       P],
+        "pa_decode_step_quant": [P, P, P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
+        "pa_decode_step_partitions_quant": [P, P, P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P,
+                                            D, P, sz, P],
         "pa_gather_kv": [P, P, P, P, P, i32, P, i32, P, P, P, P, D, P],
         "pa_copy_blocks": [P, P, P, P, P, i32, D, P],
         "pa_hbm_read_probe": [P, sz, P, P, P],
@@ -444,6 +447,56 @@ def decode_step_partitions(q, k_new, v_new, k_cache, v_cache, block_tables, cont
         int(partition_tokens), _dev(out, "out", k_cache.dtype), ctypes.byref(desc),
         _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel(), _stream(q)),
         lib)
+    return out
+
+
+def _quant_step_args(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     context_lens, out, int4):
+    """Shared checks of the quantized decode-step calls: the cache descriptor,
+    (S, Hq, max_blocks) and the marshalled tensor pointers up to context_lens."""
+    desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
+    if desc.dtype not in (DTYPE_CODE[torch.int8], DTYPE_CODE[torch.float8_e4m3fn], INT4):
+        raise ValueError("a quantized decode step needs an int8, fp8 or int4 cache")
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out, int4)
+    if k_new.shape != (s, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{s}, {desc.num_kv_heads}, {desc.head_dim}]")
+    ptrs = (_dev(q, "q", torch.float16, 3), _dev(k_new, "k_new", torch.float16),
+            _dev(v_new, "v_new", torch.float16), _dev(k_cache, "k_cache", ndim=4),
+            _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(k_scale, "k_scale", torch.float16),
+            _dev(v_scale, "v_scale", torch.float16),
+            _dev(block_tables, "block_tables", torch.int32), maxb,
+            _dev(context_lens, "context_lens", torch.int32), s, hq)
+    return desc, s, hq, maxb, ptrs
+
+
+def decode_step_quant(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                      context_lens, scale, out, workspace=None, int4=False):
+    """One decode step over a quantized cache: quantize each sequence's fp16
+    k_new/v_new [S, Hkv, D] rows into codes and scales at position
+    context_lens[s]-1 inside the attention launch, then attend over all
+    context_lens[s] rows (see pa_decode_step_quant).  int4: uint8 pools
+    [NB, Hkv, BS, D/2] hold int4 codes."""
+    lib = library()
+    desc, s, hq, maxb, ptrs = _quant_step_args(q, k_new, v_new, k_cache, v_cache, k_scale,
+                                               v_scale, block_tables, context_lens, out, int4)
+    ws = _workspace(workspace, decode_workspace_bytes(desc, s, hq, maxb), q.device)
+    _ok(lib.pa_decode_step_quant(*ptrs, float(scale), _dev(out, "out", torch.float16),
+                                 ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+                                 _stream(q)), lib)
+    return out
+
+
+def decode_step_partitions_quant(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                                 block_tables, context_lens, scale, out, partition_tokens,
+                                 workspace, int4=False):
+    """Phase 1 of decode_step_quant with an explicit partition length."""
+    lib = library()
+    desc, _, _, _, ptrs = _quant_step_args(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                                           block_tables, context_lens, out, int4)
+    _ok(lib.pa_decode_step_partitions_quant(
+        *ptrs, float(scale), int(partition_tokens), _dev(out, "out", torch.float16),
+        ctypes.byref(desc), _dev(workspace, "workspace"),
+        0 if workspace is None else workspace.numel(), _stream(q)), lib)
     return out
 
 

@@ -416,6 +416,45 @@ pa_status pa_decode_step_partitions(const void* q, const void* k_new, const void
                         workspace_bytes, (hipStream_t)stream, k_new, v_new);
 }
 
+pa_status pa_decode_step_quant(const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, float scale, void* out,
+                               const pa_cache_desc* cache, void* workspace,
+                               size_t workspace_bytes, pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (!quantized(cache->dtype))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_step_quant needs an int8, fp8 or int4 cache");
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
+  return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
+                       workspace_bytes, (hipStream_t)stream, cache->dtype, k_new, v_new);
+}
+
+pa_status pa_decode_step_partitions_quant(const void* q, const void* k_new, const void* v_new,
+                                          void* k_cache, void* v_cache, void* k_scale,
+                                          void* v_scale, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, float scale,
+                                          int32_t partition_tokens, void* out,
+                                          const pa_cache_desc* cache, void* workspace,
+                                          size_t workspace_bytes, pa_stream_t stream) {
+  Plan plan;
+  pa_status st = make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan);
+  if (st != PA_OK) return st;
+  if (!quantized(cache->dtype))
+    return fail(PA_ERR_UNSUPPORTED,
+                "pa_decode_step_partitions_quant needs an int8, fp8 or int4 cache");
+  if (num_seqs == 0) return PA_OK;
+  if (!k_new || !v_new) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
+  return run_partitions(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                        context_lens, num_seqs, num_q_heads, scale, out, cache, plan, workspace,
+                        workspace_bytes, (hipStream_t)stream, k_new, v_new);
+}
+
 pa_status pa_lse_merge(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
                        int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                        int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_tokens,

@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "device.h"
+#include "quant.h"
 
 namespace pa {
 
@@ -133,6 +134,53 @@ __device__ __forceinline__ void append_new_rows(const DecodeParams& p, const int
   }
   __threadfence_block();
   __syncthreads();
+}
+
+// Fused append into a quantized cache (int8, fp8, int4): the new rows come
+// as fp16 [S][Hkv][D].  Wave 0 quantizes them, K on lanes [0, D/8) and V on
+// lanes [D/8, D/4), 8 dims a lane, with the quantizer of the standalone
+// quantizing append, and stores codes and scales at the token's slot; then
+// the same workgroup-wide release as above.
+template <Fmt F, int D, int BS>
+__device__ __forceinline__ void append_new_rows_quant(const DecodeParams& p,
+                                                      const int32_t* table, int s, int kvh,
+                                                      int pos) {
+  constexpr int KIND = quant_kind<F>();
+  constexpr int LQ = D / 8;
+  constexpr int LG = KIND == kQuantI4 ? kInt4Group / 8 : LQ;
+  static_assert(2 * LQ <= kWave, "K and V rows must fit one wave");
+  if (threadIdx.x < kWave) {  // wave 0: every lane takes part in the absmax
+    const int lane = threadIdx.x;
+    const bool is_v = lane >= LQ;
+    const int c = lane % LQ;
+    const int bid = table[pos / BS];
+    const bool store = lane < 2 * LQ && (unsigned)bid < (unsigned)p.num_blocks;
+    u32x4 x = {0, 0, 0, 0};
+    if (store)
+      x = load16((const char*)(is_v ? p.v_new : p.k_new) +
+                 (((size_t)s * p.num_kv_heads + kvh) * D + 8 * c) * 2);
+    uint32_t packed[2];
+    const uint16_t sbits = quantize_piece<KIND, LG>(x, packed);
+    if (store) {
+      const size_t dst_row = ((size_t)bid * p.num_kv_heads + kvh) * BS + pos % BS;
+      store_quant_piece<KIND, D>((uint8_t*)(is_v ? p.v_cache : p.k_cache),
+                                 (uint16_t*)(is_v ? p.v_scale : p.k_scale), dst_row, c,
+                                 packed, sbits);
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+}
+
+// The fused append of the decoded token at position pos, in the cache's
+// format.  NT: threads of the workgroup.
+template <Fmt F, int D, int BS, int NT>
+__device__ __forceinline__ void append_new_token(const DecodeParams& p, const int32_t* table,
+                                                 int s, int kvh, int pos) {
+  if constexpr (FmtInfo<F>::quantized)
+    append_new_rows_quant<F, D, BS>(p, table, s, kvh, pos);
+  else
+    append_new_rows<D * FmtInfo<F>::bytes, BS, NT>(p, table, s, kvh, pos);
 }
 
 // Per-format fragment arithmetic.  A fragment is 16 bytes of cache data.
@@ -401,8 +449,8 @@ void decode_partition_kernel(const DecodeParams p) {
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
   // Fused append: the decoded token (position ctx-1) is this partition's last
   // row when tok_end == ctx.
-  if (!kQuant && p.k_new != nullptr && tok_end == ctx)
-    append_new_rows<ROWB, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
+  if (p.k_new != nullptr && tok_end == ctx)
+    append_new_token<F, D, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
 
   const int lrow = lane / LR;  // row of this lane inside a wave-load
   const int lcol = lane % LR;  // 16-byte column of this lane inside a row

@@ -163,8 +163,8 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
   // Fused append: the decoded token (position ctx-1) is this partition's last
   // row when tok_end == ctx.
-  if (!kQuant && p.k_new != nullptr && tok_end == ctx)
-    append_new_rows<ROWB, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
+  if (p.k_new != nullptr && tok_end == ctx)
+    append_new_token<F, D, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
 
   // B operand of the score product: Q^T, lane (g, n) holds head n's dims
   // 32c + 8g .. +8 (zero for padding heads).

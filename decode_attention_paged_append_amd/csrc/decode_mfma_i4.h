@@ -108,6 +108,10 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   const int t_first = (max(tok0, start) - tok0) / TT;
   const bool low_cut = start > tok0 + t_first * TT;
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
+  // Fused append: the decoded token (position ctx-1) is this partition's last
+  // row when tok_end == ctx.
+  if (p.k_new != nullptr && tok_end == ctx)
+    append_new_token<Fmt::I4, D, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
 
   // Query of column n's head (4 sigma + n % 4), dims 32c + 8g .. +8: the B
   // operand of score MFMA c; the accumulator start removes the code bias.
@@ -469,6 +473,10 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   const int t_first = (max(tok0, start) - tok0) / TT;
   const bool low_cut = start > tok0 + t_first * TT;
   const int32_t* __restrict__ table = p.block_tables + (size_t)s * p.max_blocks;
+  // Fused append: the decoded token (position ctx-1) is this partition's last
+  // row when tok_end == ctx.
+  if (p.k_new != nullptr && tok_end == ctx)
+    append_new_token<Fmt::I4, D, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
 
   // Query of column n's head, dims 32c + 8g .. +8: the B operand of score
   // MFMA c; the accumulator start removes the code bias.

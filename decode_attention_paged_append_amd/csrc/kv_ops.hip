@@ -10,6 +10,7 @@
 #include <algorithm>
 
 #include "kv_ops.h"
+#include "quant.h"
 
 namespace pa {
 
@@ -72,35 +73,10 @@ __global__ void kv_append_kernel(const u32x4* __restrict__ k_new, const u32x4* _
   v_cache[dst] = v_new[i];
 }
 
-// OCP E4M3 code of r: nearest value, ties to even, magnitudes above 448
-// saturate, NaN gives 0.  Exponent e = floor(log2 |r|) from the float's bits;
-// from 2^-6 up the code is (e + 7) * 8 + (q - 8) with q = rint(|r| * 2^(3-e))
-// in [8, 16] (q = 16 carries into the next exponent); below 2^-6 the step is
-// 2^-9 and the code is rint(|r| * 2^9), whose 8 is again the smallest normal.
-__device__ __forceinline__ uint32_t e4m3_code(float r) {
-  if (r != r) return 0u;
-  const float a = fminf(fabsf(r), 448.0f);
-  const int e = (int)((float_to_bits(a) >> 23) & 0xffu) - 127;
-  uint32_t code;
-  if (e < -6) {
-    code = (uint32_t)rintf(a * 512.0f);
-  } else {
-    const float q = rintf(a * bits_to_float((uint32_t)(127 + 3 - e) << 23));
-    code = (uint32_t)((e + 7) * 8) + (uint32_t)q - 8u;
-  }
-  return code | (r < 0.0f && code != 0u ? 0x80u : 0u);
-}
-
 // Quantizing append.  LQ = D/8 lanes hold one (token, head) row of fp16
-// values, 8 each.  KIND 0: int8, 1: fp8 (E4M3), both with one fp16 scale per
-// row; KIND 2: int4, with one scale per group of kInt4Group dims (the 4
-// lanes of the group).  Over the row (int4: the group):
-//   a = max |x| (exact);  s = fp16(a / R) (IEEE fp32 divide, round to nearest
-//   even), R = 127, 448 or 7;
-//   int8: code = clamp(rint(x / s), -127, 127);  fp8: code = E4M3(x / s);
-//   int4: code = clamp(rint(x / s), -7, 7), stored as the nibble code + 8
-//   (dim 2i low, 2i + 1 high in byte i);
-//   codes are 0 when s == 0 (and for a NaN input).
+// values, 8 each; the quantizer and its reading of the pages are in quant.h
+// (KIND 0: int8, 1: fp8 E4M3, both with one fp16 scale per row; KIND 2: int4,
+// with one scale per group of kInt4Group dims, the 4 lanes of the group).
 template <int D, int KIND>
 __global__ __launch_bounds__(256) void kv_append_quant_kernel(
     const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
@@ -108,9 +84,7 @@ __global__ __launch_bounds__(256) void kv_append_quant_kernel(
     uint8_t* __restrict__ v_cache, uint16_t* __restrict__ k_scale, uint16_t* __restrict__ v_scale,
     int32_t num_kv_heads, int32_t block_size, int64_t pool_slots) {
   constexpr int LQ = D / 8;  // lanes per row
-  constexpr bool kInt4 = KIND == 2;
-  constexpr int LG = kInt4 ? kInt4Group / 8 : LQ;  // lanes sharing a scale
-  constexpr float R = KIND == 1 ? 448.0f : KIND == 2 ? 7.0f : 127.0f;
+  constexpr int LG = KIND == kQuantI4 ? kInt4Group / 8 : LQ;  // lanes sharing a scale
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / LQ;        // (token, head) row
   const int c = (int)(gid % LQ);       // 8-value piece of the row
@@ -120,62 +94,22 @@ __global__ __launch_bounds__(256) void kv_append_quant_kernel(
   const int64_t slot = live ? slots[t] : -1;
   const bool store = live && slot >= 0 && slot < pool_slots;
   // Rows are whole lane groups, so a group shares 'store'; every lane still
-  // takes part in the reductions below.
+  // takes part in the reductions.
   u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
   if (store) {
     kx = k_new[row * LQ + c];
     vx = v_new[row * LQ + c];
   }
-  auto quantize = [&](u32x4 x, uint8_t* cache, uint16_t* scales) {
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = f16_lo(x[i]);
-      f[2 * i + 1] = f16_hi(x[i]);
-    }
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
-    a = group_max<LG>(a);
-    const _Float16 s16 = (_Float16)(a / R);
-    const float s = (float)s16;
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t code = 0u;
-      if constexpr (KIND == 1) {
-        if (s != 0.0f) code = e4m3_code(f[i] / s);
-        packed[i / 4] |= code << (8 * (i % 4));
-      } else {
-        const float lim = kInt4 ? 7.0f : 127.0f;
-        float r = 0.0f;
-        if (s != 0.0f) {
-          r = rintf(f[i] / s);
-          r = r != r ? 0.0f : fminf(fmaxf(r, -lim), lim);
-        }
-        if constexpr (kInt4) {
-          packed[0] |= ((uint32_t)((int32_t)r + 8) & 0xfu) << (4 * i);
-        } else {
-          packed[i / 4] |= ((uint32_t)(int32_t)r & 0xffu) << (8 * (i % 4));
-        }
-      }
-    }
-    if (store) {
-      const int64_t block = slot / block_size;
-      const int64_t off = slot - block * block_size;
-      const int64_t dst_row = (block * num_kv_heads + h) * block_size + off;
-      if constexpr (kInt4) {
-        ((uint32_t*)cache)[dst_row * LQ + c] = packed[0];  // D/2 bytes per row
-        if (c % LG == 0)
-          scales[dst_row * (D / kInt4Group) + c / LG] = __builtin_bit_cast(uint16_t, s16);
-      } else {
-        ((u32x2*)cache)[dst_row * LQ + c] = u32x2{packed[0], packed[1]};
-        if (c == 0) scales[dst_row] = __builtin_bit_cast(uint16_t, s16);
-      }
-    }
-  };
-  quantize(kx, k_cache, k_scale);
-  quantize(vx, v_cache, v_scale);
+  uint32_t kp[2], vp[2];
+  const uint16_t ks = quantize_piece<KIND, LG>(kx, kp);
+  const uint16_t vs = quantize_piece<KIND, LG>(vx, vp);
+  if (store) {
+    const int64_t block = slot / block_size;
+    const int64_t off = slot - block * block_size;
+    const size_t dst_row = (size_t)((block * num_kv_heads + h) * block_size + off);
+    store_quant_piece<KIND, D>(k_cache, k_scale, dst_row, c, kp, ks);
+    store_quant_piece<KIND, D>(v_cache, v_scale, dst_row, c, vp, vs);
+  }
 }
 
 // ---------------------------------------------------------------- gather

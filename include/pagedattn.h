@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum {
   PA_F32 = 0,
@@ -294,6 +294,41 @@ pa_status pa_decode_step_partitions(const void* q, const void* k_new, const void
                                     int32_t partition_tokens, void* out,
                                     const pa_cache_desc* cache, void* workspace,
                                     size_t workspace_bytes, pa_stream_t stream);
+
+/* One decode step for a quantized (int8, fp8 or int4) cache: the
+ * quantizing append of pa_kv_append_int8 / _fp8 / _int4 (by cache->dtype) of
+ * each sequence's new K and V rows (k_new, v_new: device fp16 [S][Hkv][D])
+ * at position context_lens[s] - 1, codes to k_cache/v_cache and scales to
+ * k_scale/v_scale in those entry points' layouts, followed by the attention
+ * of pa_paged_decode_attention_int8 / _fp8 / _int4 over all context_lens[s]
+ * rows, the new one included ([notes] steps 2-4 and "Quantized KV cache";
+ * [viz] "What the page leaves out").  As in pa_decode_step, the append
+ * happens inside the attention launch, and a multi-partition plan's merge is
+ * the second launch.  Stores the same codes and scales, bit for bit, as
+ * pa_decode_slot_mapping + the quantizing append, and gives the same output
+ * as the attention call after them.  q, out: device fp16.  Caches and
+ * scales are updated in place; other arguments as for pa_decode_step. */
+pa_status pa_decode_step_quant(const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, float scale, void* out,
+                               const pa_cache_desc* cache, void* workspace,
+                               size_t workspace_bytes, pa_stream_t stream);
+
+/* Phase 1 of pa_decode_step_quant with an explicit partition length (as for
+ * pa_decode_partitions): the quantizing append at context_lens[s] - 1 and the
+ * partitions' attention, in one launch; pa_lse_merge (out_dtype PA_F16)
+ * follows a multi-partition plan. */
+pa_status pa_decode_step_partitions_quant(const void* q, const void* k_new, const void* v_new,
+                                          void* k_cache, void* v_cache, void* k_scale,
+                                          void* v_scale, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, float scale,
+                                          int32_t partition_tokens, void* out,
+                                          const pa_cache_desc* cache, void* workspace,
+                                          size_t workspace_bytes, pa_stream_t stream);
 
 /* Phase 2: log-sum-exp merge of the partitions' partials into out
  * (max M = max_p m_p; out = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p),
