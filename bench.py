@@ -142,6 +142,10 @@ class Bench:
         if self.window:
             pa.paged_decode_attention_window(c.q, c.k_cache, c.v_cache, self.bt, self.ctx,
                                              sh.scale, self.window, out, workspace=self.wws)
+        elif self.fused_append and self.quant:
+            pa.decode_step_partitions_quant(c.q, c.k_new, c.v_new, c.k_cache, c.v_cache,
+                                            c.k_scale, c.v_scale, self.bt, self.ctx, sh.scale,
+                                            out, self.part, self.ws, int4=self.int4)
         elif self.fused_append:
             pa.decode_step_partitions(c.q, c.k_new, c.v_new, c.k_cache, c.v_cache, self.bt,
                                       self.ctx, sh.scale, out, self.part, self.ws)
@@ -152,7 +156,7 @@ class Bench:
 
     @property
     def fused_append(self) -> bool:
-        return self.append and not self.quant and not self.separate and not self.window
+        return self.append and not self.separate and not self.window
 
     def kv_bytes_per_layer(self) -> int:
         return W.kv_bytes_per_layer_step(self.shape, self.layout.context_lens.tolist())
@@ -170,7 +174,14 @@ class Bench:
                      for c, f in zip(self.layout.context_lens, first)) * 4
         new_rows = 0
         if self.fused_append:
-            new_rows = 2 * 2 * sh.num_seqs * sh.num_kv_heads * sh.head_dim * W.ELEM_BYTES[sh.cache_dtype]
+            rows = 2 * sh.num_seqs * sh.num_kv_heads     # K and V rows of the new tokens
+            if self.int4:       # fp16 read, packed codes + group scales written
+                new_rows = rows * (2 * sh.head_dim + sh.head_dim // 2 +
+                                   2 * (sh.head_dim // W.INT4_GROUP))
+            elif self.quant:    # fp16 read, codes + one scale written
+                new_rows = rows * (2 * sh.head_dim + sh.head_dim + 2)
+            else:               # read and written in the cache's format
+                new_rows = rows * 2 * sh.head_dim * W.ELEM_BYTES[sh.cache_dtype]
         return self.kv_bytes_per_layer() + qo + tables + new_rows
 
 
@@ -638,7 +649,8 @@ def main():
             "workload": f"{shape.name}: {shape.description}; step = per layer "
                         + ("append, then the windowed attention call (partitions, merge)"
                            if b.window
-                           else "attention launch with the slot and append fused in, then merge"
+                           else "attention launch with the slot and "
+                           + ("quantizing " if b.quant else "") + "append fused in, then merge"
                            if b.fused_append
                            else "slots, append, attention partitions, merge launches"
                            if b.append else "attention partitions, merge launches"),
