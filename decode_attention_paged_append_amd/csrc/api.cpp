@@ -389,7 +389,7 @@ pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, vo
   if (st != PA_OK) return st;
   if (quantized(cache->dtype))
     return fail(PA_ERR_UNSUPPORTED,
-                "quantized cache: append with pa_kv_append_int8/_fp8, then attend");
+                "quantized cache: use pa_decode_step_quant");
   if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
   return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
@@ -408,7 +408,7 @@ pa_status pa_decode_step_partitions(const void* q, const void* k_new, const void
   if (st != PA_OK) return st;
   if (quantized(cache->dtype))
     return fail(PA_ERR_UNSUPPORTED,
-                "quantized cache: append with pa_kv_append_int8/_fp8, then pa_decode_partitions");
+                "quantized cache: use pa_decode_step_partitions_quant");
   if (num_seqs == 0) return PA_OK;
   if (!k_new || !v_new) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
   return run_partitions(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,

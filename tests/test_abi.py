@@ -112,6 +112,41 @@ def test_decode_argument_checks(lib):
     assert lib.pa_lse_merge(FAKE, 1 << 30, FAKE, 4, 4, 128, 16, 16, 64, 3, FAKE, None) == UNSUPPORTED
 
 
+def test_decode_step_quant_argument_checks(lib):
+    """pa_decode_step_quant / _partitions_quant: quantized caches only, both
+    new rows and both scale arrays, workspace and partition checks; the
+    16-bit step entry points point quantized caches to them."""
+    f16, i8, fp8, i4 = desc(), desc(dtype=3), desc(dtype=4), desc(dtype=5)
+    step = lambda d_, kn=FAKE, ks=FAKE, s=4, ws=FAKE, wsb=1 << 30: lib.pa_decode_step_quant(
+        FAKE, kn, FAKE, FAKE, FAKE, ks, FAKE, FAKE, 16, FAKE, s, 4, 0.1, FAKE, ctypes.byref(d_),
+        ws, wsb, None)
+    assert step(f16) == UNSUPPORTED
+    assert b"int8, fp8 or int4" in lib.pa_last_error()
+    for d_ in (i8, fp8, i4):
+        assert step(d_, kn=None) == INVALID
+        assert step(d_, ks=None) == INVALID
+        assert b"k_scale" in lib.pa_last_error()
+        assert step(d_, kn=None, ks=None, s=0, ws=None, wsb=0) == OK   # nothing to do
+    part = lambda d_, pt, wsb, kn=FAKE: lib.pa_decode_step_partitions_quant(
+        FAKE, kn, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 4, 0.1, pt, FAKE,
+        ctypes.byref(d_), FAKE, wsb, None)
+    need = lib.pa_decode_workspace_bytes(ctypes.byref(i8), 4, 4, 16, 64)
+    assert need > 0
+    assert part(i8, 64, need - 1) == WORKSPACE
+    assert part(i8, 24, need) == INVALID
+    assert b"multiple of the tile" in lib.pa_last_error()
+    assert part(i8, 64, need, kn=None) == INVALID
+    assert part(f16, 64, need) == UNSUPPORTED
+    # the 16-bit step entry points name the quantized ones
+    assert lib.pa_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 4, 0.1, FAKE,
+                              ctypes.byref(i8), FAKE, 1 << 30, None) == UNSUPPORTED
+    assert b"pa_decode_step_quant" in lib.pa_last_error()
+    assert lib.pa_decode_step_partitions(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 4, 0.1,
+                                         64, FAKE, ctypes.byref(fp8), FAKE, 1 << 30,
+                                         None) == UNSUPPORTED
+    assert b"pa_decode_step_partitions_quant" in lib.pa_last_error()
+
+
 @pytest.mark.parametrize("dtype,d,bs,tile", [(0, 64, 4, 4), (1, 128, 16, 16), (1, 64, 4, 8),
                                               (3, 64, 4, 16), (3, 128, 32, 32), (0, 128, 8, 8),
                                               (4, 64, 4, 16), (4, 128, 16, 16)])
