@@ -188,20 +188,28 @@ class Bench:
 READ_PROBE_BYTES = 4 << 30   # 16x the 256 MiB last-level cache
 
 
-def read_probe(dev, launches: int = 10) -> dict:
+def read_probe(dev, launches: int = 10, groups=()) -> dict:
     """The library's HBM read-rate probe (pa_hbm_read_probe) over a 4 GiB
     buffer, timed between HIP events: 4 KiB chunks read in sequence, and in a
     seeded random order (the access pattern of the attention kernels' block
     gather).  These are the practical read bandwidths the attention kernels'
-    rates are compared with."""
+    rates are compared with.  groups: also random orders of runs of n
+    adjacent chunks (n waves of one workgroup read 4n contiguous KiB), the
+    rate a kernel that read bigger contiguous pieces could reach."""
     src = torch.empty(READ_PROBE_BYTES // 4, dtype=torch.int32, device=dev)
     src.fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     chunks = READ_PROBE_BYTES // 4096
     gen = torch.Generator().manual_seed(3)
-    order = torch.randperm(chunks, generator=gen).to(torch.int32).to(dev)
+
+    def runs_of(n):
+        perm = torch.randperm(chunks // n, generator=gen)
+        return (perm[:, None] * n + torch.arange(n)[None, :]).reshape(-1).to(torch.int32).to(dev)
+
+    orders = [("sequential", None), ("random_chunks", runs_of(1))]
+    orders += [(f"random_{4 * n}KiB_runs", runs_of(n)) for n in groups]
     result = {"bytes": READ_PROBE_BYTES, "chunk_bytes": 4096}
-    for name, o in (("sequential", None), ("random_chunks", order)):
+    for name, o in orders:
         for _ in range(2):
             pa.hbm_read_probe(src, sink, o)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -213,7 +221,7 @@ def read_probe(dev, launches: int = 10) -> dict:
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / launches
         result[name + "_GB/s"] = round(READ_PROBE_BYTES / (ms / 1e3) / 1e9, 1)
-    del src, order
+    del src, orders
     return result
 
 
@@ -568,7 +576,8 @@ def main():
     ap.add_argument("--copy-kernel", type=int, default=0,
                     help="only run N copies of a 1 GiB tensor (counter calibration) and exit")
     ap.add_argument("--read-probe", action="store_true",
-                    help="only time the HBM read-rate probe over 4 GiB and exit")
+                    help="only time the HBM read-rate probe over 4 GiB (also random runs of "
+                         "2-16 adjacent chunks) and exit")
     ap.add_argument("--no-read-probe", action="store_true")
     args = ap.parse_args()
 
@@ -588,7 +597,7 @@ def main():
         return
 
     if args.read_probe:
-        print(json.dumps({"hbm_read_probe": read_probe(dev)}))
+        print(json.dumps({"hbm_read_probe": read_probe(dev, groups=(2, 4, 8, 16))}))
         return
 
     if args.workload == "block-pool":
