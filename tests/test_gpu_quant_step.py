@@ -180,3 +180,67 @@ def test_decode_step_quant_rejects_unquantized_cache():
     with pytest.raises(ValueError):
         pa.decode_step_quant(q, kn, vn, kc, vc, sc, sc, bt, ctx_t, shape.scale,
                              torch.empty_like(q))
+
+
+@pytest.mark.parametrize("shape", [W.LLAMA3_8B_I8, W.LLAMA3_8B_FP8, W.LLAMA3_8B_I4],
+                         ids=lambda s: s.name)
+def test_decode_step_quant_full_size(shape, orc):
+    """The benchmark's quantized step at full size (64 sequences x 8192, the
+    library's plan): the new rows' codes and scales bit-exact against the
+    oracle's quantizer, whose pool slots were poisoned first, and sampled
+    outputs within tolerance of the oracle over the sampled sequences'
+    blocks."""
+    from test_gpu_int4 import quantize_all_gpu, quantize_all_oracle
+    from gpu_cases import quantize_blocks_oracle, quantize_pool_gpu
+    from test_gpu_workloads import sample_pairs
+
+    fmt = shape.cache_dtype
+    int4 = fmt == "i4"
+    bs = shape.block_size
+    print(f"decode_step_quant full size {shape.name}", flush=True)
+    lay = W.layout_for(shape)
+    case = W.make_case(shape, lay, device=dev(), seed=7, poison=False)
+    if int4:
+        pools = list(quantize_all_gpu(case.k_cache, case.v_cache))
+    else:
+        pools = list(quantize_pool_gpu(case.k_cache, case.v_cache, None, fmt))
+    slots = oracle.decode_slot_mapping(host(lay.block_tables), host(lay.context_lens), bs)
+    b_idx = torch.as_tensor(slots // bs, device=dev())
+    o_idx = torch.as_tensor(slots % bs, device=dev())
+    for t in pools[:2]:
+        t.view(torch.uint8)[b_idx, :, o_idx] = 0x5A
+    for t in pools[2:]:
+        t[b_idx, :, o_idx] = float("nan")
+    bt, ctx = lay.block_tables.to(dev()), lay.context_lens.to(dev())
+    out = torch.empty_like(case.q)
+    pa.decode_step_quant(case.q, case.k_new, case.v_new, *pools, bt, ctx, shape.scale, out,
+                         int4=int4)
+    torch.cuda.synchronize()
+
+    # the new rows: the oracle's quantizer on the same fp16 rows
+    s, hkv, d = case.k_new.shape
+    width = d // 2 if int4 else d
+    small = [np.zeros((s, hkv, bs, width), CODE_NP[fmt]) for _ in range(2)]
+    small += [np.zeros((s, hkv, bs) + ((d // W.INT4_GROUP,) if int4 else ()), np.float16)
+              for _ in range(2)]
+    ORACLE_APPEND[fmt](host(case.k_new), host(case.v_new), np.arange(s, dtype=np.int64) * bs,
+                       *small)
+    for got, exp in zip(pools, small):
+        assert same_bits(got[b_idx, :, o_idx], exp[:, :, 0])
+
+    # sampled outputs over the sampled sequences' blocks
+    pairs = sample_pairs(shape.num_seqs, shape.num_q_heads, 5, extra=0)[::8]
+    seqs = sorted({q for q, _ in pairs})
+    blocks = lay.block_tables[seqs].flatten()
+    blocks = blocks[blocks >= 0]
+    if int4:
+        want = list(quantize_all_oracle(case.k_cache, case.v_cache, blocks.tolist()))
+    else:
+        want = list(quantize_blocks_oracle(case.k_cache, case.v_cache, blocks, fmt)[:4])
+    ORACLE_APPEND[fmt](host(case.k_new), host(case.v_new), slots, *want)
+    ref = oracle.paged_decode_attention(host(case.q), want[0], want[1], host(lay.block_tables),
+                                        host(lay.context_lens), shape.scale, k_scale=want[2],
+                                        v_scale=want[3], pairs=pairs, int4=int4,
+                                        num_threads=8, lib=orc)
+    assert torch.isfinite(out).all()
+    assert max_abs_err(out, ref, pairs) <= TOL["i8" if int4 else fmt]
