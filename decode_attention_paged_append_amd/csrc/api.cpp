@@ -86,6 +86,8 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
   p.k_new = k_new;
   p.v_new = v_new;
   p.window = window;
+  p.pair = plan.pair ? 1 : 0;
+  p.num_seqs = num_seqs;
   hipError_t e;
   const int D = cache->head_dim, BS = cache->block_size;
   if (plan.mfma) {

@@ -66,7 +66,7 @@ static hipError_t launch_fmt(const DecodeParams& p, int head_dim, int bs, int gc
 template <Fmt F, int D, int BS, int GC>
 static hipError_t launch_mfma_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_parts, (unsigned)(p.num_kv_heads * p.head_chunks),
-                  (unsigned)num_seqs);
+                  (unsigned)(p.pair ? (num_seqs + 1) / 2 : num_seqs));
   hipLaunchKernelGGL((decode_mfma_kernel<F, D, BS, GC, kDecodeWaves>), grid,
                      dim3(kDecodeWaves * kWave), 0, stream, p);
   return hipGetLastError();

@@ -70,6 +70,11 @@ struct DecodeParams {
   // partition start / part_tokens + k, and partials are stored by slot
   // (num_parts = slots); slots past the sequence's end are left unwritten.
   int32_t window;
+  // Paired plan (matrix-core kernel, one partition; 0: off): the grid's z
+  // dimension holds ceil(num_seqs / 2) workgroups, and workgroup k attends
+  // the k-th longest sequence, then the k-th shortest (paired_sequences).
+  int32_t pair;
+  int32_t num_seqs;
 };
 
 // Workgroup coordinates (partition, KV head x chunk, sequence).  Workgroups
@@ -102,6 +107,44 @@ __device__ __forceinline__ int window_start(const DecodeParams& p, int ctx) {
 __device__ __forceinline__ int partition_of_slot(const DecodeParams& p, int slot, int ctx) {
   if (p.window <= 0 || ctx < 0) return slot;
   return window_start(p, ctx) / p.part_tokens + slot;
+}
+
+// Sequences of a paired plan.  Two workgroups share each CU, and with ragged
+// lengths the CUs that drew two long sequences finish last; taking a long and
+// a short sequence in one workgroup evens out the work per CU.  The context
+// lengths are ranked longest first, ties by index: a strict order whatever
+// the lengths hold (broken ones included), so the ranks are a permutation and
+// every sequence is taken exactly once.  Workgroup k takes ranks k and
+// S - 1 - k; *second is -1 when they coincide (the middle of an odd S).
+// Every thread of the workgroup must call this.
+constexpr int kPairMaxSeqs = 256;
+template <int NT>
+__device__ __forceinline__ int paired_sequences(const DecodeParams& p, int k, int* second) {
+  __shared__ __attribute__((aligned(16))) int s_ctx[kPairMaxSeqs];
+  __shared__ int s_pick[2];
+  const int S = p.num_seqs;
+  const int S4 = (S + 3) / 4;
+  // pad to whole int4s with INT_MIN: never longer, and past every index
+  for (int i = threadIdx.x; i < 4 * S4; i += NT)
+    s_ctx[i] = i < S ? p.context_lens[i] : INT32_MIN;
+  __syncthreads();
+  for (int i = threadIdx.x; i < S; i += NT) {
+    const int ci = s_ctx[i];
+    int rank = 0;
+    for (int j4 = 0; j4 < S4; ++j4) {
+      const int4 c = ((const int4*)s_ctx)[j4];
+      const int j = 4 * j4;
+      rank += (c.x > ci || (c.x == ci && j < i)) ? 1 : 0;
+      rank += (c.y > ci || (c.y == ci && j + 1 < i)) ? 1 : 0;
+      rank += (c.z > ci || (c.z == ci && j + 2 < i)) ? 1 : 0;
+      rank += (c.w > ci || (c.w == ci && j + 3 < i)) ? 1 : 0;
+    }
+    if (rank == k) s_pick[0] = i;
+    if (rank == S - 1 - k) s_pick[1] = i;
+  }
+  __syncthreads();
+  *second = S - 1 - k != k ? s_pick[1] : -1;
+  return s_pick[0];
 }
 
 template <Fmt F>

@@ -105,8 +105,7 @@ constexpr float kSub = 16777216.0f;  // 2^24: scale of the int8 subnormal codes
 
 // Heads per workgroup (GC, padded to 16 in the MFMA) x NW waves.
 template <Fmt F, int D, int BS, int GC, int NW>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(3, 8)))
-void decode_mfma_kernel(const DecodeParams p) {
+__device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const WgCoord wc) {
   constexpr bool kQuant = FmtInfo<F>::quantized;
   constexpr bool kBias = F == Fmt::I8;          // codes biased by +128 (subnormals)
   constexpr Fmt OF = kQuant ? Fmt::F16 : F;     // MFMA operand format
@@ -130,7 +129,6 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4;
   const int n = lane & 15;
-  const WgCoord wc = wg_coord();
   const int slot = wc.part;
   const int kvh = wc.y / p.head_chunks;
   const int chunk = wc.y - kvh * p.head_chunks;
@@ -457,6 +455,26 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
     if (bad) M = L = acc = __builtin_nanf("");
     store_result<F, D>(p, single, out_row0 + h, slot, d, M, L, acc);
+  }
+}
+
+// One (partition, KV head x chunk, sequence) item per workgroup, or for a
+// paired plan two sequences one after the other (paired_sequences).
+template <Fmt F, int D, int BS, int GC, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void decode_mfma_kernel(const DecodeParams p) {
+  WgCoord wc = wg_coord();
+  if (!p.pair) {
+    decode_mfma_item<F, D, BS, GC, NW>(p, wc);
+    return;
+  }
+  int second;
+  wc.s = paired_sequences<NW * kWave>(p, wc.s, &second);
+  decode_mfma_item<F, D, BS, GC, NW>(p, wc);
+  if (second >= 0) {
+    __syncthreads();  // the first sequence's merge is done with LDS
+    wc.s = second;
+    decode_mfma_item<F, D, BS, GC, NW>(p, wc);
   }
 }
 

@@ -67,6 +67,7 @@ inline pa_status check_cache(const pa_cache_desc* c) {
 //    merge cost more than the imbalance of long partitions (Llama-2-70B's
 //    ragged batch runs fastest as one partition per sequence); int8 tiles
 //    carry half the bytes and do best with ~2048 workgroups.
+inline constexpr int32_t kComputeUnits = 256;
 inline constexpr int32_t kTargetWorkgroups = 2048;
 inline constexpr int32_t kTargetWorkgroupsMfma = 256;
 inline constexpr int32_t kTargetWorkgroupsMfmaInt8 = 2048;
@@ -83,6 +84,7 @@ struct Plan {
   int32_t tile = 0;       // positions per tile
   int32_t part_tokens = 0;
   int32_t num_parts = 0;
+  bool pair = false;      // matrix-core kernel: two sequences per workgroup
   size_t ml_bytes = 0;    // workspace: partial (max, sum)
   size_t o_offset = 0;    // workspace: offset of the partial outputs
   size_t ws_bytes = 0;
@@ -167,6 +169,14 @@ inline pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num
   if (window > 0 && p.num_parts > 1)
     p.num_parts = (int32_t)std::min<int64_t>(p.num_parts,
                                              (window + p.part_tokens - 1) / p.part_tokens + 1);
+  // Paired plan: one partition per sequence on the matrix cores, with at
+  // least two (sequence, KV head x chunk) items per CU.  A workgroup then
+  // takes a long and a short sequence, so that ragged lengths even out per
+  // CU (a Llama-2-70B batch with lengths U[128, 32768]: 788 -> 726 us when
+  // its sequences were ordered so that each CU drew such a pair).
+  p.pair = p.mfma && p.num_parts == 1 && window == 0 && num_seqs >= 2 &&
+           num_seqs <= kPairMaxSeqs &&
+           (int64_t)num_seqs * c->num_kv_heads * p.chunks >= 2 * kComputeUnits;
   if (num_seqs > 65535 || (int64_t)c->num_kv_heads * p.chunks > 65535)
     return fail(PA_ERR_UNSUPPORTED, "grid too large (%d sequences, %d KV heads x %d chunks)",
                 num_seqs, c->num_kv_heads, p.chunks);
