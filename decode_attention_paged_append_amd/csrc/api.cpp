@@ -86,6 +86,7 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
   p.k_new = k_new;
   p.v_new = v_new;
   p.window = window;
+  p.tile = plan.tile;
   p.pair = plan.pair ? 1 : 0;
   p.num_seqs = num_seqs;
   hipError_t e;
@@ -119,7 +120,7 @@ pa_status run_merge(const Plan& plan, const void* workspace, const int32_t* cont
   const hipError_t e = pa::launch_lse_merge(
       (const float*)workspace, (const float*)((const char*)workspace + plan.o_offset),
       context_lens, num_seqs, num_q_heads, head_dim, max_tokens, plan.part_tokens,
-      plan.num_parts, window, out_dtype, out, stream);
+      plan.num_parts, window, plan.tile, out_dtype, out, stream);
   return hip_status(e, "lse merge launch");
 }
 

@@ -66,10 +66,12 @@ struct DecodeParams {
   const void* v_new;
   // Sliding window (0: none): the token attends to the last `window`
   // positions, [ctx - window, ctx).  The grid then covers only the
-  // partitions a window can touch: partition slot k of a sequence is its
-  // partition start / part_tokens + k, and partials are stored by slot
-  // (num_parts = slots); slots past the sequence's end are left unwritten.
+  // partitions a window can touch: grid slot k of a sequence is the k-th
+  // partition counted from the window's first tile (partition_start), and
+  // partials are stored by slot (num_parts = slots); slots past the
+  // sequence's end are left unwritten.
   int32_t window;
+  int32_t tile;             // the plan's tile length (positions)
   // Paired plan (matrix-core kernel, one partition; 0: off): the grid's z
   // dimension holds ceil(num_seqs / 2) workgroups, and workgroup k attends
   // the k-th longest sequence, then the k-th shortest (paired_sequences).
@@ -102,11 +104,15 @@ __device__ __forceinline__ int window_start(const DecodeParams& p, int ctx) {
   return p.window > 0 && ctx > p.window ? ctx - p.window : 0;
 }
 
-// Partition of a grid slot: the slot itself, or for a windowed plan the
-// slot-th partition from the one holding the window's first position.
-__device__ __forceinline__ int partition_of_slot(const DecodeParams& p, int slot, int ctx) {
-  if (p.window <= 0 || ctx < 0) return slot;
-  return window_start(p, ctx) / p.part_tokens + slot;
+// First position of a grid slot's partition: slot * part_tokens, or for a
+// windowed plan the slot-th partition from the tile holding the window's
+// first position.  So a window splits into whole partitions from its first
+// tile on, whatever its offset, and no partition is cut short at its start
+// by an absolute partition boundary.
+__device__ __forceinline__ int partition_start(const DecodeParams& p, int slot, int ctx) {
+  if (p.window <= 0 || ctx < 0) return slot * p.part_tokens;
+  const int start = window_start(p, ctx);
+  return start - start % p.tile + slot * p.part_tokens;
 }
 
 // Sequences of a paired plan.  Two workgroups share each CU, and with ragged
@@ -467,7 +473,7 @@ void decode_partition_kernel(const DecodeParams p) {
 
   const int ctx = p.context_lens[s];
   const bool single = p.num_parts == 1;
-  const int tok0 = partition_of_slot(p, slot, ctx) * p.part_tokens;
+  const int tok0 = partition_start(p, slot, ctx);
   const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
   if (bad_ctx || tok0 >= ctx) {
     // Nothing to attend in this partition.  The merge skips it; a single

@@ -138,7 +138,7 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
 
   const int ctx = p.context_lens[s];
   const bool single = p.num_parts == 1;
-  const int tok0 = partition_of_slot(p, slot, ctx) * p.part_tokens;
+  const int tok0 = partition_start(p, slot, ctx);
   const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
   if (bad_ctx || tok0 >= ctx) {
     if (single) {

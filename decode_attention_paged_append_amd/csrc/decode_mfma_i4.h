@@ -87,7 +87,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
 
   const int ctx = p.context_lens[s];
   const bool single = p.num_parts == 1;
-  const int tok0 = partition_of_slot(p, slot, ctx) * p.part_tokens;
+  const int tok0 = partition_start(p, slot, ctx);
   const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
   if (bad_ctx || tok0 >= ctx) {
     if (single) {
@@ -452,7 +452,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
 
   const int ctx = p.context_lens[s];
   const bool single = p.num_parts == 1;
-  const int tok0 = partition_of_slot(p, slot, ctx) * p.part_tokens;
+  const int tok0 = partition_start(p, slot, ctx);
   const bool bad_ctx = ctx < 0 || ctx > p.max_blocks * BS;
   if (bad_ctx || tok0 >= ctx) {
     if (single) {

@@ -72,11 +72,7 @@ inline constexpr int32_t kTargetWorkgroups = 2048;
 inline constexpr int32_t kTargetWorkgroupsMfma = 256;
 inline constexpr int32_t kTargetWorkgroupsMfmaInt8 = 2048;
 inline constexpr int32_t kMinPartitionTokens = 256;
-// A windowed plan: workgroups over the window only (measured on a 4096-token
-// window of 16 sequences x 8 KV heads, partitions launched by slot: 1024
-// beat 512, 2048 and 256 by 4-7 %).
-inline constexpr int32_t kTargetWorkgroupsWindow = 1024;
-
+inline constexpr int32_t kMinWindowPartitionTokens = 512;
 struct Plan {
   bool mfma = false;      // matrix-core kernel (grouped-query heads)
   int32_t gc = 1;         // query heads per workgroup
@@ -151,24 +147,34 @@ inline pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num
     // Enough workgroups to fill the chip, each wave owning whole tiles.
     const int64_t unit = (int64_t)p.tile * pa::kDecodeWaves;
     const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads * p.chunks;
-    const int64_t target = window > 0 ? kTargetWorkgroupsWindow
-                           : !p.mfma ? kTargetWorkgroups
+    // A window's partitions are counted from its first tile, so a windowed
+    // plan splits the window like a plain one splits the table, with the
+    // same targets and partitions of at least kMinWindowPartitionTokens
+    // (windows are short spans; measured on 16 sequences, 4096-token fp16
+    // window, 8 KV heads: 256 workgroups 49.2 us, 512: 50.0, 1024: 52.5,
+    // 2048: 55.4; 2048-token windows at 32 and 16 KV heads and a 4096-token
+    // int8 window did best at 576-token partitions).
+    const int64_t target = !p.mfma ? kTargetWorkgroups
                            : quantized(c->dtype) ? kTargetWorkgroupsMfmaInt8
                                                  : kTargetWorkgroupsMfma;
     const int64_t want_parts = (target + units - 1) / units;
-    const int64_t span = window > 0 ? std::min<int64_t>(max_tok, window) : max_tok;
+    // a window's partitions start at the tile holding its first position:
+    // they cover up to tile - 1 positions before it
+    const int64_t span = window > 0 ? std::min<int64_t>(max_tok, (int64_t)window + p.tile - 1)
+                                    : max_tok;
     part = (span + want_parts - 1) / want_parts;
-    part = std::max<int64_t>(part, kMinPartitionTokens);
+    part = std::max<int64_t>(part, window > 0 ? kMinWindowPartitionTokens : kMinPartitionTokens);
     part = (part + unit - 1) / unit * unit;
   }
   if (part >= max_tok) part = (max_tok + p.tile - 1) / p.tile * p.tile;
   p.part_tokens = (int32_t)std::min<int64_t>(part, INT32_MAX / 2);
   p.num_parts = (int32_t)((max_tok + p.part_tokens - 1) / p.part_tokens);
-  // A window touches at most ceil(window / part) + 1 partitions of a
-  // sequence: the grid and the workspace hold that many slots.
+  // Counted from the tile holding its first position, a window spans at
+  // most window + tile - 1 positions, ceil((window + tile - 1) / part)
+  // partitions: the grid and the workspace hold that many slots.
   if (window > 0 && p.num_parts > 1)
-    p.num_parts = (int32_t)std::min<int64_t>(p.num_parts,
-                                             (window + p.part_tokens - 1) / p.part_tokens + 1);
+    p.num_parts = (int32_t)std::min<int64_t>(
+        p.num_parts, ((int64_t)window + p.tile - 1 + p.part_tokens - 1) / p.part_tokens);
   // Paired plan: one partition per sequence on the matrix cores, with at
   // least two (sequence, KV head x chunk) items per CU.  A workgroup then
   // takes a long and a short sequence, so that ragged lengths even out per

@@ -36,12 +36,12 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, void* k_scale, void*
                               int32_t scales_per_row, hipStream_t stream);
 
 // Log-sum-exp merge of partition partials (lse_merge.hip).
-// window > 0: partials are stored by window slot (the partition holding the
-// window's first position is slot 0).
+// window > 0: partials are stored by window slot (slot 0 starts at the tile,
+// of `tile` positions, holding the window's first position).
 hipError_t launch_lse_merge(const float* part_ml, const float* part_o,
                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                             int32_t head_dim, int32_t max_tokens, int32_t part_tokens,
-                            int32_t num_parts, int32_t window, int32_t out_fmt, void* out,
-                            hipStream_t stream);
+                            int32_t num_parts, int32_t window, int32_t tile, int32_t out_fmt,
+                            void* out, hipStream_t stream);
 
 }  // namespace pa

@@ -16,7 +16,8 @@ template <int OUT_FMT>
 __global__ void lse_merge_kernel(const float* __restrict__ part_ml, const float* __restrict__ part_o,
                                  const int32_t* __restrict__ context_lens, int32_t num_q_heads,
                                  int32_t head_dim, int32_t max_tokens, int32_t part_tokens,
-                                 int32_t num_parts, int32_t window, void* __restrict__ out) {
+                                 int32_t num_parts, int32_t window, int32_t tile,
+                                 void* __restrict__ out) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int d = threadIdx.x;
@@ -29,9 +30,11 @@ __global__ void lse_merge_kernel(const float* __restrict__ part_ml, const float*
     result = 0.0f;
   } else {
     // partitions (slots) the sequence used: all up to its end, or for a
-    // sliding window those from the one holding the window's first position
-    const int first = window > 0 && ctx > window ? (ctx - window) / part_tokens : 0;
-    const int np = (ctx + part_tokens - 1) / part_tokens - first;
+    // sliding window those counted from the tile holding the window's first
+    // position (the attention kernels' partition_start)
+    const int start = window > 0 && ctx > window ? ctx - window : 0;
+    const int base = start - start % tile;
+    const int np = (ctx - base + part_tokens - 1) / part_tokens;
     const float* ml = part_ml + row * num_parts * 2;
     const float* o = part_o + row * num_parts * head_dim + d;
     float M = -__builtin_inff();
@@ -57,25 +60,25 @@ __global__ void lse_merge_kernel(const float* __restrict__ part_ml, const float*
 hipError_t launch_lse_merge(const float* part_ml, const float* part_o,
                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                             int32_t head_dim, int32_t max_tokens, int32_t part_tokens,
-                            int32_t num_parts, int32_t window, int32_t out_fmt, void* out,
-                            hipStream_t stream) {
+                            int32_t num_parts, int32_t window, int32_t tile, int32_t out_fmt,
+                            void* out, hipStream_t stream) {
   const dim3 grid((unsigned)num_q_heads, (unsigned)num_seqs);
   const dim3 block((unsigned)head_dim);
   switch (out_fmt) {
     case (int)Fmt::F32:
       hipLaunchKernelGGL(lse_merge_kernel<(int)Fmt::F32>, grid, block, 0, stream, part_ml, part_o,
                          context_lens, num_q_heads, head_dim, max_tokens, part_tokens, num_parts,
-                         window, out);
+                         window, tile, out);
       break;
     case (int)Fmt::F16:
       hipLaunchKernelGGL(lse_merge_kernel<(int)Fmt::F16>, grid, block, 0, stream, part_ml, part_o,
                          context_lens, num_q_heads, head_dim, max_tokens, part_tokens, num_parts,
-                         window, out);
+                         window, tile, out);
       break;
     case (int)Fmt::BF16:
       hipLaunchKernelGGL(lse_merge_kernel<(int)Fmt::BF16>, grid, block, 0, stream, part_ml,
                          part_o, context_lens, num_q_heads, head_dim, max_tokens, part_tokens,
-                         num_parts, window, out);
+                         num_parts, window, tile, out);
       break;
     default:
       return hipErrorInvalidValue;
