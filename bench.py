@@ -139,7 +139,11 @@ class Bench:
         the append fused into it for 16/32-bit caches)."""
         c, sh = self.cases[layer], self.shape
         out = self.outs[layer]
-        if self.window:
+        if self.window and self.fused_append:
+            pa.decode_step_window(c.q, c.k_new, c.v_new, c.k_cache, c.v_cache, self.bt, self.ctx,
+                                  sh.scale, self.window, out, getattr(c, "k_scale", None),
+                                  getattr(c, "v_scale", None), self.wws, int4=self.int4)
+        elif self.window:
             pa.paged_decode_attention_window(c.q, c.k_cache, c.v_cache, self.bt, self.ctx,
                                              sh.scale, self.window, out, workspace=self.wws)
         elif self.fused_append and self.quant:
@@ -156,7 +160,7 @@ class Bench:
 
     @property
     def fused_append(self) -> bool:
-        return self.append and not self.separate and not self.window
+        return self.append and not self.separate
 
     def kv_bytes_per_layer(self) -> int:
         return W.kv_bytes_per_layer_step(self.shape, self.layout.context_lens.tolist())
@@ -656,8 +660,10 @@ def main():
                 "permutation of the pool",
         "config": {
             "workload": f"{shape.name}: {shape.description}; step = per layer "
-                        + ("append, then the windowed attention call (partitions, merge)"
-                           if b.window
+                        + ("windowed attention launch with the slot and append fused in, "
+                           "then merge" if b.window and b.fused_append
+                           else "slots, append, then the windowed attention call (partitions, "
+                           "merge)" if b.window
                            else "attention launch with the slot and "
                            + ("quantizing " if b.quant else "") + "append fused in, then merge"
                            if b.fused_append

@@ -25,7 +25,7 @@ __all__ = [
     "decode_step_partitions", "decode_step_quant", "decode_step_partitions_quant", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
     "hbm_read_probe",
     "BlockManager", "copy_blocks", "paged_prefill_attention", "paged_decode_attention_window",
-    "decode_window_workspace_bytes",
+    "decode_window_workspace_bytes", "decode_step_window",
 ]
 
 # PA_LIBRARY_PATH may name another build of the same library (e.g. a variant
@@ -106,6 +106,8 @@ def _declare(lib):
         "pa_paged_prefill_attention": [P, P, P, P, i32, P, P, i32, i32, i32, f32, P, D, P],
         "pa_paged_decode_attention_window": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D,
                                              P, sz, P],
+        "pa_decode_step_window": [P, P, P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D, P,
+                                  sz, P],
         "pa_bm_create": [i32, i32, ctypes.POINTER(P)],
         "pa_bm_add_sequence": [P, ctypes.POINTER(i32)],
         "pa_bm_fork": [P, i32, i32, ctypes.POINTER(i32)],
@@ -554,6 +556,33 @@ def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_len
     _ok(lib.pa_paged_decode_attention_window(
         _dev(q, "q", q_dtype, 3), _dev(k_cache, "k_cache", ndim=4),
         _dev(v_cache, "v_cache", k_cache.dtype, 4),
+        _dev(k_scale, "k_scale", torch.float16) if quant else None,
+        _dev(v_scale, "v_scale", torch.float16) if quant else None,
+        _dev(block_tables, "block_tables", torch.int32), maxb,
+        _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale), int(window),
+        _dev(out, "out", q_dtype), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _stream(q)), lib)
+    return out
+
+
+def decode_step_window(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                       window, out, k_scale=None, v_scale=None, workspace=None, int4=False):
+    """One decode step with a sliding window: store (or, for int8 / fp8 /
+    int4 caches, quantize from fp16) each sequence's k_new/v_new [S, Hkv, D]
+    rows at position context_lens[s]-1 inside the attention launch, then
+    attend over the last `window` positions (see pa_decode_step_window)."""
+    lib = library()
+    desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out, int4)
+    quant = int4 or k_cache.dtype in QUANTIZED
+    q_dtype = torch.float16 if quant else k_cache.dtype
+    if k_new.shape != (s, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{s}, {desc.num_kv_heads}, {desc.head_dim}]")
+    need = decode_window_workspace_bytes(desc, s, hq, maxb, int(window))
+    ws = _workspace(workspace, need, q.device)
+    _ok(lib.pa_decode_step_window(
+        _dev(q, "q", q_dtype, 3), _dev(k_new, "k_new", q_dtype), _dev(v_new, "v_new", q_dtype),
+        _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", k_cache.dtype, 4),
         _dev(k_scale, "k_scale", torch.float16) if quant else None,
         _dev(v_scale, "v_scale", torch.float16) if quant else None,
         _dev(block_tables, "block_tables", torch.int32), maxb,

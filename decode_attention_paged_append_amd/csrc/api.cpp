@@ -518,6 +518,23 @@ pa_status pa_hbm_read_probe(const void* src, size_t bytes, const int32_t* chunk_
                     "read probe launch");
 }
 
+pa_status pa_decode_step_window(const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, float scale, int32_t window, void* out,
+                                const pa_cache_desc* cache, void* workspace,
+                                size_t workspace_bytes, pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
+  return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
+                       workspace_bytes, (hipStream_t)stream,
+                       quantized(cache->dtype) ? cache->dtype : -1, k_new, v_new, window);
+}
+
 pa_status pa_paged_prefill_attention(const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                                      const int32_t* query_start, const int32_t* context_lens,

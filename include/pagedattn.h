@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum {
   PA_F32 = 0,
@@ -398,6 +398,24 @@ pa_status pa_paged_decode_attention_window(const void* q, const void* k_cache,
                                            void* out, const pa_cache_desc* cache,
                                            void* workspace, size_t workspace_bytes,
                                            pa_stream_t stream);
+
+/* One decode step with a sliding window, for any cache format: the append
+ * of pa_decode_step (fp32 / fp16 / bf16 caches: k_new, v_new in the cache's
+ * format) or of pa_decode_step_quant (int8, fp8, int4: fp16 rows quantized
+ * into codes and scales) at position context_lens[s] - 1, inside the
+ * attention launch of pa_paged_decode_attention_window, which then attends
+ * over the last `window` positions, the new one included ([notes] steps 2-4;
+ * [viz] "What the page leaves out": sliding-window attention).  The merge of
+ * a multi-partition plan is the second launch.  workspace: >=
+ * pa_decode_window_workspace_bytes; k_scale, v_scale: NULL for unquantized
+ * caches.  Other arguments and errors as for those entry points. */
+pa_status pa_decode_step_window(const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, float scale, int32_t window, void* out,
+                                const pa_cache_desc* cache, void* workspace,
+                                size_t workspace_bytes, pa_stream_t stream);
 
 /* ---------------------------------------------------------------- prefill */
 
