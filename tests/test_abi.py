@@ -147,6 +147,23 @@ def test_decode_step_quant_argument_checks(lib):
     assert b"pa_decode_step_partitions_quant" in lib.pa_last_error()
 
 
+def test_decode_step_window_argument_checks(lib):
+    """pa_decode_step_window: both new rows, a non-negative window, scales for
+    quantized caches, the window workspace; nothing to do at S = 0."""
+    f16, i8 = desc(), desc(dtype=3)
+    step = lambda d_, kn=FAKE, ks=FAKE, w=2048, s=4, ws=FAKE, wsb=1 << 30: \
+        lib.pa_decode_step_window(FAKE, kn, FAKE, FAKE, FAKE, ks, FAKE, FAKE, 256, FAKE, s, 4,
+                                  0.1, w, FAKE, ctypes.byref(d_), ws, wsb, None)
+    assert step(f16, kn=None) == INVALID
+    assert step(f16, w=-1) == INVALID
+    assert b"window" in lib.pa_last_error()
+    assert step(i8, ks=None) == INVALID
+    need = lib.pa_decode_window_workspace_bytes(ctypes.byref(f16), 4, 4, 256, 2048)
+    assert need > 0
+    assert step(f16, wsb=need - 1) == WORKSPACE
+    assert step(f16, kn=None, s=0, ws=None, wsb=0) == OK
+
+
 @pytest.mark.parametrize("dtype,d,bs,tile", [(0, 64, 4, 4), (1, 128, 16, 16), (1, 64, 4, 8),
                                               (3, 64, 4, 16), (3, 128, 32, 32), (0, 128, 8, 8),
                                               (4, 64, 4, 16), (4, 128, 16, 16)])
