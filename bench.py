@@ -40,6 +40,7 @@ METRIC = ("decode-attention KV-read GB/s (% of HBM peak) + seq-steps/s, "
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 KERNEL_SOURCES = ["decode_attention_paged_append_amd/csrc/decode_kernel.h",
                   "decode_attention_paged_append_amd/csrc/device.h",
+                  "decode_attention_paged_append_amd/csrc/quant.h",
                   "decode_attention_paged_append_amd/csrc/decode_dispatch.h",
                   "decode_attention_paged_append_amd/csrc/decode_plan.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
