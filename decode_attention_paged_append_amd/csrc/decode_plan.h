@@ -67,7 +67,6 @@ inline pa_status check_cache(const pa_cache_desc* c) {
 //    merge cost more than the imbalance of long partitions (Llama-2-70B's
 //    ragged batch runs fastest as one partition per sequence); int8 tiles
 //    carry half the bytes and do best with ~2048 workgroups.
-inline constexpr int32_t kComputeUnits = 256;
 inline constexpr int32_t kTargetWorkgroups = 2048;
 inline constexpr int32_t kTargetWorkgroupsMfma = 256;
 inline constexpr int32_t kTargetWorkgroupsMfmaInt8 = 2048;
@@ -175,14 +174,19 @@ inline pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num
   if (window > 0 && p.num_parts > 1)
     p.num_parts = (int32_t)std::min<int64_t>(
         p.num_parts, ((int64_t)window + p.tile - 1 + p.part_tokens - 1) / p.part_tokens);
-  // Paired plan: one partition per sequence on the matrix cores, with at
-  // least two (sequence, KV head x chunk) items per CU.  A workgroup then
-  // takes a long and a short sequence, so that ragged lengths even out per
-  // CU (a Llama-2-70B batch with lengths U[128, 32768]: 788 -> 726 us when
-  // its sequences were ordered so that each CU drew such a pair).
+  // Paired plan: one partition per sequence on the matrix cores, with
+  // enough (sequence, KV head x chunk) items that half as many workgroups
+  // still meet the format's target (16-bit: two items per CU).  A workgroup
+  // then takes a long and a short sequence, so that ragged lengths even out
+  // per CU (a Llama-2-70B batch with lengths U[128, 32768]: 788 -> 726 us
+  // when its sequences were ordered so that each CU drew such a pair).  The
+  // quantized kernels need their 2048 workgroups: an int8 batch of 512
+  // items run paired in one partition took 275 us against 196 in four.
+  const int64_t mfma_target = quantized(c->dtype) ? kTargetWorkgroupsMfmaInt8
+                                                  : kTargetWorkgroupsMfma;
   p.pair = p.mfma && p.num_parts == 1 && window == 0 && num_seqs >= 2 &&
            num_seqs <= kPairMaxSeqs &&
-           (int64_t)num_seqs * c->num_kv_heads * p.chunks >= 2 * kComputeUnits;
+           (int64_t)num_seqs * c->num_kv_heads * p.chunks >= 2 * mfma_target;
   if (num_seqs > 65535 || (int64_t)c->num_kv_heads * p.chunks > 65535)
     return fail(PA_ERR_UNSUPPORTED, "grid too large (%d sequences, %d KV heads x %d chunks)",
                 num_seqs, c->num_kv_heads, p.chunks);

@@ -1,7 +1,8 @@
 """The paired plan of the matrix-core decode kernel on the GPU (needs an
-MI355X): with one partition per sequence and at least two (sequence, KV head)
-items per CU, each workgroup ranks the context lengths on the device and
-attends the k-th longest and the k-th shortest sequence.  Ragged batches of
+MI355X): with one partition per sequence and enough (sequence, KV head) items
+that half as many workgroups still meet the plan's target, each workgroup
+ranks the context lengths on the device and attends the k-th longest and the
+k-th shortest sequence.  Ragged batches of
 an odd number of sequences, with zero lengths, equal lengths and broken
 lengths among them (the ranking must still take every sequence exactly
 once), against the oracle; the fused decode step through the same plan."""
@@ -32,12 +33,17 @@ def whole_table(lay, bs):
     return lay.max_blocks * bs
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8", "fp8"])
-@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8), (128, 8)])
-def test_paired_plan_matches_oracle(dtype, hq, hkv, orc):
+# 16-bit caches pair from 512 items (two per CU); int8 and fp8 from 4096
+# (their kernel's 2048-workgroup target, halved grid)
+PAIRED = [(dt, hq, hkv, 65) for dt in ("f16", "bf16") for hq, hkv in ((32, 8), (64, 8), (128, 8))]
+PAIRED += [(dt, 128, 32, 255) for dt in ("i8", "fp8")]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,nseq", PAIRED)
+def test_paired_plan_matches_oracle(dtype, hq, hkv, nseq, orc):
     d, bs = 128, 16
-    ctx = ragged(65, bs, seed=hq)
-    print(f"paired plan {dtype} hq={hq} hkv={hkv}", flush=True)
+    ctx = ragged(nseq, bs, seed=hq)
+    print(f"paired plan {dtype} hq={hq} hkv={hkv} seqs={nseq}", flush=True)
     src = "f16" if dtype in ("i8", "fp8") else dtype
     shape, lay, case = make(src, hq, hkv, d, bs, ctx, seed=31)
     q, bt = to_dev(case.q, lay.block_tables)
