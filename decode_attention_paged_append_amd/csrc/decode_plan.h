@@ -184,7 +184,8 @@ inline pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num
   // items run paired in one partition took 275 us against 196 in four.
   const int64_t mfma_target = quantized(c->dtype) ? kTargetWorkgroupsMfmaInt8
                                                   : kTargetWorkgroupsMfma;
-  p.pair = p.mfma && p.num_parts == 1 && window == 0 && num_seqs >= 2 &&
+  // (The int4 matrix-core kernels take one sequence per workgroup.)
+  p.pair = p.mfma && c->dtype != PA_I4 && p.num_parts == 1 && window == 0 && num_seqs >= 2 &&
            num_seqs <= kPairMaxSeqs &&
            (int64_t)num_seqs * c->num_kv_heads * p.chunks >= 2 * mfma_target;
   if (num_seqs > 65535 || (int64_t)c->num_kv_heads * p.chunks > 65535)
