@@ -518,20 +518,14 @@ def prefill_bench(name, dev, steps, warmup, cpu: bool) -> dict:
     }
 
 
-def attention_launch_ms(b, layers, steps):
-    """Average duration of the dominant kernel: the same launches (every
-    layer, K times) back to back between two events on the stream they run
-    on.  They are captured once in a HIP graph and replayed, so that neither
-    per-launch events nor the binding's host work between launches (which a
-    short kernel would wait on) enter the figure; if capture fails, the
-    launches are issued directly."""
+def graph_timed_ms(launches, count):
+    """Average duration of the launches one launches() call issues (count of
+    them): they run back to back between two events on the stream they use,
+    captured once in a HIP graph and replayed, so that neither per-launch
+    events nor the binding's host work between launches (which a short kernel
+    would wait on) enter the figure; if capture fails, the launches are
+    issued directly."""
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def launches():
-        for _ in range(steps):
-            for layer in range(layers):
-                b.attend(layer)
-
     try:
         graph = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
@@ -550,7 +544,56 @@ def attention_launch_ms(b, layers, steps):
         k1.record()
         how = "launches issued back to back"
     torch.cuda.synchronize()
-    return k0.elapsed_time(k1) / (steps * layers), how
+    return k0.elapsed_time(k1) / count, how
+
+
+def attention_launch_ms(b, layers, steps):
+    """Average duration of the dominant kernel: the same launches (every
+    layer, K times) back to back (graph_timed_ms)."""
+    def launches():
+        for _ in range(steps):
+            for layer in range(layers):
+                b.attend(layer)
+
+    return graph_timed_ms(launches, steps * layers)
+
+
+def append_report(b, layers, steps) -> dict | None:
+    """The append on its own (pa_kv_append, or the quantizing append of an
+    int8 / fp8 / int4 cache): every layer's new rows at their decode slots,
+    K times, timed like the attention launch.  Its bytes: the new K and V rows
+    read (fp16 for the quantizing appends) and stored (codes and scales), and
+    the slots read."""
+    if not b.append:
+        return None
+    sh = b.shape
+    pa.decode_slot_mapping(b.bt, b.ctx, sh.block_size, out=b.slots)
+
+    def launches():
+        for _ in range(steps):
+            for c in b.cases:
+                if b.quant:
+                    b.quant_append(c.k_new, c.v_new, b.slots, c.k_cache, c.v_cache, c.k_scale,
+                                   c.v_scale)
+                else:
+                    pa.kv_append(c.k_new, c.v_new, b.slots, c.k_cache, c.v_cache)
+
+    ms, how = graph_timed_ms(launches, steps * layers)
+    rows = 2 * sh.num_seqs * sh.num_kv_heads
+    d = sh.head_dim
+    if b.int4:
+        moved = rows * (2 * d + d // 2 + 2 * (d // W.INT4_GROUP))
+    elif b.quant:
+        moved = rows * (2 * d + d + 2)
+    else:
+        moved = rows * 2 * d * W.ELEM_BYTES[sh.cache_dtype]
+    moved += 8 * sh.num_seqs
+    kernel = {"i8": "kv_append_quant_kernel<128, 0>", "fp8": "kv_append_quant_kernel<128, 1>",
+              "i4": "kv_append_quant_kernel<128, 2>"}.get(sh.cache_dtype, "kv_append_kernel")
+    return {"kernel": kernel, "avg_launch_us": round(ms * 1e3, 2), "bytes_per_launch": moved,
+            "GBps": round(moved / (ms / 1e3) / 1e9, 1), "timing": how,
+            "note": "timed on its own; the step fuses it into the attention launch"
+            if b.fused_append else "timed on its own; the step launches it separately"}
 
 
 def unique_bytes_report(b, layers, ms_step, kv_step) -> dict:
@@ -567,8 +610,8 @@ def unique_bytes_report(b, layers, ms_step, kv_step) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=W.LLAMA2_7B.name,
                     choices=sorted(W.SHAPES) + ["block-pool"] + sorted(PREFILL_WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="0: the workload's own layer count")
@@ -637,6 +680,7 @@ def main():
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
 
     kernel_ms, kernel_timing = attention_launch_ms(b, layers, args.steps)
+    append = append_report(b, layers, min(args.steps, 10))
 
     kv_step = b.kv_bytes_per_layer() * layers
     value = kv_step / (ms_step / 1e3) / 1e9
@@ -678,6 +722,7 @@ def main():
                {"partition_tokens": b.part, "partitions": b.nparts}),
         },
         "seq_steps_per_s": round(shape.num_seqs * 1e3 / ms_step, 2),
+        "steps_per_s": round(1e3 / ms_step, 2),
         **unique_bytes_report(b, layers, ms_step, kv_step),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": kv_step,
@@ -698,6 +743,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if append:
+        result["append"] = append
     if not args.no_read_probe:
         probe = read_probe(dev)
         probe["kernel_frac_of_sequential"] = round(achieved / probe["sequential_GB/s"], 4)
