@@ -278,7 +278,8 @@ def cpu_baseline(b: Bench, min_seconds: float = 10.0) -> dict:
             "single_thread": {"value": round(one * reps1 / dt1 / 1e9, 4), "unit": "GB/s",
                               "sample": f"layer 0, sequence 0 (all {b.shape.num_q_heads} "
                                         f"heads), {reps1} time(s) in {dt1:.1f} s"},
-            "cpu_model": cpu_model()}
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
 def cpu_model() -> str:
