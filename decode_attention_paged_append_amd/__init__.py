@@ -545,7 +545,7 @@ def decode_window_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks, wi
 def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_lens, scale, window,
                                   out, k_scale=None, v_scale=None, workspace=None, int4=False):
     """Decode attention over each sequence's last `window` positions (0: all);
-    any cache format, scales for int8 / fp8 (see pa_paged_decode_attention_window)."""
+    any cache format, scales for int8 / fp8 / int4 (see pa_paged_decode_attention_window)."""
     lib = library()
     desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
     s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out, int4)

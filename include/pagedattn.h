@@ -275,7 +275,7 @@ pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, vo
  * workspace.  When the partition covers the whole table width
  * (partition_tokens >= max_blocks_per_seq * BS) the result is final and is
  * written to out directly; otherwise pa_lse_merge must follow.  k_scale and
- * v_scale are used only for a quantized (int8, fp8) cache (NULL otherwise). */
+ * v_scale are used only for a quantized (int8, fp8, int4) cache (NULL otherwise). */
 pa_status pa_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
                                const void* k_scale, const void* v_scale,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
