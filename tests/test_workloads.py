@@ -1,4 +1,7 @@
-"""Byte counts the bench reports, on hand-made layouts (CPU only)."""
+"""Byte counts the bench reports, on hand-made layouts, and its one-GPU guard
+(CPU only)."""
+import os
+
 import workloads as W
 
 
@@ -31,3 +34,16 @@ def test_unique_bytes_of_quantized_caches_carry_scales():
     assert i8 == 40 * 2 * 2 * (64 + 2)
     i4 = W.unique_kv_bytes_per_layer_step(_shape("i4"), lay)
     assert i4 == 40 * 2 * 2 * (32 + 2 * 2)
+
+
+def test_bench_rejects_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus above 1 exits with a message before
+    touching a device."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in r.stdout + r.stderr
