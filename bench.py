@@ -293,6 +293,49 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def write_traffic_record(counter_dir: str) -> dict:
+    """Rebuild the traffic record from the four rocprofv3 --pmc runs listed in
+    the headline counters summary: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the headline attention kernel, each scaled by what the same
+    counter reads for a 1 GiB device copy (2^30 bytes read and written).
+    counter_dir holds pmc_fetch/, pmc_write/, pmc_copy_fetch/ and
+    pmc_copy_write/ as rocprofv3 wrote them.  The record carries the hash of
+    the kernel sources it was taken on."""
+    import csv
+    import glob
+
+    def mean_per_dispatch(sub, counter, kernel):
+        files = glob.glob(os.path.join(counter_dir, sub, "**", "*counter_collection.csv"),
+                          recursive=True)
+        if not files:
+            raise FileNotFoundError(f"no counter CSV under {os.path.join(counter_dir, sub)}")
+        per = {}
+        with open(files[0]) as f:
+            for r in csv.DictReader(f):
+                if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not per:
+            raise ValueError(f"no {counter} samples of {kernel} in {files[0]}")
+        return sum(per.values()) / len(per)
+
+    fetch = mean_per_dispatch("pmc_fetch", "FETCH_SIZE", "decode_partition_kernel")
+    write = mean_per_dispatch("pmc_write", "WRITE_SIZE", "decode_partition_kernel")
+    cf = mean_per_dispatch("pmc_copy_fetch", "FETCH_SIZE", "copy")
+    cw = mean_per_dispatch("pmc_copy_write", "WRITE_SIZE", "copy")
+    ff, fw = 2**30 / (cf * 1024), 2**30 / (cw * 1024)
+    rec = {"kernel": "decode_partition_kernel<F16,128,16,1,4>",
+           "workload": "llama2-7b-f16 16x4096, fused append",
+           "bench_workload": "llama2-7b-f16",
+           "kernel_source_sha256": kernel_source_hash(),
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "copy_fetch_factor": ff, "copy_write_factor": fw,
+           "traffic_bytes_per_launch": round(fetch * 1024 * ff) + round(write * 1024 * fw)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
 def traffic_block(workload: str, default_launch: bool):
     """HBM bytes per launch measured with rocprofv3 counters, if they were taken
     on this workload's default launch and the current kernel sources (else
@@ -628,7 +671,13 @@ def main():
                     help="only time the HBM read-rate probe over 4 GiB (also random runs of "
                          "2-16 adjacent chunks) and exit")
     ap.add_argument("--no-read-probe", action="store_true")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="only rebuild the headline traffic record from the four rocprofv3 "
+                         "--pmc runs under DIR (no GPU) and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(write_traffic_record(args.traffic_from)))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
