@@ -66,3 +66,34 @@ def test_decode_step_window_matches_oracle(fmt, hq, hkv, d, bs, window, orc):
         shape.scale, window, bf16=fmt == "bf16", int4=int4, num_threads=8, lib=orc, **oscales)
     assert torch.isfinite(out).all()
     assert max_abs_err(out, ref) <= TOL["i8" if int4 else fmt]
+
+
+def test_decode_step_window_full_size(orc):
+    """The benchmark's windowed step at full size: Llama-3-8B layer shape
+    (32 q / 8 KV heads, fp16, block 16), 16 sequences of 16384 positions, a
+    4096-token window, the library's plan; the new rows bit-exact, sampled
+    outputs within tolerance."""
+    ctx = [16384] * 16
+    bs = 16
+    print("decode_step_window full size", flush=True)
+    shape, lay, case = make("f16", 32, 8, 128, bs, ctx, seed=19, spare_blocks=0,
+                            poison_new=True)
+    kh, vh = host(case.k_cache).copy(), host(case.v_cache).copy()
+    q, kc, vc, kn, vn, bt, ctx_t = to_dev(case.q, case.k_cache, case.v_cache, case.k_new,
+                                          case.v_new, lay.block_tables, lay.context_lens)
+    out = torch.empty_like(q)
+    pa.decode_step_window(q, kn, vn, kc, vc, bt, ctx_t, shape.scale, 4096, out)
+    torch.cuda.synchronize()
+    slots = oracle.decode_slot_mapping(host(lay.block_tables), host(lay.context_lens), bs)
+    oracle.kv_append(host(case.k_new), host(case.v_new), slots, kh, vh)
+    b, o = torch.as_tensor(slots // bs), torch.as_tensor(slots % bs)
+    assert np.array_equal(host(kc[b.to(dev()), :, o.to(dev())]), kh[slots // bs, :, slots % bs])
+    assert np.array_equal(host(vc[b.to(dev()), :, o.to(dev())]), vh[slots // bs, :, slots % bs])
+    rng = np.random.default_rng(13)
+    pairs = [(s, 0) for s in range(16)] + [(int(rng.integers(16)), int(rng.integers(32)))
+                                           for _ in range(16)]
+    ref = oracle.paged_decode_attention_window(
+        host(case.q), kh, vh, host(lay.block_tables), host(lay.context_lens), shape.scale, 4096,
+        pairs=pairs, num_threads=8, lib=orc)
+    assert torch.isfinite(out).all()
+    assert max_abs_err(out, ref, pairs) <= TOL["f16"]
