@@ -655,7 +655,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 100 warm-up steps (0.5 s of the headline): after 5, some runs still
+    # had a slow transient (6246 against 6403-6431 GB/s after 100 or 300)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=W.LLAMA2_7B.name,
                     choices=sorted(W.SHAPES) + ["block-pool"] + sorted(PREFILL_WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="0: the workload's own layer count")
