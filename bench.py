@@ -293,7 +293,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def write_traffic_record(counter_dir: str) -> dict:
+def write_traffic_record(counter_dir: str, out_path: str = TRAFFIC_FILE) -> dict:
     """Rebuild the traffic record from the four rocprofv3 --pmc runs listed in
     the headline counters summary: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch) of the headline attention kernel, each scaled by what the same
@@ -330,7 +330,7 @@ def write_traffic_record(counter_dir: str) -> dict:
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "copy_fetch_factor": ff, "copy_write_factor": fw,
            "traffic_bytes_per_launch": round(fetch * 1024 * ff) + round(write * 1024 * fw)}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     return rec
