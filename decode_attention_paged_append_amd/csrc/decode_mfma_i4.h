@@ -67,6 +67,12 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   constexpr int VE = D / 16;              // value MFMAs per column set
   constexpr int CS = GC / 4;              // column sets
   constexpr int CHUNKS = D / 8;           // 16-byte chunks per fp16 row in LDS
+  // K chunk c of row r sits at kslot(c ^ (r % CHUNKS)): bit 1 flipped in each
+  // row's upper half, so the 4 lanes of each of two rows that write chunks
+  // w, w+4, w+8, w+12 of their rows fall on distinct banks (they collided in
+  // pairs: 2.7-3.2 conflict cycles per LDS instruction); the A-layout reads
+  // stay conflict-free.
+  auto kslot = [](int x) { return x ^ ((x >> 2) & 2); };
   constexpr int K_LPR = ROWB / 16;        // lanes per row in a K load
   constexpr int TPI = GC == 4 ? 2 : 1;    // tiles fetched per loop iteration
   static_assert(GC == 4 || GC == 8, "four or eight heads per workgroup");
@@ -225,7 +231,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     const int nvalid = raw.nvalid;
     const int nlow = raw.nlow;
 
-    // ---- K tile -> LDS as subnormal codes, chunk c of row r at c ^ (r % CHUNKS)
+    // ---- K tile -> LDS as subnormal codes, chunk c of row r at kslot(c ^ (r % CHUNKS))
     {
       const int r = lane / K_LPR;
       const int c0 = 4 * (lane % K_LPR);
@@ -233,7 +239,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
       for (int w = 0; w < 4; ++w) {
         const uint32_t x = raw.k[w];
         const uint32_t lo = x & kNibbles, hi = (x >> 4) & kNibbles;
-        ktile[r * CHUNKS + ((c0 + w) ^ (r % CHUNKS))] =
+        ktile[r * CHUNKS + kslot((c0 + w) ^ (r % CHUNKS))] =
             u32x4{__builtin_amdgcn_perm(hi, lo, i4_sel(0)), __builtin_amdgcn_perm(hi, lo, i4_sel(1)),
                   __builtin_amdgcn_perm(hi, lo, i4_sel(2)), __builtin_amdgcn_perm(hi, lo, i4_sel(3))};
       }
@@ -262,7 +268,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
 
     u32x4 ka[KG];
 #pragma unroll
-    for (int c = 0; c < KG; ++c) ka[c] = ktile[n * CHUNKS + ((4 * c + g) ^ (n % CHUNKS))];
+    for (int c = 0; c < KG; ++c) ka[c] = ktile[n * CHUNKS + kslot((4 * c + g) ^ (n % CHUNKS))];
 
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) {
@@ -428,6 +434,12 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   constexpr int KG = D / kInt4Group;      // scale groups per row = score MFMAs
   constexpr int VE = D / 16;              // value MFMAs (two per group)
   constexpr int CHUNKS = D / 8;           // 16-byte chunks per fp16 row in LDS
+  // K chunk c of row r sits at kslot(c ^ (r % CHUNKS)): bit 1 flipped in each
+  // row's upper half, so the 4 lanes of each of two rows that write chunks
+  // w, w+4, w+8, w+12 of their rows fall on distinct banks (they collided in
+  // pairs: 2.7-3.2 conflict cycles per LDS instruction); the A-layout reads
+  // stay conflict-free.
+  auto kslot = [](int x) { return x ^ ((x >> 2) & 2); };
   constexpr int K_LPR = ROWB / 16;        // lanes per row in a K or V load
   constexpr int ACC_STRIDE = D + 4;       // floats per head row of the merge buffer
   constexpr int TPI = 2;                  // tiles fetched per loop iteration
@@ -572,7 +584,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     const int nlow = raw.nlow;
 
     // ---- K and V tiles -> LDS as subnormal codes.  K's 16-byte chunk c of
-    // row r sits at c ^ (r % CHUNKS) (read whole rows), V's at c ^ (r & 7)
+    // row r sits at kslot(c ^ (r % CHUNKS)) (read whole rows), V's at c ^ (r & 7)
     // (read transposed).
     {
       const int r = lane / K_LPR;
@@ -582,7 +594,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
       for (int w = 0; w < 4; ++w) {
         const uint32_t xk = raw.k[w];
         const uint32_t klo = xk & kNibbles, khi = (xk >> 4) & kNibbles;
-        ktile[r * CHUNKS + ((c0 + w) ^ (r % CHUNKS))] =
+        ktile[r * CHUNKS + kslot((c0 + w) ^ (r % CHUNKS))] =
             u32x4{__builtin_amdgcn_perm(khi, klo, i4_sel(0)), __builtin_amdgcn_perm(khi, klo, i4_sel(1)),
                   __builtin_amdgcn_perm(khi, klo, i4_sel(2)), __builtin_amdgcn_perm(khi, klo, i4_sel(3))};
         // V: odd dims as 16 x code (high nibbles masked in place), taken out
@@ -600,7 +612,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
 
     u32x4 ka[KG];
 #pragma unroll
-    for (int c = 0; c < KG; ++c) ka[c] = ktile[n * CHUNKS + ((4 * c + g) ^ (n % CHUNKS))];
+    for (int c = 0; c < KG; ++c) ka[c] = ktile[n * CHUNKS + kslot((4 * c + g) ^ (n % CHUNKS))];
     // scales of tokens 4g .. 4g+3 x KG groups (one address per 16 lanes)
     uint32_t ks[8], vs[8];
     {
