@@ -584,7 +584,8 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     const int nlow = raw.nlow;
 
     // ---- K and V tiles -> LDS as subnormal codes.  K's 16-byte chunk c of
-    // row r sits at kslot(c ^ (r % CHUNKS)) (read whole rows), V's at c ^ (r & 7)
+    // row r sits at kslot(c ^ (r % CHUNKS)) (read whole rows), V's at
+    // kslot(c ^ (r & 7))
     // (read transposed).
     {
       const int r = lane / K_LPR;
@@ -601,7 +602,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
         // again with the 2^24 of the epilogue
         const uint32_t xv = raw.v[w];
         const uint32_t vlo = xv & kNibbles, vhi = xv & (kNibbles << 4);
-        vtile[r * CHUNKS + ((c0 + w) ^ (r & 7))] =
+        vtile[r * CHUNKS + kslot((c0 + w) ^ (r & 7))] =
             u32x4{__builtin_amdgcn_perm(vhi, vlo, i4_sel(0)), __builtin_amdgcn_perm(vhi, vlo, i4_sel(1)),
                   __builtin_amdgcn_perm(vhi, vlo, i4_sel(2)), __builtin_amdgcn_perm(vhi, vlo, i4_sel(3))};
       }
@@ -688,7 +689,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
       for (int h = 0; h < 2; ++h) {
         const int e = 2 * c + h;
         const int ch = 2 * e + (vq >> 1);
-        const int off = vrow * D + (ch ^ (vrow & 7)) * 8 + (vq & 1) * 4;
+        const int off = vrow * D + kslot(ch ^ (vrow & 7)) * 8 + (vq & 1) * 4;
         const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(vt + off));
         o[e] = Mfma<Fmt::F16>::pv(__builtin_bit_cast(u32x2, va), pb, o[e]);
