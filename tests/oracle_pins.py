@@ -676,6 +676,76 @@ def pin_int4_attention_dequantizes_exactly(lib):
             assert np.array_equal(kso[s_, i], ks[bt[s_, b_], :, o])
 
 
+# ---------------------------------------------------------------- quantizing appends: placement
+
+def _dequant_rows(kind, codes, scales):
+    """Test-side numpy decoding of stored rows: codes [..., D] (int4: [..., D/2]
+    packed) times their scales ([...] or, for int4, [..., D/32]), in float64."""
+    if kind == "int8":
+        return codes.astype(np.float64) * scales.astype(np.float64)[..., None]
+    if kind == "fp8":
+        return _e4m3_table()[codes] * scales.astype(np.float64)[..., None]
+    return _int4_unpack(codes).astype(np.float64) * np.repeat(scales.astype(np.float64), 32,
+                                                              axis=-1)
+
+
+def _within_quantizer_bound(kind, x, deq, scales):
+    """Each quantizer's stated error bound (the pins above): half a code step,
+    plus the binary16 rounding of the scale (fp8: half an E4M3 step relative,
+    or half a subnormal step)."""
+    x = x.astype(np.float64)
+    if kind == "fp8":
+        s = scales.astype(np.float64)[..., None]
+        return np.all(np.abs(x - deq) <= np.abs(x) * (2.0 ** -4 + 2.0 ** -10) + s * 2.0 ** -10 *
+                      1.0001)
+    s = scales.astype(np.float64)
+    s = s[..., None] if kind == "int8" else np.repeat(s, 32, axis=-1)
+    return np.all(np.abs(x - deq) <= s / 2 * (1 + 1e-6) + np.abs(x) * 2.0 ** -10)
+
+
+def pin_quantizing_appends_place_source_rows(lib):
+    """Every quantizing append stores token t's K row in the K pool and its V
+    row in the V pool at (slot // block_size, slot % block_size), for every KV
+    head ([viz] "PagedAttention: the cache in blocks": a slot names one
+    position of one block; [notes] "Quantized KV cache": the cache holds the
+    rows in fewer bits).  Slots are a seeded permutation with -1 pads, K and V
+    are drawn at different magnitudes, and decoding each stored row must land
+    within the quantizer's bound of the row it came from.  A slot of -1 and
+    every slot the call does not name keep their bytes."""
+    rng = np.random.default_rng(61)
+    nb, hkv, bs, d = 12, 3, 4, 64
+    for kind in ("int8", "fp8", "int4"):
+        t_real = 17
+        slots = rng.permutation(nb * bs)[:t_real].astype(np.int64)
+        slots = np.insert(slots, [0, 5, t_real], -1)      # pads at the front, middle and end
+        t = slots.shape[0]
+        k_new = (rng.standard_normal((t, hkv, d)) * 3.0).astype(np.float16)
+        v_new = (rng.standard_normal((t, hkv, d)) * 0.25 + 0.5).astype(np.float16)
+        cdt, cw = (np.int8, d) if kind == "int8" else (np.uint8, d if kind == "fp8" else d // 2)
+        sshape = (nb, hkv, bs) if kind != "int4" else (nb, hkv, bs, d // 32)
+        kq = rng.integers(-100, 100, (nb, hkv, bs, cw)).astype(cdt)
+        vq = rng.integers(-100, 100, (nb, hkv, bs, cw)).astype(cdt)
+        ks = rng.uniform(1, 2, sshape).astype(np.float16)
+        vs = rng.uniform(3, 4, sshape).astype(np.float16)
+        before = [a.copy() for a in (kq, vq, ks, vs)]
+        fn = {"int8": oracle.kv_append_int8, "fp8": oracle.kv_append_fp8,
+              "int4": oracle.kv_append_int4}[kind]
+        fn(k_new, v_new, slots, kq, vq, ks, vs, lib=lib)
+        written = np.zeros((nb, bs), bool)
+        for i, slot in enumerate(slots):
+            if slot < 0:
+                continue
+            b, o = divmod(int(slot), bs)
+            written[b, o] = True
+            for src, codes, sc in ((k_new, kq, ks), (v_new, vq, vs)):
+                deq = _dequant_rows(kind, codes[b, :, o], sc[b, :, o])
+                assert _within_quantizer_bound(kind, src[i], deq, sc[b, :, o]), (kind, i, slot)
+        for now, old in zip((kq, vq, ks, vs), before):
+            keep = np.broadcast_to(~written[:, None, :].reshape(nb, 1, bs, *([1] * (now.ndim - 3))),
+                                   now.shape)
+            assert np.array_equal(now[keep], old[keep]), kind
+
+
 # ---------------------------------------------------------------- prefill
 
 def _sdpa64_rows(q, K, V, scale, mask):

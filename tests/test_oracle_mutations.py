@@ -9,6 +9,13 @@ import pytest
 import oracle
 import oracle_pins
 
+# the store of one quantized (token, head) row, as each quantizing append writes it
+_QROW = ("int64_t block = slots[t] {div} block_size, off = slots[t] {mod} block_size;\n"
+         "    for (int32_t h = 0; h < num_kv_heads; ++h) {{\n"
+         "      size_t src = ((size_t)t * num_kv_heads + h) * head_dim;\n"
+         "      size_t srow = ((size_t)block * num_kv_heads + h) * block_size + off;\n"
+         "      oracle_quantize_row_{kind}(")
+
 MUTANTS = {
     "scale dropped from the scores": ("z[i] = scale * dot;", "z[i] = dot;"),
     "GQA head mapped round-robin": (
@@ -60,6 +67,19 @@ MUTANTS = {
     "int4 range 8": ("volatile float ratio = a / 7.0f;", "volatile float ratio = a / 8.0f;"),
     "int4 one scale per row": ("size_t g = row * (head_dim / OR_I4_GROUP) + d / OR_I4_GROUP;",
                                "size_t g = row * (head_dim / OR_I4_GROUP);"),
+    "int8 V pool quantized from the K row": ("oracle_quantize_row_int8(v_new + src",
+                                             "oracle_quantize_row_int8(k_new + src"),
+    "fp8 K pool quantized from the V row": ("oracle_quantize_row_fp8(k_new + src",
+                                            "oracle_quantize_row_fp8(v_new + src"),
+    "int4 K pool quantized from the V row": ("oracle_quantize_row_int4(k_new + src",
+                                             "oracle_quantize_row_int4(v_new + src"),
+    **{f"{kind} append block/offset swapped": (
+        _QROW.format(div="/", mod="%", kind=kind), _QROW.format(div="%", mod="/", kind=kind))
+       for kind in ("int8", "fp8", "int4")},
+    **{f"{kind} append writes the pad slot's token to the next slot": (
+        f"if (slots[t] < 0) continue;\n    int64_t block = slots[t] / block_size, off = slots[t] % block_size;\n    for (int32_t h = 0; h < num_kv_heads; ++h) {{\n      size_t src = ((size_t)t * num_kv_heads + h) * head_dim;\n      size_t srow = ((size_t)block * num_kv_heads + h) * block_size + off;\n      oracle_quantize_row_{kind}(",
+        f"if (slots[t] < 0) continue;\n    int64_t block = slots[t] / block_size, off = slots[t] % block_size;\n    for (int32_t h = 0; h < num_kv_heads; ++h) {{\n      size_t src = ((size_t)(t > 0 && slots[t - 1] < 0 ? t - 1 : t) * num_kv_heads + h) * head_dim;\n      size_t srow = ((size_t)block * num_kv_heads + h) * block_size + off;\n      oracle_quantize_row_{kind}(")
+       for kind in ("int8", "fp8", "int4")},
     "dot product over half the head": (
         "for (int32_t d = 0; d < head_dim; ++d) dot += q[d] * K[i * head_dim + d];",
         "for (int32_t d = 0; d < head_dim / 2; ++d) dot += q[d] * K[i * head_dim + d];"),
