@@ -164,6 +164,31 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _nbytes(t: torch.Tensor | None) -> int:
+    """Size in bytes of a workspace tensor of any dtype (0 for None)."""
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _check_pools(k_cache, v_cache, k_scale=None, v_scale=None, int4=False):
+    """The V pool must be the K pool's twin (shape and dtype), since the
+    library sizes both from one descriptor; a quantized cache (int8, fp8,
+    int4) needs fp16 scales [NB, Hkv, BS] (int4: [NB, Hkv, BS, D/32]) for
+    both pools.  Raises ValueError before anything reaches the GPU."""
+    if k_cache.dim() != 4:
+        raise ValueError(f"k_cache must be [NB, Hkv, BS, D], got {tuple(k_cache.shape)}")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError(f"v_cache {tuple(v_cache.shape)} {v_cache.dtype} must match k_cache "
+                         f"{tuple(k_cache.shape)} {k_cache.dtype}")
+    if int4 or k_cache.dtype in QUANTIZED:
+        want = tuple(k_cache.shape[:3]) + ((2 * k_cache.shape[3] // INT4_GROUP,) if int4 else ())
+        for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if sc is None:
+                raise ValueError(f"a quantized cache needs {name}")
+            if tuple(sc.shape) != want or sc.dtype != torch.float16:
+                raise ValueError(f"{name} must be float16 {want}, got {sc.dtype} "
+                                 f"{tuple(sc.shape)}")
+
+
 def abi_version() -> int:
     return library().pa_abi_version()
 
@@ -202,8 +227,7 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache):
     """Scatter k_new/v_new [T, Hkv, D] into the [NB, Hkv, BS, D] pools."""
     lib = library()
     desc = CacheDesc.of(k_cache)
-    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
-        raise ValueError("k_cache and v_cache must match")
+    _check_pools(k_cache, v_cache)
     t = slot_mapping.numel()
     if k_new.shape != (t, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
         raise ValueError(f"k_new/v_new must be [{t}, {desc.num_kv_heads}, {desc.head_dim}]")
@@ -220,8 +244,7 @@ def kv_append_int8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scal
     t = slot_mapping.numel()
     if k_new.shape != (t, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
         raise ValueError(f"k_new/v_new must be [{t}, {desc.num_kv_heads}, {desc.head_dim}]")
-    if k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_scale.shape:
-        raise ValueError("scales must be [NB, Hkv, BS]")
+    _check_pools(k_cache, v_cache, k_scale, v_scale)
     _ok(lib.pa_kv_append_int8(_dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),
                               _dev(slot_mapping, "slot_mapping", torch.int64), t,
                               _dev(k_cache, "k_cache", torch.int8, 4),
@@ -252,9 +275,7 @@ def kv_append_int4(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scal
     t = slot_mapping.numel()
     if k_new.shape != (t, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
         raise ValueError(f"k_new/v_new must be [{t}, {desc.num_kv_heads}, {desc.head_dim}]")
-    want = (*k_cache.shape[:3], desc.head_dim // INT4_GROUP)
-    if tuple(k_scale.shape) != want or tuple(v_scale.shape) != want:
-        raise ValueError(f"scales must be {want}")
+    _check_pools(k_cache, v_cache, k_scale, v_scale, int4=True)
     _ok(lib.pa_kv_append_int4(_dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),
                               _dev(slot_mapping, "slot_mapping", torch.int64), t,
                               _dev(k_cache, "k_cache", torch.uint8, 4),
@@ -271,8 +292,7 @@ def kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale
     t = slot_mapping.numel()
     if k_new.shape != (t, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
         raise ValueError(f"k_new/v_new must be [{t}, {desc.num_kv_heads}, {desc.head_dim}]")
-    if k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_scale.shape:
-        raise ValueError("scales must be [NB, Hkv, BS]")
+    _check_pools(k_cache, v_cache, k_scale, v_scale)
     e4m3 = torch.float8_e4m3fn
     _ok(lib.pa_kv_append_fp8(_dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16),
                              _dev(slot_mapping, "slot_mapping", torch.int64), t,
@@ -303,7 +323,13 @@ def _workspace(ws, nbytes, device):
     return ws
 
 
-def _shapes(q, k_cache, block_tables, context_lens, out, int4=False):
+def _shapes(q, k_cache, v_cache, block_tables, context_lens, out, int4=False, k_scale=None,
+            v_scale=None):
+    """(S, Hq, max_blocks) of a decode call, after checking the pools
+    (_check_pools), q / out / table / length shapes and head_dim."""
+    _check_pools(k_cache, v_cache, k_scale, v_scale, int4)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [S, Hq, D], got {tuple(q.shape)}")
     s, hq, d = q.shape
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
@@ -319,14 +345,14 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
     """out[s,h] = softmax(q[s,h] . K_s^T * scale) . V_s over the paged cache."""
     lib = library()
     desc = CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out)
     need = decode_workspace_bytes(desc, s, hq, maxb)
     ws = _workspace(workspace, need, q.device)
     _ok(lib.pa_paged_decode_attention(
         _dev(q, "q", k_cache.dtype, 3), _dev(k_cache, "k_cache", ndim=4),
         _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(block_tables, "block_tables", torch.int32),
         maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
-        _dev(out, "out", k_cache.dtype), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _dev(out, "out", k_cache.dtype), ctypes.byref(desc), _dev(ws, "workspace"), _nbytes(ws),
         _stream(q)), lib)
     return out
 
@@ -336,7 +362,8 @@ def paged_decode_attention_int8(q, k_cache, v_cache, k_scale, v_scale, block_tab
     """Decode attention over an int8 cache with fp16 per-(token, head) scales."""
     lib = library()
     desc = CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out, False, k_scale,
+                          v_scale)
     need = decode_workspace_bytes(desc, s, hq, maxb)
     ws = _workspace(workspace, need, q.device)
     _ok(lib.pa_paged_decode_attention_int8(
@@ -344,7 +371,7 @@ def paged_decode_attention_int8(q, k_cache, v_cache, k_scale, v_scale, block_tab
         _dev(v_cache, "v_cache", torch.int8, 4), _dev(k_scale, "k_scale", torch.float16),
         _dev(v_scale, "v_scale", torch.float16), _dev(block_tables, "block_tables", torch.int32),
         maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
-        _dev(out, "out", torch.float16), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _dev(out, "out", torch.float16), ctypes.byref(desc), _dev(ws, "workspace"), _nbytes(ws),
         _stream(q)), lib)
     return out
 
@@ -354,7 +381,8 @@ def paged_decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tabl
     """Decode attention over an fp8 (E4M3) cache with fp16 per-(token, head) scales."""
     lib = library()
     desc = CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out, False, k_scale,
+                          v_scale)
     need = decode_workspace_bytes(desc, s, hq, maxb)
     ws = _workspace(workspace, need, q.device)
     e4m3 = torch.float8_e4m3fn
@@ -363,7 +391,7 @@ def paged_decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tabl
         _dev(v_cache, "v_cache", e4m3, 4), _dev(k_scale, "k_scale", torch.float16),
         _dev(v_scale, "v_scale", torch.float16), _dev(block_tables, "block_tables", torch.int32),
         maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
-        _dev(out, "out", torch.float16), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _dev(out, "out", torch.float16), ctypes.byref(desc), _dev(ws, "workspace"), _nbytes(ws),
         _stream(q)), lib)
     return out
 
@@ -374,12 +402,8 @@ def paged_decode_attention_int4(q, k_cache, v_cache, k_scale, v_scale, block_tab
     fp16 scales [NB, Hkv, BS, D/32])."""
     lib = library()
     desc = int4_desc(k_cache)
-    s, hq, d = q.shape
-    if out.shape != q.shape or d != desc.head_dim:
-        raise ValueError("q and out must be [S, Hq, D] with the cache's D")
-    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.numel() != s:
-        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
-    maxb = block_tables.shape[1]
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out, True, k_scale,
+                          v_scale)
     need = decode_workspace_bytes(desc, s, hq, maxb)
     ws = _workspace(workspace, need, q.device)
     _ok(lib.pa_paged_decode_attention_int4(
@@ -387,7 +411,7 @@ def paged_decode_attention_int4(q, k_cache, v_cache, k_scale, v_scale, block_tab
         _dev(v_cache, "v_cache", torch.uint8, 4), _dev(k_scale, "k_scale", torch.float16),
         _dev(v_scale, "v_scale", torch.float16), _dev(block_tables, "block_tables", torch.int32),
         maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
-        _dev(out, "out", torch.float16), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _dev(out, "out", torch.float16), ctypes.byref(desc), _dev(ws, "workspace"), _nbytes(ws),
         _stream(q)), lib)
     return out
 
@@ -399,7 +423,7 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, s
     all context_lens[s] rows (see pa_decode_step)."""
     lib = library()
     desc = CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out)
     if k_new.shape != (s, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
         raise ValueError(f"k_new/v_new must be [{s}, {desc.num_kv_heads}, {desc.head_dim}]")
     need = decode_workspace_bytes(desc, s, hq, maxb)
@@ -409,7 +433,7 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, s
         _dev(v_new, "v_new", k_cache.dtype), _dev(k_cache, "k_cache", ndim=4),
         _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(block_tables, "block_tables", torch.int32),
         maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
-        _dev(out, "out", k_cache.dtype), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _dev(out, "out", k_cache.dtype), ctypes.byref(desc), _dev(ws, "workspace"), _nbytes(ws),
         _stream(q)), lib)
     return out
 
@@ -420,7 +444,8 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     int4: uint8 pools [NB, Hkv, BS, D/2] hold int4 codes."""
     lib = library()
     desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out, int4)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out, int4, k_scale,
+                          v_scale)
     q_dtype = torch.float16 if int4 or k_cache.dtype in QUANTIZED else k_cache.dtype
     _ok(lib.pa_decode_partitions(
         _dev(q, "q", q_dtype, 3), _dev(k_cache, "k_cache", ndim=4),
@@ -428,7 +453,7 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, ou
         _dev(v_scale, "v_scale", torch.float16), _dev(block_tables, "block_tables", torch.int32),
         maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
         int(partition_tokens), _dev(out, "out", q_dtype), ctypes.byref(desc),
-        _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel(), _stream(q)),
+        _dev(workspace, "workspace"), _nbytes(workspace), _stream(q)),
         lib)
     return out
 
@@ -438,7 +463,7 @@ def decode_step_partitions(q, k_new, v_new, k_cache, v_cache, block_tables, cont
     """Phase 1 of decode_step with an explicit partition length."""
     lib = library()
     desc = CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out)
     if k_new.shape != (s, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
         raise ValueError(f"k_new/v_new must be [{s}, {desc.num_kv_heads}, {desc.head_dim}]")
     _ok(lib.pa_decode_step_partitions(
@@ -447,7 +472,7 @@ def decode_step_partitions(q, k_new, v_new, k_cache, v_cache, block_tables, cont
         _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(block_tables, "block_tables", torch.int32),
         maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
         int(partition_tokens), _dev(out, "out", k_cache.dtype), ctypes.byref(desc),
-        _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel(), _stream(q)),
+        _dev(workspace, "workspace"), _nbytes(workspace), _stream(q)),
         lib)
     return out
 
@@ -459,7 +484,8 @@ def _quant_step_args(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_
     desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
     if desc.dtype not in (DTYPE_CODE[torch.int8], DTYPE_CODE[torch.float8_e4m3fn], INT4):
         raise ValueError("a quantized decode step needs an int8, fp8 or int4 cache")
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out, int4)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out, int4, k_scale,
+                          v_scale)
     if k_new.shape != (s, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
         raise ValueError(f"k_new/v_new must be [{s}, {desc.num_kv_heads}, {desc.head_dim}]")
     ptrs = (_dev(q, "q", torch.float16, 3), _dev(k_new, "k_new", torch.float16),
@@ -483,7 +509,7 @@ def decode_step_quant(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block
                                                v_scale, block_tables, context_lens, out, int4)
     ws = _workspace(workspace, decode_workspace_bytes(desc, s, hq, maxb), q.device)
     _ok(lib.pa_decode_step_quant(*ptrs, float(scale), _dev(out, "out", torch.float16),
-                                 ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+                                 ctypes.byref(desc), _dev(ws, "workspace"), _nbytes(ws),
                                  _stream(q)), lib)
     return out
 
@@ -497,8 +523,7 @@ def decode_step_partitions_quant(q, k_new, v_new, k_cache, v_cache, k_scale, v_s
                                            block_tables, context_lens, out, int4)
     _ok(lib.pa_decode_step_partitions_quant(
         *ptrs, float(scale), int(partition_tokens), _dev(out, "out", torch.float16),
-        ctypes.byref(desc), _dev(workspace, "workspace"),
-        0 if workspace is None else workspace.numel(), _stream(q)), lib)
+        ctypes.byref(desc), _dev(workspace, "workspace"), _nbytes(workspace), _stream(q)), lib)
     return out
 
 
@@ -506,7 +531,7 @@ def lse_merge(workspace, context_lens, num_q_heads, head_dim, max_blocks, block_
               partition_tokens, out):
     """Phase 2: merge the partials phase 1 left in the workspace into out."""
     lib = library()
-    _ok(lib.pa_lse_merge(_dev(workspace, "workspace"), workspace.numel(),
+    _ok(lib.pa_lse_merge(_dev(workspace, "workspace"), _nbytes(workspace),
                          _dev(context_lens, "context_lens", torch.int32), context_lens.numel(),
                          num_q_heads, head_dim, max_blocks, block_size, int(partition_tokens),
                          DTYPE_CODE[out.dtype], _dev(out, "out"), _stream(out)), lib)
@@ -521,7 +546,19 @@ def gather_kv(k_cache, v_cache, block_tables, context_lens, k_out, v_out, k_scal
     rows past a length untouched."""
     lib = library()
     desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
+    _check_pools(k_cache, v_cache, k_scale, v_scale, int4)
+    if block_tables.dim() != 2 or context_lens.numel() != block_tables.shape[0]:
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
     s, maxb = block_tables.shape
+    quant = int4 or k_cache.dtype in QUANTIZED
+    if quant and (k_scale_out is None) != (v_scale_out is None):
+        raise ValueError("k_scale_out and v_scale_out go together")
+    if quant and k_scale_out is not None:
+        swant = (s, maxb * desc.block_size, desc.num_kv_heads) + (
+            (desc.head_dim // INT4_GROUP,) if int4 else ())
+        for name, t in (("k_scale_out", k_scale_out), ("v_scale_out", v_scale_out)):
+            if tuple(t.shape) != swant or t.dtype != torch.float16:
+                raise ValueError(f"{name} must be float16 {swant}")
     want = (s, maxb * desc.block_size, desc.num_kv_heads, k_cache.shape[3])
     if tuple(k_out.shape) != want or tuple(v_out.shape) != want:
         raise ValueError(f"k_out/v_out must be {want}")
@@ -548,7 +585,8 @@ def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_len
     any cache format, scales for int8 / fp8 / int4 (see pa_paged_decode_attention_window)."""
     lib = library()
     desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out, int4)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out, int4, k_scale,
+                          v_scale)
     quant = int4 or k_cache.dtype in QUANTIZED
     q_dtype = torch.float16 if quant else k_cache.dtype
     need = decode_window_workspace_bytes(desc, s, hq, maxb, int(window))
@@ -560,7 +598,7 @@ def paged_decode_attention_window(q, k_cache, v_cache, block_tables, context_len
         _dev(v_scale, "v_scale", torch.float16) if quant else None,
         _dev(block_tables, "block_tables", torch.int32), maxb,
         _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale), int(window),
-        _dev(out, "out", q_dtype), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _dev(out, "out", q_dtype), ctypes.byref(desc), _dev(ws, "workspace"), _nbytes(ws),
         _stream(q)), lib)
     return out
 
@@ -573,7 +611,8 @@ def decode_step_window(q, k_new, v_new, k_cache, v_cache, block_tables, context_
     attend over the last `window` positions (see pa_decode_step_window)."""
     lib = library()
     desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
-    s, hq, maxb = _shapes(q, k_cache, block_tables, context_lens, out, int4)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out, int4, k_scale,
+                          v_scale)
     quant = int4 or k_cache.dtype in QUANTIZED
     q_dtype = torch.float16 if quant else k_cache.dtype
     if k_new.shape != (s, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
@@ -587,7 +626,7 @@ def decode_step_window(q, k_new, v_new, k_cache, v_cache, block_tables, context_
         _dev(v_scale, "v_scale", torch.float16) if quant else None,
         _dev(block_tables, "block_tables", torch.int32), maxb,
         _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale), int(window),
-        _dev(out, "out", q_dtype), ctypes.byref(desc), _dev(ws, "workspace"), ws.numel(),
+        _dev(out, "out", q_dtype), ctypes.byref(desc), _dev(ws, "workspace"), _nbytes(ws),
         _stream(q)), lib)
     return out
 
@@ -604,6 +643,7 @@ def paged_prefill_attention(q, k_cache, v_cache, block_tables, query_start, cont
     query_start, which synchronizes."""
     lib = library()
     desc = CacheDesc.of(k_cache)
+    _check_pools(k_cache, v_cache)
     if q.dtype != k_cache.dtype or out.dtype != q.dtype:
         raise ValueError("q, caches and out must share one format")
     s = block_tables.shape[0]
@@ -739,6 +779,7 @@ def copy_blocks(k_cache, v_cache, block_pairs, k_scale=None, v_scale=None, int4=
     n = block_pairs.shape[0]
     i8 = int4 or k_cache.dtype in QUANTIZED
     desc = int4_desc(k_cache) if int4 else CacheDesc.of(k_cache)
+    _check_pools(k_cache, v_cache, k_scale, v_scale, int4)
     _ok(lib.pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(k_scale, "k_scale", torch.float16) if i8 else None,
                            _dev(v_scale, "v_scale", torch.float16) if i8 else None,

@@ -2,6 +2,7 @@
 the CPU oracle on the same seeded inputs, and compare."""
 from __future__ import annotations
 
+import os
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -84,23 +85,30 @@ def quantize_pool_gpu(src_k, src_v, layout_blocks, fmt="i8"):
 
 
 def quantize_blocks_oracle(src_k, src_v, blocks, fmt="i8"):
-    """Oracle int8 / fp8 pool holding only the given blocks (others zero)."""
+    """Oracle int8 / fp8 / int4 pool holding only the given blocks (others
+    zero), quantized from the fp16 pools [NB, Hkv, BS, D] on host threads."""
     nb, hkv, bs, d = src_k.shape
     blocks = np.asarray(sorted(set(int(b) for b in blocks)), dtype=np.int64)
-    sk = host(src_k[torch.as_tensor(blocks, device=src_k.device)])   # [n, Hkv, BS, D]
-    sv = host(src_v[torch.as_tensor(blocks, device=src_v.device)])
+    bi = torch.as_tensor(blocks, device=src_k.device)
+    sk = host(src_k[bi])   # [n, Hkv, BS, D]
+    sv = host(src_v[bi])
     rows_k = np.ascontiguousarray(sk.transpose(0, 2, 1, 3).reshape(-1, hkv, d))
     rows_v = np.ascontiguousarray(sv.transpose(0, 2, 1, 3).reshape(-1, hkv, d))
+    del sk, sv
     slots = (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
-    kq = np.zeros((nb, hkv, bs, d), np.int8 if fmt == "i8" else np.uint8)
+    int4 = fmt == "i4"
+    width = d // 2 if int4 else d
+    kq = np.zeros((nb, hkv, bs, width), np.int8 if fmt == "i8" else np.uint8)
     vq = np.zeros_like(kq)
-    ks = np.zeros((nb, hkv, bs), np.float16)
+    ks = np.zeros((nb, hkv, bs) + ((d // 32,) if int4 else ()), np.float16)
     vs = np.zeros_like(ks)
-    append = oracle.kv_append_int8 if fmt == "i8" else oracle.kv_append_fp8
+    append = {"i8": oracle.kv_append_int8, "fp8": oracle.kv_append_fp8,
+              "i4": oracle.kv_append_int4}[fmt]
     # chunks of whole blocks write disjoint slots: run them on host threads
     # (the oracle's C routine runs without the interpreter lock)
     n = rows_k.shape[0]
-    step = -(-max(n // bs, 1) // 8) * bs
+    workers = min(16, os.cpu_count() or 1)
+    step = -(-max(n // bs, 1) // workers) * bs
     spans = [(a, min(a + step, n)) for a in range(0, n, step)]
     with ThreadPoolExecutor(len(spans)) as ex:
         list(ex.map(lambda s: append(rows_k[s[0]:s[1]], rows_v[s[0]:s[1]], slots[s[0]:s[1]],

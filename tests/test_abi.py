@@ -76,6 +76,18 @@ def test_append_argument_checks(lib):
                                 None) == INVALID
 
 
+def test_copy_blocks_argument_checks(lib):
+    """Quantized pools need both scale pointers; a negative count is rejected
+    and an empty one is a no-op (all on the host, before any launch)."""
+    i8 = desc(dtype=3)
+    assert lib.pa_copy_blocks(FAKE, FAKE, None, FAKE, FAKE, 1, ctypes.byref(i8), None) == INVALID
+    assert b"NULL" in lib.pa_last_error()
+    assert lib.pa_copy_blocks(FAKE, FAKE, FAKE, None, FAKE, 1, ctypes.byref(i8), None) == INVALID
+    assert lib.pa_copy_blocks(FAKE, FAKE, None, None, FAKE, -1, ctypes.byref(desc()),
+                              None) == INVALID
+    assert lib.pa_copy_blocks(None, None, None, None, None, 0, ctypes.byref(desc()), None) == OK
+
+
 def test_decode_argument_checks(lib):
     d = desc()
     call = lambda hq, ws, wsb, desc_=d, s=4, maxb=16: lib.pa_paged_decode_attention(

@@ -57,7 +57,7 @@ def test_copy_blocks_bit_exact(fmt, d, bs, hkv):
 def test_copy_blocks_empty_and_checks():
     kc = torch.zeros((4, 1, 16, 64), dtype=torch.float16, device=dev())
     pa.copy_blocks(kc, kc.clone(), np.zeros((0, 2), np.int32))
-    with pytest.raises(pa.PagedAttnError, match="NULL"):
+    with pytest.raises(ValueError, match="k_scale"):      # the library's own NULL check: test_abi
         pa.copy_blocks(kc.to(torch.int8), kc.to(torch.int8), np.array([[0, 1]], np.int32))
 
 

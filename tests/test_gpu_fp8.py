@@ -86,26 +86,23 @@ def test_fp8_decode_matches_oracle(d, bs, hq, hkv):
         assert max_abs_err(out, ref) <= TOL["fp8"], part
 
 
-def test_fp8_full_size_sampled():
+def test_fp8_full_size():
     """Llama-3-8B layer, 64 sequences x 8192 positions in fp8, the library's
-    own plan, on sampled (sequence, head) rows."""
+    own plan: the whole pool bit-exact against the oracle's quantizer and
+    every (sequence, head) output within tolerance of the oracle."""
     shape = W.LLAMA3_8B_FP8
     lay = W.layout_for(shape)
     case = W.make_case(shape, lay, device=dev(), poison=False)
     print("fp8 full size", flush=True)
     kq, vq, ks, vs = quantize_pool_gpu(case.k_cache, case.v_cache, None, "fp8")
-    rng = np.random.default_rng(6)
-    seqs = [0, 29, shape.num_seqs - 1]
-    pairs = [(s, int(rng.integers(shape.num_q_heads))) for s in seqs for _ in range(6)]
-    blocks = lay.block_tables[seqs].flatten()
-    okq, ovq, oks, ovs, used = quantize_blocks_oracle(case.k_cache, case.v_cache,
-                                                      blocks[blocks >= 0], "fp8")
-    ui = torch.as_tensor(used, device=dev())
-    assert host(kq[ui]).tobytes() == okq[used].tobytes()
-    assert host(vs[ui]).tobytes() == ovs[used].tobytes()
+    okq, ovq, oks, ovs, _ = quantize_blocks_oracle(case.k_cache, case.v_cache,
+                                                   range(lay.num_blocks), "fp8")
+    assert host(kq).tobytes() == okq.tobytes() and host(vq).tobytes() == ovq.tobytes()
+    assert host(ks).tobytes() == oks.tobytes() and host(vs).tobytes() == ovs.tobytes()
     bt, ctx = lay.block_tables.to(dev()), lay.context_lens.to(dev())
     out = decode_gpu(case.q, kq, vq, bt, ctx, shape.scale, None, ks, vs)
     ref = oracle.paged_decode_attention(host(case.q), okq, ovq, host(lay.block_tables),
                                         host(lay.context_lens), shape.scale, k_scale=oks,
-                                        v_scale=ovs, pairs=pairs)
-    assert max_abs_err(out, ref, pairs) <= TOL["fp8"]
+                                        v_scale=ovs)
+    assert torch.isfinite(out).all()
+    assert max_abs_err(out, ref) <= TOL["fp8"]

@@ -186,54 +186,27 @@ def test_int4_window_head_columns(hq, bs, orc):
         assert max_abs_err(out, ref) <= TOL_I4, window
 
 
-def test_int4_full_size_sampled(orc):
-    """Llama-3-8B layer, 32 sequences x 8192 positions in int4, the library's
-    own plan, on sampled (sequence, head) rows."""
-    shape = W.Shape("llama3-8b-int4kv-test", "f16", 32, 32, 8, 128, 16)
-    lay = W.carve_layout([8192] * 32, 16, num_blocks=32 * 512, seed=2)
+@pytest.mark.parametrize("shape", [W.LLAMA3_8B_I4, W.LLAMA3_70B_I4], ids=lambda s: s.name)
+def test_int4_full_size(shape, orc):
+    """The benchmark's int4 layers at full size (Llama-3-8B: 64 sequences x
+    8192, four heads per workgroup; Llama-3-70B: 32 x 8192 with 64 query / 8
+    KV heads, one head per column), the library's own plan: the whole pool
+    bit-exact against the oracle's quantizer and every (sequence, head)
+    output within tolerance of the oracle over that pool."""
+    from gpu_cases import quantize_blocks_oracle
+    lay = W.layout_for(shape)
     case = W.make_case(shape, lay, device=dev(), poison=False)
-    print("int4 full size", flush=True)
+    print(f"int4 full size {shape.name}", flush=True)
     kq, vq, ks, vs = quantize_all_gpu(case.k_cache, case.v_cache)
     bt, ctx = lay.block_tables.to(dev()), lay.context_lens.to(dev())
     out = torch.empty_like(case.q)
     pa.paged_decode_attention_int4(case.q, kq, vq, ks, vs, bt, ctx, shape.scale, out)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    seqs = [0, 13, 31]
-    pairs = [(s_, int(rng.integers(32))) for s_ in seqs for _ in range(4)]
-    used = lay.block_tables[seqs].flatten()
-    okq, ovq, oks, ovs = quantize_all_oracle(case.k_cache, case.v_cache,
-                                             used[used >= 0].tolist())
-    ref = oracle.paged_decode_attention(host(case.q), okq, ovq, host(lay.block_tables),
-                                        host(lay.context_lens), shape.scale, k_scale=oks,
-                                        v_scale=ovs, pairs=pairs, int4=True, num_threads=8,
-                                        lib=orc)
+    want = quantize_blocks_oracle(case.k_cache, case.v_cache, range(lay.num_blocks), "i4")[:4]
+    for got, exp in zip((kq, vq, ks, vs), want):
+        assert host(got).tobytes() == exp.tobytes()
+    ref = oracle.paged_decode_attention(host(case.q), *want[:2], host(lay.block_tables),
+                                        host(lay.context_lens), shape.scale, k_scale=want[2],
+                                        v_scale=want[3], int4=True, lib=orc)
     assert torch.isfinite(out).all()
-    assert max_abs_err(out, ref, pairs) <= TOL_I4
-
-
-def test_int4_full_size_head_columns_sampled(orc):
-    """Llama-3-70B layer (64 query / 8 KV heads), 16 sequences x 8192
-    positions in int4: the one-head-per-column kernel under the library's own
-    plan, on sampled (sequence, head) rows."""
-    shape = W.Shape("llama3-70b-int4kv-test", "f16", 16, 64, 8, 128, 16)
-    lay = W.carve_layout([8192] * 16, 16, num_blocks=16 * 512, seed=3)
-    case = W.make_case(shape, lay, device=dev(), poison=False)
-    print("int4 full size, head columns", flush=True)
-    kq, vq, ks, vs = quantize_all_gpu(case.k_cache, case.v_cache)
-    bt, ctx = lay.block_tables.to(dev()), lay.context_lens.to(dev())
-    out = torch.empty_like(case.q)
-    pa.paged_decode_attention_int4(case.q, kq, vq, ks, vs, bt, ctx, shape.scale, out)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(9)
-    seqs = [0, 15]
-    pairs = [(s_, int(rng.integers(64))) for s_ in seqs for _ in range(4)]
-    used = lay.block_tables[seqs].flatten()
-    okq, ovq, oks, ovs = quantize_all_oracle(case.k_cache, case.v_cache,
-                                             used[used >= 0].tolist())
-    ref = oracle.paged_decode_attention(host(case.q), okq, ovq, host(lay.block_tables),
-                                        host(lay.context_lens), shape.scale, k_scale=oks,
-                                        v_scale=ovs, pairs=pairs, int4=True, num_threads=8,
-                                        lib=orc)
-    assert torch.isfinite(out).all()
-    assert max_abs_err(out, ref, pairs) <= TOL_I4
+    assert max_abs_err(out, ref) <= TOL_I4

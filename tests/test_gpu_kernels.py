@@ -398,3 +398,25 @@ def test_read_probe_runs_and_leaves_sink():
         pa.hbm_read_probe(src.cpu(), sink)
     with pytest.raises(ValueError):
         pa.hbm_read_probe(src, sink, order[:5].to(dev()))
+
+
+def test_workspace_of_any_dtype_is_sized_in_bytes():
+    """A float32 workspace holding exactly the plan's bytes is accepted (the
+    binding passes bytes, not elements) and gives the uint8 workspace's bits."""
+    shape, lay, case = make("f16", 8, 2, 128, 16, [700, 1500, 3, 2049], seed=9)
+    q, kc, vc, bt, ctx_t = to_dev(case.q, case.k_cache, case.v_cache, lay.block_tables,
+                                  lay.context_lens)
+    s, hq, _ = q.shape
+    need = pa.decode_workspace_bytes(kc, s, hq, lay.max_blocks)
+    assert need % 4 == 0 and need > 0
+    a, b = torch.empty_like(q), torch.empty_like(q)
+    pa.paged_decode_attention(q, kc, vc, bt, ctx_t, shape.scale, a,
+                              workspace=torch.empty(need, dtype=torch.uint8, device=dev()))
+    pa.paged_decode_attention(q, kc, vc, bt, ctx_t, shape.scale, b,
+                              workspace=torch.empty(need // 4, dtype=torch.float32, device=dev()))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    with pytest.raises(pa.PagedAttnError, match="workspace"):
+        pa.paged_decode_attention(q, kc, vc, bt, ctx_t, shape.scale, b,
+                                  workspace=torch.empty(need // 4 - 1, dtype=torch.float32,
+                                                        device=dev()))

@@ -56,23 +56,54 @@ def make_batch(rng, fmt, ctx, tq, hq, hkv, d, bs, spare_blocks=8):
     return kp, vp, bt, qs, np.array(ctx, np.int32), q
 
 
-# Unit roundoff of the operand/output format.  A prefill row near the start of
-# a prompt averages few value rows, so |out| is close to |v| rather than the
-# ~sqrt(e/ctx) of a long decode context that the absolute tolerances assume;
-# rounding the output (<= u |out|) and the softmax weights fed to the matrix
-# cores (<= u sum_i w_i |v_i| <= u max|v|) then add a relative term.
+# Unit roundoff of the operand/output format.
 UNIT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+LONG_ROW = 128      # rows that see at least this many positions meet the plain tolerance
 
 
-def within(got, ref, fmt, vmax):
-    """Max-abs tolerance plus twice the format's rounding of out and weights."""
-    bound = TOL[fmt] + 2 * UNIT[fmt] * (np.abs(ref) + vmax)
-    return bool(np.all(np.abs(got - ref) <= bound)), float(np.max(np.abs(got - ref)))
+def abs_pool(vp, fmt):
+    """|V| in the pool's own format (clearing the sign bit is exact; NaN stays NaN)."""
+    return np.abs(vp) if fmt == "f16" else (vp & np.uint16(0x7FFF))
 
 
-def vmax_of(vp, fmt):
-    v = vp.astype(np.float32) if fmt == "f16" else (vp.astype(np.uint32) << 16).view(np.float32)
-    return float(np.nanmax(np.abs(v)))
+def visible(qs, ctx):
+    """Positions each query row attends to: token i of a chunk of T tokens of
+    a context of c sits at position c - T + i and sees c - T + i + 1 rows."""
+    n = [c - (qs[s + 1] - qs[s]) + 1 + np.arange(qs[s + 1] - qs[s])
+         for s, c in enumerate(ctx)]
+    return np.concatenate(n) if n else np.zeros(0, np.int64)
+
+
+def within(got, ref, ref_abs_v, vis, fmt):
+    """Per-element bound of the GPU output against the fp64 oracle.
+
+    The kernel rounds each softmax weight w_i to the operand format before the
+    value product (relative error <= u) and normalises by the sum of those
+    same rounded weights, so the result is an exact weighted mean of V with
+    perturbed weights: |error| <= u * sum_i wbar_i |v_i - out| <=
+    u * (sum_i wbar_i |v_i| + |out|).  Rounding the output adds <= u |out|.
+    sum_i wbar_i |v_i| is the oracle run once more on |V| (ref_abs_v).  The
+    brief's max-abs tolerance covers the fp32 accumulation and exp; a row
+    near the start of a prompt averages few value rows, so the relative
+    terms are what matter there.  Rows that see LONG_ROW or more positions
+    must meet the plain tolerance."""
+    bound = TOL[fmt] + UNIT[fmt] * (2.0 * np.abs(ref) + ref_abs_v)
+    long_rows = np.broadcast_to((vis >= LONG_ROW).reshape(vis.shape + (1,) * (ref.ndim - 1)),
+                                bound.shape)
+    bound = np.where(long_rows, TOL[fmt], bound)
+    err = np.abs(got - ref)
+    worst_long = float(err[long_rows].max()) if long_rows.any() else 0.0
+    return bool(np.all(err <= bound)), float(err.max()), worst_long
+
+
+def oracle_pair(q, kp, vp, bt, qs, ctx, scale, fmt, orc, rows=None):
+    """The oracle's output and its output over |V| (same weights)."""
+    kw = dict(bf16=fmt == "bf16", num_threads=0, lib=orc)
+    if rows is not None:
+        kw["rows"] = rows
+    ref = oracle.paged_prefill_attention(q, kp, vp, bt, qs, ctx, scale, **kw)
+    ref_abs = oracle.paged_prefill_attention(q, kp, abs_pool(vp, fmt), bt, qs, ctx, scale, **kw)
+    return ref, ref_abs
 
 
 def run_gpu(fmt, kp, vp, bt, qs, ctx, q, scale, max_query_len=None):
@@ -104,11 +135,10 @@ def test_prefill_matches_oracle(fmt, d, bs, hq, hkv, case, orc):
     scale = 1.0 / np.sqrt(d)
     print(f"prefill {fmt} d={d} bs={bs} hq={hq} hkv={hkv} case={case}", flush=True)
     got = run_gpu(fmt, kp, vp, bt, qs, ctx_a, q, scale)
-    ref = oracle.paged_prefill_attention(q, kp, vp, bt, qs, ctx_a, scale, bf16=fmt == "bf16",
-                                         num_threads=8, lib=orc)
+    ref, ref_abs = oracle_pair(q, kp, vp, bt, qs, ctx_a, scale, fmt, orc)
     assert np.isfinite(got).all()
-    ok, err = within(got, ref, fmt, vmax_of(vp, fmt))
-    assert ok, err
+    ok, err, err_long = within(got, ref, ref_abs, visible(qs, ctx_a), fmt)
+    assert ok, (err, err_long)
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
@@ -131,8 +161,9 @@ def test_chunked_equals_whole_prompt_bit_exact(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-def test_one_token_chunks_match_decode(fmt):
-    """T = 1 is a decode step: same rows as the decode kernel, within tolerance."""
+def test_one_token_chunks_match_decode(fmt, orc):
+    """T = 1 is a decode step: the prefill rows and the decode kernel's rows
+    each within their bound of the oracle."""
     rng = np.random.default_rng(8)
     hq, hkv, d, bs = 32, 8, 128, 16
     ctx = [1, 17, 500, 2049]
@@ -145,8 +176,10 @@ def test_one_token_chunks_match_decode(fmt):
                               scale, out)
     torch.cuda.synchronize()
     dec = out.double().cpu().numpy()
-    ok, err = within(got, dec, fmt, 2 * vmax_of(vp, fmt))
-    assert ok, err
+    ref, ref_abs = oracle_pair(q, kp, vp, bt, qs, ctx_a, scale, fmt, orc)
+    ok, err, err_long = within(got, ref, ref_abs, visible(qs, ctx_a), fmt)
+    assert ok, (err, err_long)
+    assert np.max(np.abs(dec - ref)) <= TOL[fmt]
 
 
 def test_bad_context_gives_nan_rows():
@@ -174,7 +207,9 @@ def test_prefill_argument_checks():
 
 def test_full_size_sampled_rows(orc):
     """Llama-3-8B layer shape: 4 prompts of 2048 tokens plus a 512-token chunk
-    after 3584 cached positions, checked on sampled rows."""
+    after 3584 cached positions.  Every query head of 100 tokens (the first,
+    second and last of each prompt and of the chunk, and 80 drawn at random)
+    against the oracle: all rows would take the fp64 oracle minutes."""
     rng = np.random.default_rng(10)
     hq, hkv, d, bs = 32, 8, 128, 16
     ctx, tq = [2048, 2048, 2048, 2048, 4096], [2048, 2048, 2048, 2048, 512]
@@ -182,14 +217,16 @@ def test_full_size_sampled_rows(orc):
     scale = 1.0 / np.sqrt(d)
     got = run_gpu("f16", kp, vp, bt, qs, ctx_a, q, scale)
     total = int(qs[-1])
-    rows = [(t, h) for t in (0, 1, 2047, 2048, total - 512, total - 1) for h in (0, hq - 1)]
-    rows += [(int(rng.integers(total)), int(rng.integers(hq))) for _ in range(40)]
-    ref = oracle.paged_prefill_attention(q, kp, vp, bt, qs, ctx_a, scale, rows=rows,
-                                         num_threads=8, lib=orc)
+    toks = {int(qs[s]) + i for s in range(len(ctx)) for i in (0, 1)} | {int(t) - 1 for t in qs[1:]}
+    toks |= {int(t) for t in rng.choice(total, 100 - len(toks), replace=False)}
+    toks = sorted(toks)[:100]
+    rows = [(t, h) for t in toks for h in range(hq)]
+    ref, ref_abs = oracle_pair(q, kp, vp, bt, qs, ctx_a, scale, "f16", orc, rows=rows)
     g = np.stack([got[t, h] for t, h in rows])
+    vis = visible(qs, ctx_a)[[t for t, _ in rows]]
     assert np.isfinite(got).all()
-    ok, err = within(g, ref, "f16", vmax_of(vp, "f16"))
-    assert ok, err
+    ok, err, err_long = within(g, ref, ref_abs, vis, "f16")
+    assert ok, (err, err_long)
 
 
 def test_tokens_past_max_query_len_are_not_written():

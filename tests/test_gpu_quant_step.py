@@ -186,13 +186,13 @@ def test_decode_step_quant_rejects_unquantized_cache():
                          ids=lambda s: s.name)
 def test_decode_step_quant_full_size(shape, orc):
     """The benchmark's quantized step at full size (64 sequences x 8192, the
-    library's plan): the new rows' codes and scales bit-exact against the
-    oracle's quantizer, whose pool slots were poisoned first, and sampled
-    outputs within tolerance of the oracle over the sampled sequences'
-    blocks."""
-    from test_gpu_int4 import quantize_all_gpu, quantize_all_oracle
+    library's plan): the whole pool after the step -- every code and scale,
+    the new rows included -- bit-exact against the oracle's quantizing append
+    of every source row followed by its append of the new rows, whose pool
+    slots were poisoned first; and every (sequence, head) output within
+    tolerance of the oracle's attention over that pool."""
+    from test_gpu_int4 import quantize_all_gpu
     from gpu_cases import quantize_blocks_oracle, quantize_pool_gpu
-    from test_gpu_workloads import sample_pairs
 
     fmt = shape.cache_dtype
     int4 = fmt == "i4"
@@ -228,19 +228,13 @@ def test_decode_step_quant_full_size(shape, orc):
     for got, exp in zip(pools, small):
         assert same_bits(got[b_idx, :, o_idx], exp[:, :, 0])
 
-    # sampled outputs over the sampled sequences' blocks
-    pairs = sample_pairs(shape.num_seqs, shape.num_q_heads, 5, extra=0)[::8]
-    seqs = sorted({q for q, _ in pairs})
-    blocks = lay.block_tables[seqs].flatten()
-    blocks = blocks[blocks >= 0]
-    if int4:
-        want = list(quantize_all_oracle(case.k_cache, case.v_cache, blocks.tolist()))
-    else:
-        want = list(quantize_blocks_oracle(case.k_cache, case.v_cache, blocks, fmt)[:4])
+    # every output, over the oracle's whole pool
+    want = list(quantize_blocks_oracle(case.k_cache, case.v_cache, range(lay.num_blocks), fmt)[:4])
     ORACLE_APPEND[fmt](host(case.k_new), host(case.v_new), slots, *want)
+    for got, exp in zip(pools, want):
+        assert same_bits(got, exp)
     ref = oracle.paged_decode_attention(host(case.q), want[0], want[1], host(lay.block_tables),
                                         host(lay.context_lens), shape.scale, k_scale=want[2],
-                                        v_scale=want[3], pairs=pairs, int4=int4,
-                                        num_threads=8, lib=orc)
+                                        v_scale=want[3], int4=int4, lib=orc)
     assert torch.isfinite(out).all()
-    assert max_abs_err(out, ref, pairs) <= TOL["i8" if int4 else fmt]
+    assert max_abs_err(out, ref) <= TOL["i8" if int4 else fmt]
