@@ -591,6 +591,44 @@ def graph_timed_ms(launches, count):
     return k0.elapsed_time(k1) / count, how
 
 
+def capture_step(b):
+    """One whole decode step (every layer's launches, as Bench.step issues
+    them) captured in a HIP graph, the way a serving loop replays its decode
+    step; None if capture fails.  The step enqueues kernels only (no memset,
+    allocation or synchronization), so a replay does exactly the eager
+    step's work: the GPU tests replay such captures and compare every replay
+    with the eager result bit for bit."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            b.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            b.step()
+        torch.cuda.synchronize()
+        return graph
+    except RuntimeError:
+        torch.cuda.synchronize()
+        return None
+
+
+def timed_steps(run, steps):
+    """(ms per step over `steps` calls of run() between two events on torch's
+    current stream, sorted per-step durations from an event after each)."""
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record()
+    for i in range(steps):
+        run()
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    return marks[0].elapsed_time(marks[-1]) / steps, per_step
+
+
 def attention_launch_ms(b, layers, steps):
     """Average duration of the dominant kernel: the same launches (every
     layer, K times) back to back (graph_timed_ms)."""
@@ -665,6 +703,9 @@ def main():
                     help="0: the library's own plan (what pa_paged_decode_attention runs)")
     ap.add_argument("--separate", action="store_true",
                     help="separate launches for slots, append, partitions and merge")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay a HIP graph of one whole step instead of issuing its launches "
+                         "from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-kernel", type=int, default=0,
@@ -714,22 +755,22 @@ def main():
     layers = args.layers or shape.layers
     b = Bench(shape, layers, dev, args.partition_tokens, args.separate)
     torch.cuda.synchronize()
+    b.step()
+    torch.cuda.synchronize()
+    # The step's launches are issued from Python every step; --graph replays
+    # one captured step instead (measured: no faster on the 32-layer steps,
+    # and each replay adds ~12 us, which a one-layer step feels).
+    graph = capture_step(b) if args.graph else None
+    run = graph.replay if graph is not None else b.step
     for _ in range(args.warmup):
-        b.step()
+        run()
     torch.cuda.synchronize()
 
     # Timed region: K whole steps, bracketed by events on torch's current
-    # stream, which is the stream the binding hands to every launch; an event
-    # after every step gives the spread of single steps.
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    marks[0].record()
-    for i in range(args.steps):
-        b.step()
-        marks[i + 1].record()
-    torch.cuda.synchronize()
-    ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
-    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    # stream, which is the stream the binding hands to every launch (and the
+    # one a graph replays on); an event after every step gives the spread of
+    # single steps.
+    ms_step, per_step = timed_steps(run, args.steps)
 
     kernel_ms, kernel_timing = attention_launch_ms(b, layers, args.steps)
     append = append_report(b, layers, min(args.steps, 10))
@@ -749,6 +790,8 @@ def main():
         "step_ms": {"median": round(float(np.median(per_step)), 4),
                     "p10": round(float(np.percentile(per_step, 10)), 4),
                     "p90": round(float(np.percentile(per_step, 90)), 4)},
+        "step_timing": ("hip graph replay of one whole step (every layer's launches)"
+                        if graph is not None else "launches issued from Python every step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -63,6 +63,8 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
   if (plan.num_parts > 1 && (!workspace || workspace_bytes < plan.ws_bytes))
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes,
                 plan.ws_bytes);
+  if (plan.num_parts > 1 && ((uintptr_t)workspace & 15) != 0)
+    return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   pa::DecodeParams p{};
   p.q = q;
   p.k_cache = k_cache;
@@ -117,6 +119,7 @@ pa_status run_partitions(const void* q, const void* k_cache, const void* v_cache
 pa_status run_merge(const Plan& plan, const void* workspace, const int32_t* context_lens,
                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_tokens,
                     int32_t out_dtype, void* out, hipStream_t stream, int32_t window = 0) {
+  if (((uintptr_t)out & 15) != 0) return fail(PA_ERR_INVALID_ARG, "out must be 16-byte aligned");
   const hipError_t e = pa::launch_lse_merge(
       (const float*)workspace, (const float*)((const char*)workspace + plan.o_offset),
       context_lens, num_seqs, num_q_heads, head_dim, max_tokens, plan.part_tokens,
@@ -481,6 +484,8 @@ pa_status pa_lse_merge(const void* workspace, size_t workspace_bytes, const int3
   if (!workspace || !context_lens || !out) return fail(PA_ERR_INVALID_ARG, "NULL pointer");
   if (workspace_bytes < plan.ws_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, plan.ws_bytes);
+  if (((uintptr_t)workspace & 15) != 0)
+    return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   return run_merge(plan, workspace, context_lens, num_seqs, num_q_heads, head_dim, (int32_t)max_tok,
                    out_dtype, out, (hipStream_t)stream);
 }

@@ -65,11 +65,15 @@ inline pa_status check_cache(const pa_cache_desc* c) {
 //  * matrix-core kernel (3 waves/SIMD, two tiles in flight per wave): as few
 //    partitions as keep >= 256 workgroups (one per CU) for 16-bit caches -- its per-workgroup prologue and
 //    merge cost more than the imbalance of long partitions (Llama-2-70B's
-//    ragged batch runs fastest as one partition per sequence); int8 tiles
-//    carry half the bytes and do best with ~2048 workgroups.
+//    ragged batch runs fastest as one partition per sequence); int8, fp8 and
+//    int4 tiles carry half the bytes or less and do best with ~1536
+//    workgroups, two full rounds of three per CU (64 sequences x 8192 at the
+//    Llama-3-8B shape, same box: 3 partitions against 4, kernel 185-189 us
+//    against 191-193 us for fp8, 188-190 against 194 for int8; int4
+//    150-154 against 155-156 us, and 83 against 86 us at 64 query heads).
 inline constexpr int32_t kTargetWorkgroups = 2048;
 inline constexpr int32_t kTargetWorkgroupsMfma = 256;
-inline constexpr int32_t kTargetWorkgroupsMfmaInt8 = 2048;
+inline constexpr int32_t kTargetWorkgroupsMfmaInt8 = 1536;
 inline constexpr int32_t kMinPartitionTokens = 256;
 inline constexpr int32_t kMinWindowPartitionTokens = 512;
 struct Plan {

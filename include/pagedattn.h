@@ -182,7 +182,8 @@ pa_status pa_kv_append_int4(const void* k_new, const void* v_new,
  * partition.  partition_tokens = 0 picks the library's own plan, the one
  * pa_paged_decode_attention uses; pass the same value to the phase entry
  * points below.  Pure host arithmetic; returns 0 for an invalid shape or a
- * single-partition plan (which needs no workspace).  Contents are scratch;
+ * single-partition plan (which needs no workspace).  The workspace must be
+ * 16-byte aligned (PA_ERR_INVALID_ARG otherwise).  Contents are scratch;
  * calls that overlap on one workspace race. */
 size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq,
@@ -335,7 +336,8 @@ pa_status pa_decode_step_partitions_quant(const void* q, const void* k_new, cons
  * which is the same softmax-weighted sum a single pass gives ([guide]
  * "Flash attention": tiling leaves the math unchanged).  Arguments as for
  * pa_decode_partitions with the same partition_tokens; out_dtype is the
- * format of out (PA_F32, PA_F16 or PA_BF16). */
+ * format of out (PA_F32, PA_F16 or PA_BF16).  workspace and out must be
+ * 16-byte aligned (PA_ERR_INVALID_ARG otherwise). */
 pa_status pa_lse_merge(const void* workspace, size_t workspace_bytes,
                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                        int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
