@@ -25,7 +25,7 @@ __all__ = [
     "decode_step_partitions", "decode_step_quant", "decode_step_partitions_quant", "lse_merge", "gather_kv", "abi_version", "OutOfBlocks",
     "hbm_read_probe",
     "BlockManager", "copy_blocks", "paged_prefill_attention", "paged_decode_attention_window",
-    "decode_window_workspace_bytes", "decode_step_window",
+    "decode_window_workspace_bytes", "decode_step_window", "decode_step_noalloc",
 ]
 
 # PA_LIBRARY_PATH may name another build of the same library (e.g. a variant
@@ -97,6 +97,7 @@ def _declare(lib):
         "pa_decode_step": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
         "pa_decode_step_partitions": [P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P, D, P, sz,
                                       P],
+        "pa_decode_step_noalloc": [P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P],
         "pa_decode_step_quant": [P, P, P, P, P, P, P, P, i32, P, i32, i32, f32, P, D, P, sz, P],
         "pa_decode_step_partitions_quant": [P, P, P, P, P, P, P, P, i32, P, i32, i32, f32, i32, P,
                                             D, P, sz, P],
@@ -435,6 +436,25 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, s
         maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
         _dev(out, "out", k_cache.dtype), ctypes.byref(desc), _dev(ws, "workspace"), _nbytes(ws),
         _stream(q)), lib)
+    return out
+
+
+def decode_step_noalloc(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                        out):
+    """decode_step with no workspace: the partials go to the library's
+    static device scratch (see pa_decode_step_noalloc), so the call
+    allocates nothing; calls that overlap on one device race."""
+    lib = library()
+    desc = CacheDesc.of(k_cache)
+    s, hq, maxb = _shapes(q, k_cache, v_cache, block_tables, context_lens, out)
+    if k_new.shape != (s, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{s}, {desc.num_kv_heads}, {desc.head_dim}]")
+    _ok(lib.pa_decode_step_noalloc(
+        _dev(q, "q", k_cache.dtype, 3), _dev(k_new, "k_new", k_cache.dtype),
+        _dev(v_new, "v_new", k_cache.dtype), _dev(k_cache, "k_cache", ndim=4),
+        _dev(v_cache, "v_cache", k_cache.dtype, 4), _dev(block_tables, "block_tables", torch.int32),
+        maxb, _dev(context_lens, "context_lens", torch.int32), s, hq, float(scale),
+        _dev(out, "out", k_cache.dtype), ctypes.byref(desc), _stream(q)), lib)
     return out
 
 

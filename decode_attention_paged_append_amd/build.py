@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libpagedattn.so")
 
-SOURCES = ["api.cpp", "block_manager.cpp", "kv_ops.hip", "lse_merge.hip", "decode_f32.hip",
+SOURCES = ["api.cpp", "block_manager.cpp", "kv_ops.hip", "lse_merge.hip", "noalloc.hip",
+           "decode_f32.hip",
            "decode_f16.hip", "decode_bf16.hip", "decode_i8.hip", "decode_fp8.hip",
            "decode_i4.hip",
            "prefill_f16.hip",

@@ -11,6 +11,7 @@
 #include "decode_plan.h"
 #include "prefill_dispatch.h"
 #include "kv_ops.h"
+#include "noalloc.h"
 #include "status.h"
 
 namespace pa {
@@ -400,6 +401,34 @@ pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, vo
   return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_q_heads, scale, out, cache, workspace,
                        workspace_bytes, (hipStream_t)stream, -1, k_new, v_new);
+}
+
+pa_status pa_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                                 void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, float scale, void* out,
+                                 const pa_cache_desc* cache, pa_stream_t stream) {
+  pa_status st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (quantized(cache->dtype))
+    return fail(PA_ERR_UNSUPPORTED, "quantized cache: pa_decode_step_noalloc takes 16/32-bit caches");
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, "NULL k_new / v_new");
+  Plan plan;
+  st = make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, &plan);
+  if (st != PA_OK) return st;
+  if (plan.ws_bytes > pa::kNoAllocScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "this shape's partials need %zu bytes, above the %zu-byte static scratch of "
+                "pa_decode_step_noalloc: use pa_decode_step with a workspace",
+                plan.ws_bytes, pa::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (num_seqs > 0 && plan.num_parts > 1) {
+    const hipError_t e = pa::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "static scratch address");
+  }
+  return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, out, cache, ws,
+                       ws ? pa::kNoAllocScratchBytes : 0, (hipStream_t)stream, -1, k_new, v_new);
 }
 
 pa_status pa_decode_step_partitions(const void* q, const void* k_new, const void* v_new,

@@ -267,6 +267,22 @@ pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, vo
                          float scale, void* out, const pa_cache_desc* cache, void* workspace,
                          size_t workspace_bytes, pa_stream_t stream);
 
+/* pa_decode_step without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The partials of a multi-partition plan go to a
+ * static device array of the library (32 MiB per device, held by every
+ * device the library runs on until the process ends); no call allocates or
+ * frees memory.  Shapes whose partials exceed it return PA_ERR_WORKSPACE
+ * (use pa_decode_step).  Every call on one device shares that device's
+ * array: calls that overlap on one device race (enqueue them on one stream,
+ * or order the streams).  Nothing in the array needs to start at zero.
+ * Arguments, results and errors otherwise as pa_decode_step. */
+pa_status pa_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                                 void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, float scale, void* out,
+                                 const pa_cache_desc* cache, pa_stream_t stream);
+
 /* Phase 1 of the above with an explicit partition length, or 0 for the
  * plan's.  The length must be a positive multiple of the tile, which is
  * max(block_size, 1024 / (head_dim * bytes per cache element)) positions
