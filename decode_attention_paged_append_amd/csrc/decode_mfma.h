@@ -182,9 +182,7 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
 #pragma unroll
       for (int w = 0; w < 4; ++w) qbias += f16_lo(qb[c][w]) + f16_hi(qb[c][w]);
     }
-    qbias += __shfl_xor(qbias, 16);
-    qbias += __shfl_xor(qbias, 32);
-    qbias *= -128.0f / kSub;
+    qbias = rows_sum(qbias) * (-128.0f / kSub);
   }
 
   float m = kMaxInit;  // running max of head n (log2 units), same in all g
@@ -339,8 +337,7 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
       if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) z[i] = -__builtin_inff();
     }
     float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = rows_max(mt);
     const float mn = fmaxf(m, mt);
     const bool moved = mn > m;
     const float alpha = fast_exp2(m - mn);
@@ -368,6 +365,26 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
     if constexpr (kBias) corr = MM::sum2(pb[1], MM::sum2(pb[0], corr));
 
     // ---- values: O^T += V^T . P^T, MFMA e uses dim (D/16)*row + e
+    if constexpr (F == Fmt::I8) {
+      // bias every code once (c ^ 0x80 = c + 128 mod 256: the low byte of its
+      // fp16 subnormal); the v_perm then takes byte e of two tokens' words,
+      // each under a zero high byte: dim e of tokens 4g..4g+3, widened
+      uint32_t vb[4][VW / 4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int w = 0; w < VW / 4; ++w) vb[j][w] = vraw[j][w] ^ 0x80808080u;
+      }
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const int w = e >> 2;
+        const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + (e & 3)) << 16) | (uint32_t)(e & 3);
+        const u32x2 a = {__builtin_amdgcn_perm(vb[1][w], vb[0][w], sel),
+                         __builtin_amdgcn_perm(vb[3][w], vb[2][w], sel)};
+        o[e] = MM::pv(a, pb, o[e]);
+      }
+      return;
+    }
     uint32_t vh[4][VE / 2];  // fp16/bf16 words of tokens 4g+j, dims of lane n
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -425,12 +442,8 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
   }
 
   // ---- merge: sum the lanes' shares of l, then the waves through LDS
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if constexpr (kBias) {
-    corr += __shfl_xor(corr, 16);
-    corr += __shfl_xor(corr, 32);
-  }
+  lsum = rows_sum(lsum);
+  if constexpr (kBias) corr = rows_sum(corr);
   __syncthreads();  // every wave is done with its K tile region
   float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][D]
   if (n < GC) {

@@ -118,6 +118,33 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// Max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48), with gfx950's row swaps on the vector ALU instead of LDS shuffles.
+// v_permlane32_swap of (x, x) leaves lane l holding x[l] and x[l ^ 32] in
+// its two results (lanes below 32: own value first; above: the partner's),
+// and v_permlane16_swap does the same for l ^ 16 (checked on MI355X for
+// every lane), so one swap and one max (or add) combine a pair of halves.
+// Every lane ends with the same bits: max is exact, and both lanes of a
+// pair add the same two operands in the same order (lower half first).
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(float_to_bits(x), float_to_bits(x), false, false);
+  // copied out by value: __builtin_bit_cast of an element of the returned
+  // pair read element 0 for both on this compiler
+  const uint32_t a0 = a[0], a1 = a[1];
+  x = fmaxf(bits_to_float(a0), bits_to_float(a1));
+  const auto b = __builtin_amdgcn_permlane16_swap(float_to_bits(x), float_to_bits(x), false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  return fmaxf(bits_to_float(b0), bits_to_float(b1));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(float_to_bits(x), float_to_bits(x), false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  x = bits_to_float(a0) + bits_to_float(a1);
+  const auto b = __builtin_amdgcn_permlane16_swap(float_to_bits(x), float_to_bits(x), false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  return bits_to_float(b0) + bits_to_float(b1);
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
