@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "PagedAttnError", "library", "CacheDesc", "slot_mapping", "decode_slot_mapping",
-    "kv_append", "kv_append_int8", "decode_workspace_bytes", "decode_partition_tokens",
+    "kv_append", "kv_append_int8", "check_slot_mapping", "SLOT_REPEATED", "SLOT_OUTSIDE_POOL", "decode_workspace_bytes", "decode_partition_tokens",
     "paged_decode_attention", "paged_decode_attention_int8", "decode_step", "decode_partitions",
     "kv_append_fp8", "paged_decode_attention_fp8", "kv_append_int4",
     "paged_decode_attention_int4", "int4_desc",
@@ -85,6 +85,7 @@ def _declare(lib):
         "pa_slot_mapping": [P, i32, i32, P, P, i64, i32, P, P],
         "pa_decode_slot_mapping": [P, i32, P, i32, i32, P, P],
         "pa_kv_append": [P, P, P, i64, P, P, D, P],
+        "pa_check_slot_mapping": [P, i64, i64, P, P],
         "pa_kv_append_int8": [P, P, P, i64, P, P, P, P, D, P],
         "pa_kv_append_fp8": [P, P, P, i64, P, P, P, P, D, P],
         "pa_kv_append_int4": [P, P, P, i64, P, P, P, P, D, P],
@@ -220,6 +221,23 @@ def decode_slot_mapping(block_tables, context_lens, block_size, out=None):
                                    _dev(out, "slot_mapping", torch.int64),
                                    _stream(block_tables)), lib)
     return out
+
+
+SLOT_REPEATED, SLOT_OUTSIDE_POOL = 1, 2
+
+
+def check_slot_mapping(slot_mapping, pool_slots, flags=None):
+    """Device int32 [1] flags of a slot mapping (see pa_check_slot_mapping):
+    SLOT_REPEATED if some slot >= 0 repeats, | SLOT_OUTSIDE_POOL if some slot
+    is >= pool_slots; 0 when the mapping is fit for one append.  Nothing is
+    synchronized: read the flags when convenient."""
+    lib = library()
+    if flags is None:
+        flags = torch.empty(1, dtype=torch.int32, device=slot_mapping.device)
+    _ok(lib.pa_check_slot_mapping(_dev(slot_mapping, "slot_mapping", torch.int64),
+                                  slot_mapping.numel(), int(pool_slots),
+                                  _dev(flags, "flags", torch.int32), _stream(slot_mapping)), lib)
+    return flags
 
 
 # ---------------------------------------------------------------- append

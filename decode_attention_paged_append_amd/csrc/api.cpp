@@ -519,6 +519,20 @@ pa_status pa_lse_merge(const void* workspace, size_t workspace_bytes, const int3
                    out_dtype, out, (hipStream_t)stream);
 }
 
+pa_status pa_check_slot_mapping(const int64_t* slot_mapping, int64_t num_tokens,
+                                int64_t pool_slots, int32_t* flags, pa_stream_t stream) {
+  if (num_tokens < 0 || pool_slots <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_tokens %lld < 0 or pool_slots %lld <= 0",
+                (long long)num_tokens, (long long)pool_slots);
+  if (!flags || (num_tokens > 0 && !slot_mapping)) return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  if (((uintptr_t)flags & 3) != 0) return fail(PA_ERR_INVALID_ARG, "flags must be 4-byte aligned");
+  if ((uint64_t)(num_tokens + 255) / 256 > 0x7fffffffu)
+    return fail(PA_ERR_UNSUPPORTED, "%lld tokens: too many for one check", (long long)num_tokens);
+  return hip_status(pa::launch_check_slots(slot_mapping, num_tokens, pool_slots, flags,
+                                           (hipStream_t)stream),
+                    "slot check launch");
+}
+
 pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_scale,
                        const void* v_scale, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,

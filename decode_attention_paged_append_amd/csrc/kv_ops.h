@@ -12,6 +12,10 @@ hipError_t launch_slot_mapping(const int32_t* tables, int32_t max_blocks, int32_
 hipError_t launch_decode_slot_mapping(const int32_t* tables, int32_t max_blocks,
                                       const int32_t* context_lens, int32_t num_seqs,
                                       int32_t block_size, int64_t* slots, hipStream_t stream);
+// Flags of a slot mapping (bit 0 repeated slot, bit 1 slot >= pool_slots)
+// into a device int32, zeroed first by the same launch sequence.
+hipError_t launch_check_slots(const int64_t* slots, int64_t num_tokens, int64_t pool_slots,
+                              int32_t* flags, hipStream_t stream);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
                             int64_t num_tokens, void* k_cache, void* v_cache,
                             int32_t num_kv_heads, int32_t block_size, int32_t row_bytes,

@@ -49,6 +49,54 @@ __global__ void decode_slot_mapping_kernel(const int32_t* __restrict__ tables,
   slots[s] = slot;
 }
 
+// ---------------------------------------------------------------- slot check
+
+// A slot names one position of one block, so the tokens of one append must
+// not share a slot; a slot past the pool names no position at all.  Flags,
+// OR-ed into *flags (zeroed by the launcher's first kernel): bit 0 a
+// repeated slot (>= 0), bit 1 a slot >= pool_slots.  Negative slots are
+// pads and are never compared.  Token i is compared with every j < i, in
+// LDS tiles of kSlotTile slots (O(T^2 / 2) compares).
+constexpr int kSlotTile = 256;
+
+__global__ void zero_flag_kernel(int32_t* flags) { *flags = 0; }
+
+__global__ __launch_bounds__(kSlotTile) void check_slots_kernel(
+    const int64_t* __restrict__ slots, int64_t num_tokens, int64_t pool_slots,
+    int32_t* __restrict__ flags) {
+  __shared__ int64_t tile[kSlotTile];
+  const int64_t i = (int64_t)blockIdx.x * kSlotTile + threadIdx.x;
+  const int64_t mine = i < num_tokens ? slots[i] : -1;
+  int32_t found = mine >= pool_slots ? 2 : 0;
+  for (int64_t base = 0; base <= (int64_t)blockIdx.x * kSlotTile; base += kSlotTile) {
+    const int64_t j = base + threadIdx.x;
+    tile[threadIdx.x] = j < num_tokens ? slots[j] : -1;
+    __syncthreads();
+    if (mine >= 0) {
+      const int64_t upto = i - base < kSlotTile ? i - base : kSlotTile;   // j < i only
+      for (int64_t k = 0; k < upto; ++k) found |= tile[k] == mine ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  // one vector atomic per wave that found something
+  const uint64_t any = __builtin_amdgcn_ballot_w64(found != 0);
+  if (any != 0) {
+    int32_t bits = found;
+    for (int off = 32; off > 0; off >>= 1) bits |= __shfl_xor(bits, off);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+      __hip_atomic_fetch_or(flags, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+hipError_t launch_check_slots(const int64_t* slots, int64_t num_tokens, int64_t pool_slots,
+                              int32_t* flags, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_flag_kernel, dim3(1), dim3(1), 0, stream, flags);
+  if (num_tokens > 0)
+    hipLaunchKernelGGL(check_slots_kernel, dim3((unsigned)((num_tokens + kSlotTile - 1) / kSlotTile)),
+                       dim3(kSlotTile), 0, stream, slots, num_tokens, pool_slots, flags);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- append
 
 // One thread per 16-byte piece of a (token, head) row; K and V together.

@@ -122,6 +122,22 @@ pa_status pa_decode_slot_mapping(const int32_t* block_tables, int32_t max_blocks
                                  int32_t block_size, int64_t* slot_mapping,
                                  pa_stream_t stream);
 
+/* Check a slot mapping before an append.  A slot names one position of one
+ * block ([viz] "PagedAttention: the cache in blocks"), so no two tokens of
+ * one append may name the same slot: the appends do not detect it (the
+ * result is then one of the rows, unspecified which).  Writes *flags
+ * (device int32, 4-byte aligned), in stream order: 0 when every slot is
+ * negative (a pad) or in [0, pool_slots) and no slot >= 0 repeats; else
+ * PA_SLOT_REPEATED (1) if some slot >= 0 repeats, | PA_SLOT_OUTSIDE_POOL (2)
+ * if some slot >= pool_slots (the appends skip those).  Two kernels (the
+ * flag is zeroed, then the slots are compared); nothing is synchronized and
+ * nothing traps: read *flags when convenient.  Cost O(num_tokens^2 / 2)
+ * compares.  pool_slots = num_blocks * block_size. */
+#define PA_SLOT_REPEATED 1
+#define PA_SLOT_OUTSIDE_POOL 2
+pa_status pa_check_slot_mapping(const int64_t* slot_mapping, int64_t num_tokens,
+                                int64_t pool_slots, int32_t* flags, pa_stream_t stream);
+
 /* ---------------------------------------------------------------- append */
 
 /* Store each new token's K and V rows into the pool at its slot, for every

@@ -76,6 +76,17 @@ def test_append_argument_checks(lib):
                                 None) == INVALID
 
 
+def test_check_slot_mapping_argument_checks(lib):
+    """Host-side checks of the slot check, before any launch."""
+    flags = ctypes.c_void_p(0x2000)
+    assert lib.pa_check_slot_mapping(FAKE, -1, 64, flags, None) == INVALID
+    assert lib.pa_check_slot_mapping(FAKE, 4, 0, flags, None) == INVALID
+    assert lib.pa_check_slot_mapping(FAKE, 4, 64, None, None) == INVALID
+    assert lib.pa_check_slot_mapping(None, 4, 64, flags, None) == INVALID
+    assert lib.pa_check_slot_mapping(FAKE, 4, 64, ctypes.c_void_p(0x2002), None) == INVALID
+    assert b"aligned" in lib.pa_last_error()
+
+
 def test_copy_blocks_argument_checks(lib):
     """Quantized pools need both scale pointers; a negative count is rejected
     and an empty one is a no-op (all on the host, before any launch)."""
