@@ -378,12 +378,21 @@ pa_status pa_lse_merge(const void* workspace, size_t workspace_bytes,
 
 /* ---------------------------------------------------------------- gather */
 
-/* Un-page every sequence to dense rows (for checking the block-table
- * gather): k_out[s][i][h][:] = row of position i, for i < context_lens[s];
- * rows at or past the length are left untouched.  k_out, v_out: device
- * [num_seqs][max_blocks_per_seq * BS][Hkv][D] in the cache's format (int8
- * codes for an int8 cache).  k_scale/v_scale and k_scale_out/v_scale_out
- * ([S][maxB*BS][Hkv] fp16) are used for a quantized cache only (may be NULL). */
+/* Un-page every sequence to dense rows: a sequence's rows are those of the
+ * blocks its table lists, in order, position pos at offset pos % BS of block
+ * table[pos / BS] ([viz] "PagedAttention: the cache in blocks").  This is
+ * the block-table gather the attention kernels do on the fly, exported so
+ * that it can be checked byte for byte.  k_out[s][i][h][:] = row of
+ * position i, for i < context_lens[s]; rows at or past the length are left
+ * untouched.  k_out, v_out: device [num_seqs][max_blocks_per_seq * BS][Hkv]
+ * [row bytes] in the cache's format (int8 / fp8 codes; int4: D/2 bytes of
+ * packed codes).  For a quantized cache, k_scale/v_scale (the pools' fp16
+ * scales) and k_scale_out/v_scale_out ([S][maxB*BS][Hkv] fp16, int4:
+ * [S][maxB*BS][Hkv][D/32]) carry the scales along; the scale outputs may be
+ * NULL to gather codes only.  Errors: PA_ERR_INVALID_ARG for a NULL pool,
+ * table, length or output pointer or bad sizes.  Rows whose table entry lies
+ * outside the pool, and every row of a sequence whose length is negative or
+ * past the table, are left untouched (no fault).  num_seqs = 0 is a no-op. */
 pa_status pa_gather_kv(const void* k_cache, const void* v_cache, const void* k_scale,
                        const void* v_scale, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
