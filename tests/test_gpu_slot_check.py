@@ -24,7 +24,7 @@ def host_flags(slots, pool_slots):
     return (pa.SLOT_REPEATED if repeated else 0) | (pa.SLOT_OUTSIDE_POOL if outside else 0)
 
 
-def oracle_verdict(slots, pool_slots, block_size=16):
+def oracle_status(slots, pool_slots, block_size=16):
     """The oracle append's status on these slots: 0, -2 (outside) or -3 (repeated)."""
     nb = pool_slots // block_size
     t = slots.shape[0]
@@ -51,7 +51,7 @@ def test_flags_match_oracle_and_host(t):
     base[rng.random(t) < 0.1] = -1                       # pads
     print(f"slot check t={t}", flush=True)
     assert gpu_flags(base, pool_slots) == 0 == host_flags(base, pool_slots)
-    assert oracle_verdict(base, pool_slots) == 0
+    assert oracle_status(base, pool_slots) == 0
     if t >= 2:
         # a repeat: the last token takes an earlier live slot (same or earlier tile)
         live = np.flatnonzero(base >= 0)
@@ -59,7 +59,7 @@ def test_flags_match_oracle_and_host(t):
         i, j = live[0], t - 1
         dup[j] = base[i]
         assert gpu_flags(dup, pool_slots) == pa.SLOT_REPEATED == host_flags(dup, pool_slots)
-        assert oracle_verdict(dup, pool_slots) == -3
+        assert oracle_status(dup, pool_slots) == -3
         # a repeat inside the last tile only
         dup2 = base.copy()
         dup2[t - 1] = 5
@@ -69,7 +69,7 @@ def test_flags_match_oracle_and_host(t):
     out = base.copy()
     out[t // 2] = pool_slots + 3
     assert gpu_flags(out, pool_slots) == pa.SLOT_OUTSIDE_POOL == host_flags(out, pool_slots)
-    assert oracle_verdict(out, pool_slots) == -2
+    assert oracle_status(out, pool_slots) == -2
     if t >= 4:          # the repeated pair does not overwrite the outside slot
         both = out.copy()
         k = (t // 2 + 1) % t
