@@ -74,6 +74,15 @@ inline pa_status check_cache(const pa_cache_desc* c) {
 inline constexpr int32_t kTargetWorkgroups = 2048;
 inline constexpr int32_t kTargetWorkgroupsMfma = 256;
 inline constexpr int32_t kTargetWorkgroupsMfmaInt8 = 1536;
+// The quantized matrix-core kernels keep three workgroups per CU resident,
+// so 768 workgroups are one full round on 256 CUs.  Within the target
+// above, a plan takes the fewest partitions that fill whole rounds: a part
+// round leaves CUs idle at the end, and every extra round repeats each
+// workgroup's prologue and partial store.  Measured on MI355X (Llama-3-70B
+// layer, int4, 32 sequences x 8192, 8 KV heads): 768 workgroups (three
+// partitions) 72.4-75.2 us per launch, 1536 (six) 77.2-79.2, 1024 (four)
+// 84.8-90.9, 512 (two) 83.5.
+inline constexpr int32_t kQuantRoundWorkgroups = 768;
 inline constexpr int32_t kMinPartitionTokens = 256;
 inline constexpr int32_t kMinWindowPartitionTokens = 512;
 struct Plan {
@@ -160,7 +169,15 @@ inline pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num
     const int64_t target = !p.mfma ? kTargetWorkgroups
                            : quantized(c->dtype) ? kTargetWorkgroupsMfmaInt8
                                                  : kTargetWorkgroupsMfma;
-    const int64_t want_parts = (target + units - 1) / units;
+    int64_t want_parts = (target + units - 1) / units;
+    if (p.mfma && quantized(c->dtype) && window == 0) {
+      for (int64_t q = 1; q < want_parts; ++q) {
+        if (units * q >= kQuantRoundWorkgroups && units * q % kQuantRoundWorkgroups == 0) {
+          want_parts = q;  // whole rounds, fewer than the target's
+          break;
+        }
+      }
+    }
     // a window's partitions start at the tile holding its first position:
     // they cover up to tile - 1 positions before it
     const int64_t span = window > 0 ? std::min<int64_t>(max_tok, (int64_t)window + p.tile - 1)
