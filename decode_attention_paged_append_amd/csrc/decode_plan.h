@@ -72,6 +72,12 @@ inline pa_status check_cache(const pa_cache_desc* c) {
 //    against 191-193 us for fp8, 188-190 against 194 for int8; int4
 //    150-154 against 155-156 us, and 83 against 86 us at 64 query heads).
 inline constexpr int32_t kTargetWorkgroups = 2048;
+// The vector-ALU kernel over int8 caches (93 VGPRs: five waves per SIMD)
+// does best with one round of workgroups all resident at once: Llama-2-7B
+// MHA int8, 16 sequences x 4096, same box: 1024 workgroups (two partitions)
+// 86.7 us per launch, 2048 (four) 89.1-92.7, 1536 (three) 92.9.  The fp16
+// and bf16 instances measured best at 2048 (bf16: 163.8 against 164.9 us).
+inline constexpr int32_t kTargetWorkgroupsInt8 = 1024;
 inline constexpr int32_t kTargetWorkgroupsMfma = 256;
 inline constexpr int32_t kTargetWorkgroupsMfmaInt8 = 1536;
 // The quantized matrix-core kernels keep three workgroups per CU resident,
@@ -166,7 +172,7 @@ inline pa_status make_plan(const pa_cache_desc* c, int32_t num_seqs, int32_t num
     // window, 8 KV heads: 256 workgroups 49.2 us, 512: 50.0, 1024: 52.5,
     // 2048: 55.4; 2048-token windows at 32 and 16 KV heads and a 4096-token
     // int8 window did best at 576-token partitions).
-    const int64_t target = !p.mfma ? kTargetWorkgroups
+    const int64_t target = !p.mfma ? (c->dtype == PA_I8 ? kTargetWorkgroupsInt8 : kTargetWorkgroups)
                            : quantized(c->dtype) ? kTargetWorkgroupsMfmaInt8
                                                  : kTargetWorkgroupsMfma;
     int64_t want_parts = (target + units - 1) / units;
