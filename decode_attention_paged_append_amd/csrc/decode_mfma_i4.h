@@ -39,8 +39,9 @@
 //  * The rescale of the accumulators by alpha is a real branch: it runs only
 //    on tiles that raise some running max.
 //
-// Tiling, loads, the K tile in LDS and the cross-wave merge follow the
-// decode_mfma_kernel (decode_mfma.h).
+// Tiling and the cross-wave merge follow the decode_mfma_kernel
+// (decode_mfma.h); the K tile reaches the score MFMAs through two rounds of
+// cross-row lane swaps (i4_key_transpose), not through LDS.
 #pragma once
 
 #include "decode_mfma.h"
@@ -56,6 +57,30 @@ constexpr uint32_t kNibbles = 0x0F0F0F0Fu;
 constexpr float kTwo24 = 16777216.0f;    // 2^24
 constexpr float kTwoM24 = 1.0f / kTwo24;
 
+// One K tile (16 rows of 64 bytes) is loaded with lane (q, r) = (lane / 16,
+// lane % 16) holding row r, dims 32q + 8w .. +8 in word w.  Exchanging lane
+// bit 5 with bit 1 of the word index, then lane bit 4 with bit 0 (the
+// cross-row swaps of gfx950) leaves lane (g, n) = (lane / 16, lane % 16)
+// holding row n, dims 32c + 8g .. +8 in word c: the A operand of score MFMA
+// c, one scale group, with no trip through LDS.
+__device__ __forceinline__ void i4_key_transpose(uint32_t (&x)[4]) {
+  const auto a02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+  const auto a13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+  const auto b01 = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
+  const auto b23 = __builtin_amdgcn_permlane16_swap(a02[1], a13[1], false, false);
+  x[0] = b01[0];
+  x[1] = b01[1];
+  x[2] = b23[0];
+  x[3] = b23[1];
+}
+
+// Eight codes (one word) as eight fp16 subnormals in dim order.
+__device__ __forceinline__ u32x4 i4_widen(uint32_t x) {
+  const uint32_t lo = x & kNibbles, hi = (x >> 4) & kNibbles;
+  return u32x4{__builtin_amdgcn_perm(hi, lo, i4_sel(0)), __builtin_amdgcn_perm(hi, lo, i4_sel(1)),
+               __builtin_amdgcn_perm(hi, lo, i4_sel(2)), __builtin_amdgcn_perm(hi, lo, i4_sel(3))};
+}
+
 template <int BS, int GC, int NW>
 __global__ __launch_bounds__(NW * kWave)
 __attribute__((amdgpu_waves_per_eu(GC == 4 ? 3 : 2, 8)))
@@ -66,14 +91,6 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   constexpr int KG = D / kInt4Group;      // scale groups per row = score MFMAs
   constexpr int VE = D / 16;              // value MFMAs per column set
   constexpr int CS = GC / 4;              // column sets
-  constexpr int CHUNKS = D / 8;           // 16-byte chunks per fp16 row in LDS
-  // K chunk c of row r sits at kslot(c ^ (r % CHUNKS)): bit 1 flipped in each
-  // row's upper half, so the 4 lanes of each of two rows that write chunks
-  // w, w+4, w+8, w+12 of their rows fall on distinct banks (they collided in
-  // pairs: 2.7-3.2 conflict cycles per LDS instruction); the A-layout reads
-  // stay conflict-free.
-  auto kslot = [](int x) { return x ^ ((x >> 2) & 2); };
-  constexpr int K_LPR = ROWB / 16;        // lanes per row in a K load
   constexpr int TPI = GC == 4 ? 2 : 1;    // tiles fetched per loop iteration
   static_assert(GC == 4 || GC == 8, "four or eight heads per workgroup");
   static_assert(BS % TT == 0, "a tile lies inside one block");
@@ -149,12 +166,9 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   }
   bool bad_block = false;
 
-  constexpr int KTILE_BYTES = TT * D * 2;
-  constexpr int ACC_BYTES = GC * D * 4;
-  constexpr int REGION = KTILE_BYTES > ACC_BYTES ? KTILE_BYTES : ACC_BYTES;
+  constexpr int REGION = GC * D * 4;  // one wave's accumulators for the merge
   __shared__ __attribute__((aligned(16))) char s_mem[NW * REGION];
   __shared__ float s_ml[NW][GC][2];
-  u32x4* const ktile = (u32x4*)(s_mem + wave * REGION);
 
   const char* __restrict__ kbase = (const char*)p.k_cache;
   const char* __restrict__ vbase = (const char*)p.v_cache;
@@ -164,7 +178,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   int ids_base = -kWave;
 
   struct Raw {
-    u32x4 k;           // 32 codes: row lane / 4, dims 32 (lane % 4) ..
+    u32x4 k;           // 32 codes: row n, dims 32 g ..
     uint32_t v[4];     // 8 codes: token 4g+j, dims 8n ..
     uint32_t ks[8];    // fp16 key scales, tokens 4g..4g+3 x KG groups
     uint32_t vs[2];    // fp16 value scales, tokens 4g+j (j = 2w, 2w+1), group n / 4
@@ -194,9 +208,8 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     const char* kt = kbase + row0 * ROWB;
     const char* vt = vbase + row0 * ROWB;
 
-    const int kr = lane / K_LPR;
     raw.k = u32x4{0, 0, 0, 0};
-    if (!PARTIAL || (kr >= nlow && kr < nvalid)) raw.k = load16_stream(kt + lane * 16);
+    if (!PARTIAL || (n >= nlow && n < nvalid)) raw.k = load16_stream(kt + n * ROWB + g * 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * g + j;
@@ -231,23 +244,6 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     const int nvalid = raw.nvalid;
     const int nlow = raw.nlow;
 
-    // ---- K tile -> LDS as subnormal codes, chunk c of row r at kslot(c ^ (r % CHUNKS))
-    {
-      const int r = lane / K_LPR;
-      const int c0 = 4 * (lane % K_LPR);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x = raw.k[w];
-        const uint32_t lo = x & kNibbles, hi = (x >> 4) & kNibbles;
-        ktile[r * CHUNKS + kslot((c0 + w) ^ (r % CHUNKS))] =
-            u32x4{__builtin_amdgcn_perm(hi, lo, i4_sel(0)), __builtin_amdgcn_perm(hi, lo, i4_sel(1)),
-                  __builtin_amdgcn_perm(hi, lo, i4_sel(2)), __builtin_amdgcn_perm(hi, lo, i4_sel(3))};
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
     // ---- value A operands: dim 8n+e of tokens 4g..4g+3 (shared by the sets)
     u32x2 va[VE];
     {
@@ -266,9 +262,14 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
       }
     }
 
+    // ---- K: the score MFMAs' A operands straight from registers
     u32x4 ka[KG];
+    {
+      uint32_t x[4] = {raw.k[0], raw.k[1], raw.k[2], raw.k[3]};
+      i4_key_transpose(x);
 #pragma unroll
-    for (int c = 0; c < KG; ++c) ka[c] = ktile[n * CHUNKS + kslot((4 * c + g) ^ (n % CHUNKS))];
+      for (int c = 0; c < KG; ++c) ka[c] = i4_widen(x[c]);
+    }
 
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) {
@@ -360,7 +361,6 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     corr[cs] += __shfl_xor(corr[cs], 16);
     corr[cs] += __shfl_xor(corr[cs], 32);
   }
-  __syncthreads();  // every wave is done with its K tile region
   float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][D]
   if ((n >> 2) == g) {  // column group n / 4 is the group of this lane's rows
 #pragma unroll
@@ -434,13 +434,11 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   constexpr int KG = D / kInt4Group;      // scale groups per row = score MFMAs
   constexpr int VE = D / 16;              // value MFMAs (two per group)
   constexpr int CHUNKS = D / 8;           // 16-byte chunks per fp16 row in LDS
-  // K chunk c of row r sits at kslot(c ^ (r % CHUNKS)): bit 1 flipped in each
+  // V chunk c of row r sits at kslot(c ^ (r & 7)): bit 1 flipped in each
   // row's upper half, so the 4 lanes of each of two rows that write chunks
-  // w, w+4, w+8, w+12 of their rows fall on distinct banks (they collided in
-  // pairs: 2.7-3.2 conflict cycles per LDS instruction); the A-layout reads
-  // stay conflict-free.
+  // w, w+4, w+8, w+12 of their rows fall on distinct banks.
   auto kslot = [](int x) { return x ^ ((x >> 2) & 2); };
-  constexpr int K_LPR = ROWB / 16;        // lanes per row in a K or V load
+  constexpr int K_LPR = ROWB / 16;        // lanes per row in a V load
   constexpr int ACC_STRIDE = D + 4;       // floats per head row of the merge buffer
   constexpr int TPI = 2;                  // tiles fetched per loop iteration
   constexpr int SC_WORDS = TT * KG / 2;   // words of one tile's key (or value) scales
@@ -515,14 +513,13 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   bool bad_block = false;
 
   constexpr int TILE_BYTES = TT * D * 2;           // one tile of fp16 codes
-  constexpr int TILES_BYTES = 2 * TILE_BYTES + 2 * SC_WORDS * 4;
+  constexpr int TILES_BYTES = TILE_BYTES + 2 * SC_WORDS * 4;  // V, then the scales
   constexpr int ACC_BYTES = GC * ACC_STRIDE * 4;
   constexpr int REGION = TILES_BYTES > ACC_BYTES ? TILES_BYTES : ACC_BYTES;
   static_assert(2 * SC_WORDS == kWave, "one scale word per lane");
   __shared__ __attribute__((aligned(16))) char s_mem[NW * REGION];
   __shared__ float s_ml[NW][GC][2];
-  u32x4* const ktile = (u32x4*)(s_mem + wave * REGION);
-  u32x4* const vtile = ktile + TT * CHUNKS;
+  u32x4* const vtile = (u32x4*)(s_mem + wave * REGION);
   uint32_t* const stile = (uint32_t*)(vtile + TT * CHUNKS);  // key, then value scales
 
   const char* __restrict__ kbase = (const char*)p.k_cache;
@@ -537,7 +534,8 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   // spread through LDS: fetched whole by every lane, they took two thirds
   // of the registers of a tile in flight.
   struct Raw {
-    u32x4 k, v;        // 32 codes each: row lane / 4, dims 32 (lane % 4) ..
+    u32x4 k;           // 32 codes: row n, dims 32 g ..
+    u32x4 v;           // 32 codes: row lane / 4, dims 32 (lane % 4) ..
     uint32_t sc;       // scale word lane % 32 of the tile (zero on masked rows)
     int nvalid;        // rows of the tile inside the partition
     int nlow;          // rows below this one are before the window
@@ -566,10 +564,8 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     const int r = lane / K_LPR;
     raw.k = u32x4{0, 0, 0, 0};
     raw.v = u32x4{0, 0, 0, 0};
-    if (!PARTIAL || (r >= nlow && r < nvalid)) {
-      raw.k = load16_stream(kbase + row0 * ROWB + lane * 16);
-      raw.v = load16_stream(vbase + row0 * ROWB + lane * 16);
-    }
+    if (!PARTIAL || (n >= nlow && n < nvalid)) raw.k = load16_stream(kbase + (row0 + n) * ROWB + g * 16);
+    if (!PARTIAL || (r >= nlow && r < nvalid)) raw.v = load16_stream(vbase + row0 * ROWB + lane * 16);
     // rows outside [nlow, nvalid) get zero scales: their B is 0
     const int sw = lane & (SC_WORDS - 1);
     const int sr = sw / (KG / 2);
@@ -583,22 +579,23 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     const int nvalid = raw.nvalid;
     const int nlow = raw.nlow;
 
-    // ---- K and V tiles -> LDS as subnormal codes.  K's 16-byte chunk c of
-    // row r sits at kslot(c ^ (r % CHUNKS)) (read whole rows), V's at
-    // kslot(c ^ (r & 7))
-    // (read transposed).
+    // ---- K: the score MFMAs' A operands straight from registers
+    u32x4 ka[KG];
+    {
+      uint32_t x[4] = {raw.k[0], raw.k[1], raw.k[2], raw.k[3]};
+      i4_key_transpose(x);
+#pragma unroll
+      for (int c = 0; c < KG; ++c) ka[c] = i4_widen(x[c]);
+    }
+    // ---- V tile -> LDS as subnormal codes, chunk c of row r at
+    // kslot(c ^ (r & 7)) (read transposed)
     {
       const int r = lane / K_LPR;
       const int c0 = 4 * (lane % K_LPR);
       stile[lane] = raw.sc;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t xk = raw.k[w];
-        const uint32_t klo = xk & kNibbles, khi = (xk >> 4) & kNibbles;
-        ktile[r * CHUNKS + kslot((c0 + w) ^ (r % CHUNKS))] =
-            u32x4{__builtin_amdgcn_perm(khi, klo, i4_sel(0)), __builtin_amdgcn_perm(khi, klo, i4_sel(1)),
-                  __builtin_amdgcn_perm(khi, klo, i4_sel(2)), __builtin_amdgcn_perm(khi, klo, i4_sel(3))};
-        // V: odd dims as 16 x code (high nibbles masked in place), taken out
+        // odd dims as 16 x code (high nibbles masked in place), taken out
         // again with the 2^24 of the epilogue
         const uint32_t xv = raw.v[w];
         const uint32_t vlo = xv & kNibbles, vhi = xv & (kNibbles << 4);
@@ -611,9 +608,6 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    u32x4 ka[KG];
-#pragma unroll
-    for (int c = 0; c < KG; ++c) ka[c] = ktile[n * CHUNKS + kslot((4 * c + g) ^ (n % CHUNKS))];
     // scales of tokens 4g .. 4g+3 x KG groups (one address per 16 lanes)
     uint32_t ks[8], vs[8];
     {
