@@ -54,6 +54,7 @@ __device__ __forceinline__ constexpr uint32_t i4_sel(int k) {
   return 0x0C000C00u | ((uint32_t)(4 + k) << 16) | (uint32_t)k;
 }
 constexpr uint32_t kNibbles = 0x0F0F0F0Fu;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 constexpr float kTwo24 = 16777216.0f;    // 2^24
 constexpr float kTwoM24 = 1.0f / kTwo24;
 
@@ -415,11 +416,10 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
 //    scale of group c at tok), rounded to fp16.  Every row of an MFMA lies
 //    in one group, so its B operand carries that group's scale.  The rows of
 //    value MFMA e are dims 16e .. 16e+15, which no lane's 16-byte load holds
-//    for four tokens at once: V goes through a per-wave LDS tile as the same
-//    subnormal codes as K, and transposing reads (ds_read_b64_tr_b16) give
-//    lane (g, n) dim 16e + n of tokens 4g .. 4g+3.  Odd dims enter as
-//    16 * code, the high nibble masked in place (one instruction fewer per
-//    word); their output rows drop the 16 with the 2^24.
+//    for four tokens at once: the raw codes go through a per-wave LDS tile
+//    (1 KiB), and two 4-bit transposing reads (ds_read_b64_tr_b4) give lane
+//    (g, n) dim 16e + n of tokens 4g .. 4g+3 for all eight MFMAs, widened
+//    to subnormals after the read.
 //  * S^T comes out with lane (g, n) holding tokens 4g .. 4g+3 of head n,
 //    which is the B operand layout: the weights never move, and the running
 //    max, sum and column sums of B are per lane.  Lane (g, n) ends with dims
@@ -433,12 +433,11 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   constexpr int ROWB = D / 2;             // cache bytes per row
   constexpr int KG = D / kInt4Group;      // scale groups per row = score MFMAs
   constexpr int VE = D / 16;              // value MFMAs (two per group)
-  constexpr int CHUNKS = D / 8;           // 16-byte chunks per fp16 row in LDS
-  // V chunk c of row r sits at kslot(c ^ (r & 7)): bit 1 flipped in each
-  // row's upper half, so the 4 lanes of each of two rows that write chunks
-  // w, w+4, w+8, w+12 of their rows fall on distinct banks.
-  auto kslot = [](int x) { return x ^ ((x >> 2) & 2); };
   constexpr int K_LPR = ROWB / 16;        // lanes per row in a V load
+  // The 32-byte halves of V row r trade places when bits 1 and 2 of r
+  // differ: the rows one transposing read touches (4g + k % 4 over the
+  // lanes of a pass) then fall on distinct banks.
+  auto vhalf = [](int r) { return ((r >> 1) ^ (r >> 2)) & 1; };
   constexpr int ACC_STRIDE = D + 4;       // floats per head row of the merge buffer
   constexpr int TPI = 2;                  // tiles fetched per loop iteration
   constexpr int SC_WORDS = TT * KG / 2;   // words of one tile's key (or value) scales
@@ -512,7 +511,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   for (int e = 0; e < VE; ++e) o[e] = f32x4{0, 0, 0, 0};
   bool bad_block = false;
 
-  constexpr int TILE_BYTES = TT * D * 2;           // one tile of fp16 codes
+  constexpr int TILE_BYTES = TT * ROWB;            // one V tile of raw codes
   constexpr int TILES_BYTES = TILE_BYTES + 2 * SC_WORDS * 4;  // V, then the scales
   constexpr int ACC_BYTES = GC * ACC_STRIDE * 4;
   constexpr int REGION = TILES_BYTES > ACC_BYTES ? TILES_BYTES : ACC_BYTES;
@@ -520,7 +519,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char s_mem[NW * REGION];
   __shared__ float s_ml[NW][GC][2];
   u32x4* const vtile = (u32x4*)(s_mem + wave * REGION);
-  uint32_t* const stile = (uint32_t*)(vtile + TT * CHUNKS);  // key, then value scales
+  uint32_t* const stile = (uint32_t*)(vtile + TT * K_LPR);  // key, then value scales
 
   const char* __restrict__ kbase = (const char*)p.k_cache;
   const char* __restrict__ vbase = (const char*)p.v_cache;
@@ -587,22 +586,13 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
 #pragma unroll
       for (int c = 0; c < KG; ++c) ka[c] = i4_widen(x[c]);
     }
-    // ---- V tile -> LDS as subnormal codes, chunk c of row r at
-    // kslot(c ^ (r & 7)) (read transposed)
+    // ---- V tile -> LDS as raw codes, 16-byte chunk q of row r at
+    // q ^ 2 vhalf(r); the scales beside it
     {
       const int r = lane / K_LPR;
-      const int c0 = 4 * (lane % K_LPR);
+      const int q = lane % K_LPR;
+      vtile[r * K_LPR + (q ^ (2 * vhalf(r)))] = raw.v;
       stile[lane] = raw.sc;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // odd dims as 16 x code (high nibbles masked in place), taken out
-        // again with the 2^24 of the epilogue
-        const uint32_t xv = raw.v[w];
-        const uint32_t vlo = xv & kNibbles, vhi = xv & (kNibbles << 4);
-        vtile[r * CHUNKS + kslot((c0 + w) ^ (r & 7))] =
-            u32x4{__builtin_amdgcn_perm(vhi, vlo, i4_sel(0)), __builtin_amdgcn_perm(vhi, vlo, i4_sel(1)),
-                  __builtin_amdgcn_perm(vhi, vlo, i4_sel(2)), __builtin_amdgcn_perm(vhi, vlo, i4_sel(3))};
-      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -664,12 +654,20 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     }
 
     // ---- values: B_c = p * value scale of group c, fp16; A = V^T read
-    // transposed: within each 16-lane group, lane 4a + b receives half b of
-    // the 8 bytes that lanes 4k + a (k = 0..3) point at, and lane (g, 4k + a)
-    // points at token row 4g + k, dims 16e + 4a .. +3.
-    const _Float16* vt = (const _Float16*)vtile;
-    const int vrow = 4 * g + (n >> 2);
-    const int vq = n & 3;
+    // transposed: within each 16-lane group, lane b receives as its nibble k
+    // nibble b of the 8 bytes that lane k points at.  In read h lane (g, k)
+    // points at token row 4g + k % 4, dims 64h + 16(k / 4) .. +16, so word w
+    // of the result holds dim 16e + n of tokens 4g .. 4g+3 for e = 4h + 2w
+    // (low half) and e + 1 (high half).
+    u32x2 vw[2];
+    {
+      const int vrow = 4 * g + (n & 3);
+      const char* vt = (const char*)vtile + vrow * ROWB + 8 * (n >> 2);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        vw[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2*)(vt + 32 * (h ^ vhalf(vrow)))));
+    }
 #pragma unroll
     for (int c = 0; c < KG; ++c) {
       // p * scale as one mixed-precision FMA (fp16 scale, fp32 product)
@@ -679,15 +677,14 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
       };
       const u32x2 pb = {Mfma<Fmt::F16>::pack(wt(0), wt(1)), Mfma<Fmt::F16>::pack(wt(2), wt(3))};
       corr[c] = Mfma<Fmt::F16>::sum2(pb[1], Mfma<Fmt::F16>::sum2(pb[0], corr[c]));
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int e = 2 * c + h;
-        const int ch = 2 * e + (vq >> 1);
-        const int off = vrow * D + kslot(ch ^ (vrow & 7)) * 8 + (vq & 1) * 4;
-        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vt + off));
-        o[e] = Mfma<Fmt::F16>::pv(__builtin_bit_cast(u32x2, va), pb, o[e]);
-      }
+      // codes of tokens (4g, 4g+1) and (4g+2, 4g+3) sit in bytes 0/1 of the
+      // even and odd nibbles for e = 2c, bytes 2/3 for e = 2c + 1
+      const uint32_t x = vw[c >> 1][c & 1];
+      const uint32_t lo = x & kNibbles, hi = (x >> 4) & kNibbles;
+      const u32x2 a0 = {__builtin_amdgcn_perm(hi, lo, i4_sel(0)), __builtin_amdgcn_perm(hi, lo, i4_sel(1))};
+      const u32x2 a1 = {__builtin_amdgcn_perm(hi, lo, i4_sel(2)), __builtin_amdgcn_perm(hi, lo, i4_sel(3))};
+      o[2 * c] = Mfma<Fmt::F16>::pv(a0, pb, o[2 * c]);
+      o[2 * c + 1] = Mfma<Fmt::F16>::pv(a1, pb, o[2 * c + 1]);
     }
   };
 
@@ -731,13 +728,12 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   __syncthreads();  // every wave is done with its tile region
   float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][ACC_STRIDE]
   if (n < GC) {
-    constexpr float kOdd = kTwo24 / 16.0f;  // rows of odd dims hold 16 x code
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       const float b = -8.0f * corr[e / 2];
       *(f32x4*)(s_acc + n * ACC_STRIDE + 16 * e + 4 * g) =
-          f32x4{fmaf(o[e][0], kTwo24, b), fmaf(o[e][1], kOdd, b), fmaf(o[e][2], kTwo24, b),
-                fmaf(o[e][3], kOdd, b)};
+          f32x4{fmaf(o[e][0], kTwo24, b), fmaf(o[e][1], kTwo24, b), fmaf(o[e][2], kTwo24, b),
+                fmaf(o[e][3], kTwo24, b)};
     }
     if (g == 0) {
       s_ml[wave][n][0] = m;
