@@ -419,7 +419,9 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
 //    for four tokens at once: the raw codes go through a per-wave LDS tile
 //    (1 KiB), and two 4-bit transposing reads (ds_read_b64_tr_b4) give lane
 //    (g, n) dim 16e + n of tokens 4g .. 4g+3 for all eight MFMAs, widened
-//    to subnormals after the read.
+//    to subnormals after the read.  The codes of odd MFMAs enter as
+//    16 * code (the high nibble masked in place); their output rows drop
+//    the 16 with the 2^24.
 //  * S^T comes out with lane (g, n) holding tokens 4g .. 4g+3 of head n,
 //    which is the B operand layout: the weights never move, and the running
 //    max, sum and column sums of B are per lane.  Lane (g, n) ends with dims
@@ -523,6 +525,8 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
 
   const char* __restrict__ kbase = (const char*)p.k_cache;
   const char* __restrict__ vbase = (const char*)p.v_cache;
+  const uint32_t koff = n * ROWB + g * 16;  // lane (g, n): key row n, chunk g
+  const uint32_t voff = lane * 16;          // value row lane / 4, chunk lane % 4
   const int blk0 = tok0 / BS;
   const int nblk = (tok_end + BS - 1) / BS - blk0;
   int ids = 0;
@@ -559,12 +563,14 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     bad_block |= !ok;
     phys = ok ? phys : 0;
     const size_t row0 = ((size_t)phys * p.num_kv_heads + kvh) * BS + ttok % BS;
+    const char* const kt = kbase + row0 * ROWB;  // the tile's rows (wave-uniform)
+    const char* const vt = vbase + row0 * ROWB;
 
     const int r = lane / K_LPR;
     raw.k = u32x4{0, 0, 0, 0};
     raw.v = u32x4{0, 0, 0, 0};
-    if (!PARTIAL || (n >= nlow && n < nvalid)) raw.k = load16_stream(kbase + (row0 + n) * ROWB + g * 16);
-    if (!PARTIAL || (r >= nlow && r < nvalid)) raw.v = load16_stream(vbase + row0 * ROWB + lane * 16);
+    if (!PARTIAL || (n >= nlow && n < nvalid)) raw.k = load16_stream(kt + koff);
+    if (!PARTIAL || (r >= nlow && r < nvalid)) raw.v = load16_stream(vt + voff);
     // rows outside [nlow, nvalid) get zero scales: their B is 0
     const int sw = lane & (SC_WORDS - 1);
     const int sr = sw / (KG / 2);
@@ -656,13 +662,14 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     // ---- values: B_c = p * value scale of group c, fp16; A = V^T read
     // transposed: within each 16-lane group, lane b receives as its nibble k
     // nibble b of the 8 bytes that lane k points at.  In read h lane (g, k)
-    // points at token row 4g + k % 4, dims 64h + 16(k / 4) .. +16, so word w
-    // of the result holds dim 16e + n of tokens 4g .. 4g+3 for e = 4h + 2w
-    // (low half) and e + 1 (high half).
+    // points at token row 4g + k / 4, dims 64h + 16(k % 4) .. +16, so nibble
+    // k of the result is dim 64h + 16(k % 4) + n of token 4g + k / 4: byte b
+    // of word w holds token 4g + 2w + b / 2, its low nibble for MFMA
+    // 4h + 2(b % 2), its high one for the next.
     u32x2 vw[2];
     {
-      const int vrow = 4 * g + (n & 3);
-      const char* vt = (const char*)vtile + vrow * ROWB + 8 * (n >> 2);
+      const int vrow = 4 * g + (n >> 2);
+      const char* vt = (const char*)vtile + vrow * ROWB + 8 * (n & 3);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         vw[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(
@@ -677,12 +684,13 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
       };
       const u32x2 pb = {Mfma<Fmt::F16>::pack(wt(0), wt(1)), Mfma<Fmt::F16>::pack(wt(2), wt(3))};
       corr[c] = Mfma<Fmt::F16>::sum2(pb[1], Mfma<Fmt::F16>::sum2(pb[0], corr[c]));
-      // codes of tokens (4g, 4g+1) and (4g+2, 4g+3) sit in bytes 0/1 of the
-      // even and odd nibbles for e = 2c, bytes 2/3 for e = 2c + 1
-      const uint32_t x = vw[c >> 1][c & 1];
-      const uint32_t lo = x & kNibbles, hi = (x >> 4) & kNibbles;
-      const u32x2 a0 = {__builtin_amdgcn_perm(hi, lo, i4_sel(0)), __builtin_amdgcn_perm(hi, lo, i4_sel(1))};
-      const u32x2 a1 = {__builtin_amdgcn_perm(hi, lo, i4_sel(2)), __builtin_amdgcn_perm(hi, lo, i4_sel(3))};
+      // MFMA 2c from the low nibbles, 2c + 1 from the high ones (16 x code),
+      // bytes c % 2 and c % 2 + 2 of each word: tokens (4g, 4g+1) from word
+      // 0, (4g+2, 4g+3) from word 1, each under a zero high byte
+      const uint32_t x0 = vw[c >> 1][0], x1 = vw[c >> 1][1];
+      const uint32_t sel = 0x0C000C00u | ((uint32_t)((c & 1) + 2) << 16) | (uint32_t)(c & 1);
+      const u32x2 a0 = {__builtin_amdgcn_perm(0u, x0 & kNibbles, sel), __builtin_amdgcn_perm(0u, x1 & kNibbles, sel)};
+      const u32x2 a1 = {__builtin_amdgcn_perm(0u, x0 & ~kNibbles, sel), __builtin_amdgcn_perm(0u, x1 & ~kNibbles, sel)};
       o[2 * c] = Mfma<Fmt::F16>::pv(a0, pb, o[2 * c]);
       o[2 * c + 1] = Mfma<Fmt::F16>::pv(a1, pb, o[2 * c + 1]);
     }
@@ -731,9 +739,9 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       const float b = -8.0f * corr[e / 2];
+      const float f = (e & 1) ? kTwo24 / 16.0f : kTwo24;  // odd e: 16 x code
       *(f32x4*)(s_acc + n * ACC_STRIDE + 16 * e + 4 * g) =
-          f32x4{fmaf(o[e][0], kTwo24, b), fmaf(o[e][1], kTwo24, b), fmaf(o[e][2], kTwo24, b),
-                fmaf(o[e][3], kTwo24, b)};
+          f32x4{fmaf(o[e][0], f, b), fmaf(o[e][1], f, b), fmaf(o[e][2], f, b), fmaf(o[e][3], f, b)};
     }
     if (g == 0) {
       s_ml[wave][n][0] = m;
