@@ -168,11 +168,19 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   bool bad_block = false;
 
   constexpr int REGION = GC * D * 4;  // one wave's accumulators for the merge
+  constexpr int SC_WORDS = TT * KG / 2;  // words of one tile's key (or value) scales
+  static_assert(2 * SC_WORDS == kWave, "one scale word per lane");
   __shared__ __attribute__((aligned(16))) char s_mem[NW * REGION];
   __shared__ float s_ml[NW][GC][2];
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[NW][2 * SC_WORDS];  // a tile's scales
 
   const char* __restrict__ kbase = (const char*)p.k_cache;
   const char* __restrict__ vbase = (const char*)p.v_cache;
+  // lanes 0..31 fetch the tile's key scale words, 32..63 its value scale
+  // words, each [row][group pair] in order
+  const int sw = lane & (SC_WORDS - 1);
+  const int sr = sw / (KG / 2);  // row of this lane's scale word
+  const uint32_t* const ssrc = (const uint32_t*)(lane < SC_WORDS ? p.k_scale : p.v_scale) + sw;
   const int blk0 = tok0 / BS;
   const int nblk = (tok_end + BS - 1) / BS - blk0;
   int ids = 0;
@@ -181,8 +189,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   struct Raw {
     u32x4 k;           // 32 codes: row n, dims 32 g ..
     uint32_t v[4];     // 8 codes: token 4g+j, dims 8n ..
-    uint32_t ks[8];    // fp16 key scales, tokens 4g..4g+3 x KG groups
-    uint32_t vs[2];    // fp16 value scales, tokens 4g+j (j = 2w, 2w+1), group n / 4
+    uint32_t sc;       // scale word lane % 32 of the tile (zero on masked rows)
     int nvalid;        // rows of the tile inside the partition
     int nlow;          // rows below this one are before the window
   };
@@ -218,25 +225,8 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
       raw.v[j] = valid ? __builtin_nontemporal_load((const uint32_t*)(vt + (size_t)r * ROWB + 4 * n))
                        : 0u;
     }
-    const size_t srow = row0 + 4 * g;
-    const bool any = !PARTIAL || (4 * g < nvalid && 4 * g + 3 >= nlow);
-    const u32x4* ksrc = (const u32x4*)(p.k_scale + srow * KG);
-    const u32x4 a = any ? ksrc[0] : u32x4{0, 0, 0, 0};
-    const u32x4 b = any ? ksrc[1] : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      raw.ks[w] = a[w];
-      raw.ks[4 + w] = b[w];
-    }
-    uint32_t vsh[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // rows outside [nlow, nvalid) get a zero value scale: their B is 0
-      const bool valid = !PARTIAL || (4 * g + j >= nlow && 4 * g + j < nvalid);
-      vsh[j] = valid ? p.v_scale[(srow + j) * KG + (n >> 2)] : 0u;
-    }
-    raw.vs[0] = vsh[0] | (vsh[1] << 16);
-    raw.vs[1] = vsh[2] | (vsh[3] << 16);
+    // rows outside [nlow, nvalid) get zero scales: their B is 0
+    raw.sc = (!PARTIAL || (sr >= nlow && sr < nvalid)) ? ssrc[row0 * (KG / 2)] : 0u;
     return raw;
   };
 
@@ -244,6 +234,31 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     const int nvalid = raw.nvalid;
     const int nlow = raw.nlow;
+
+    // ---- scales through LDS: key scales of tokens 4g .. 4g+3 x KG groups
+    // (one address per 16 lanes), value scales of the same tokens in group
+    // n / 4 as fp16 pairs
+    uint32_t* const st = s_sc[wave];
+    st[lane] = raw.sc;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t ks[8], vs[2];
+    {
+      const u32x4* s4 = (const u32x4*)st;
+      const u32x4 k0 = s4[2 * g], k1 = s4[2 * g + 1];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        ks[w] = k0[w];
+        ks[4 + w] = k1[w];
+      }
+      // token 4g+j's words sit at 2(4g+j) + (group / 2); the group's half of
+      // two tokens' words makes one pair
+      const uint32_t* vsw = st + SC_WORDS + 8 * g + (n >> 3);
+      const uint32_t sel = ((n >> 2) & 1) ? 0x07060302u : 0x05040100u;
+      vs[0] = __builtin_amdgcn_perm(vsw[2], vsw[0], sel);
+      vs[1] = __builtin_amdgcn_perm(vsw[6], vsw[4], sel);
+    }
 
     // ---- value A operands: dim 8n+e of tokens 4g..4g+3 (shared by the sets)
     u32x2 va[VE];
@@ -282,7 +297,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
         const f32x4 sc = Mfma<Fmt::F16>::qk(ka[c], qb[cs][c], f32x4{b0, b0, b0, b0});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t w = raw.ks[(i * KG + c) >> 1];
+          const uint32_t w = ks[(i * KG + c) >> 1];
           sacc[i] = fmaf(sc[i], (c & 1) ? f16_hi(w) : f16_lo(w), sacc[i]);
         }
       }
@@ -314,10 +329,10 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
       }
       // ---- values: B = p * value scale of column n's group, fp16
       // p * scale as one mixed-precision FMA each (fp16 scale, fp32 product)
-      const u32x2 pb = {Mfma<Fmt::F16>::pack(fmaf(pw[0], f16_lo(raw.vs[0]), 0.0f),
-                                             fmaf(pw[1], f16_hi(raw.vs[0]), 0.0f)),
-                        Mfma<Fmt::F16>::pack(fmaf(pw[2], f16_lo(raw.vs[1]), 0.0f),
-                                             fmaf(pw[3], f16_hi(raw.vs[1]), 0.0f))};
+      const u32x2 pb = {Mfma<Fmt::F16>::pack(fmaf(pw[0], f16_lo(vs[0]), 0.0f),
+                                             fmaf(pw[1], f16_hi(vs[0]), 0.0f)),
+                        Mfma<Fmt::F16>::pack(fmaf(pw[2], f16_lo(vs[1]), 0.0f),
+                                             fmaf(pw[3], f16_hi(vs[1]), 0.0f))};
       corr[cs] = Mfma<Fmt::F16>::sum2(pb[1], Mfma<Fmt::F16>::sum2(pb[0], corr[cs]));
 #pragma unroll
       for (int e = 0; e < VE; ++e) o[cs][e] = Mfma<Fmt::F16>::pv(va[e], pb, o[cs][e]);
