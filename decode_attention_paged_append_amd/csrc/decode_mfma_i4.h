@@ -22,12 +22,13 @@
 //  * Values.  O^T[dim][col] += V^T[dim][tok] . B[tok][col] with the sixteen
 //    columns taken as (head, scale group) pairs: column n is head n % 4 of
 //    the column set and group n / 4, and B = p * (value scale of that group),
-//    rounded to fp16 like the weights of the 16-bit caches.  Lane (g, n)'s
-//    rows are dims 8(4g+i)+e, all in group g, so the lanes with n / 4 == g
-//    hold the result: 2^24 * O^T - 8 * (column sum of B), the column sums
-//    kept beside the running sums.  Odd dims enter as 16 * code (the high
-//    nibble masked in place, no shift), and their rows drop the 16 with the
-//    2^24.
+//    rounded to fp16 like the weights of the 16-bit caches.  The rows of
+//    value MFMA e are dims 16e .. 16e+15 (group e / 2), read from a raw-code
+//    LDS tile by 4-bit transposing reads (i4_value_read), so each lane keeps
+//    MFMAs 2(n / 4) and 2(n / 4) + 1, those of its column's group: 2^24 *
+//    O^T - 8 * (column sum of B), the column sums kept beside the running
+//    sums.  Odd MFMAs take 16 * code (the high nibble masked in place), and
+//    their rows drop the 16 with the 2^24.
 //  * Four heads per column set; the score MFMA repeats each head's query in
 //    all four groups of columns, so every lane already holds the weights of
 //    its column's head (its softmax runs four times over, in lanes that would
@@ -80,6 +81,45 @@ __device__ __forceinline__ u32x4 i4_widen(uint32_t x) {
   const uint32_t lo = x & kNibbles, hi = (x >> 4) & kNibbles;
   return u32x4{__builtin_amdgcn_perm(hi, lo, i4_sel(0)), __builtin_amdgcn_perm(hi, lo, i4_sel(1)),
                __builtin_amdgcn_perm(hi, lo, i4_sel(2)), __builtin_amdgcn_perm(hi, lo, i4_sel(3))};
+}
+
+// ---- V tile of raw codes in LDS (16 rows of 64 bytes, 1 KiB a wave).
+// The 32-byte halves of row r trade places when bits 1 and 2 of r differ:
+// the rows one transposing read touches (4g + k / 4 over the lanes of a
+// pass) then fall on distinct banks.
+__device__ __forceinline__ int i4_vhalf(int r) { return ((r >> 1) ^ (r >> 2)) & 1; }
+
+// Lane l's 16-byte load: row l / 4, chunk l % 4.
+__device__ __forceinline__ void i4_value_store(u32x4* vtile, int lane, u32x4 v) {
+  const int r = lane >> 2;
+  vtile[4 * r + ((lane & 3) ^ (2 * i4_vhalf(r)))] = v;
+}
+
+// Two 4-bit transposing reads (ds_read_b64_tr_b4: within each 16-lane group
+// lane b receives, as its nibble k, nibble b of the 8 bytes that lane k
+// points at).  In read h lane (g, k) points at token row 4g + k / 4, dims
+// 64h + 16(k % 4) .. +16, so nibble k of lane (g, n)'s result is dim
+// 64h + 16(k % 4) + n of token 4g + k / 4: byte b of word w holds token
+// 4g + 2w + b / 2, its low nibble for value MFMA 4h + 2(b % 2), its high
+// one for the next.
+__device__ __forceinline__ void i4_value_read(const u32x4* vtile, int g, int n, u32x2 (&vw)[2]) {
+  const int vrow = 4 * g + (n >> 2);
+  const char* vt = (const char*)vtile + vrow * 64 + 8 * (n & 3);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    vw[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(vt + 32 * (h ^ i4_vhalf(vrow)))));
+}
+
+// A operands of value MFMAs 2c (dims 32c + n, low nibbles) and 2c + 1
+// (dims 32c + 16 + n, high nibbles masked in place: 16 x code), tokens
+// 4g .. 4g+3: bytes c % 2 and c % 2 + 2 of each word, tokens (4g, 4g+1)
+// from word 0 and (4g+2, 4g+3) from word 1, each under a zero high byte.
+__device__ __forceinline__ void i4_value_operands(const u32x2 (&vw)[2], int c, u32x2& a0, u32x2& a1) {
+  const uint32_t x0 = vw[c >> 1][0], x1 = vw[c >> 1][1];
+  const uint32_t sel = 0x0C000C00u | ((uint32_t)((c & 1) + 2) << 16) | (uint32_t)(c & 1);
+  a0 = u32x2{__builtin_amdgcn_perm(0u, x0 & kNibbles, sel), __builtin_amdgcn_perm(0u, x1 & kNibbles, sel)};
+  a1 = u32x2{__builtin_amdgcn_perm(0u, x0 & ~kNibbles, sel), __builtin_amdgcn_perm(0u, x1 & ~kNibbles, sel)};
 }
 
 template <int BS, int GC, int NW>
@@ -173,6 +213,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char s_mem[NW * REGION];
   __shared__ float s_ml[NW][GC][2];
   __shared__ __attribute__((aligned(16))) uint32_t s_sc[NW][2 * SC_WORDS];  // a tile's scales
+  __shared__ u32x4 s_v[NW][TT * ROWB / 16];  // a tile's raw value codes
 
   const char* __restrict__ kbase = (const char*)p.k_cache;
   const char* __restrict__ vbase = (const char*)p.v_cache;
@@ -181,6 +222,8 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   const int sw = lane & (SC_WORDS - 1);
   const int sr = sw / (KG / 2);  // row of this lane's scale word
   const uint32_t* const ssrc = (const uint32_t*)(lane < SC_WORDS ? p.k_scale : p.v_scale) + sw;
+  const uint32_t koff = n * ROWB + g * 16;  // lane (g, n): key row n, chunk g
+  const uint32_t voff = lane * 16;          // value row lane / 4, chunk lane % 4
   const int blk0 = tok0 / BS;
   const int nblk = (tok_end + BS - 1) / BS - blk0;
   int ids = 0;
@@ -188,7 +231,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
 
   struct Raw {
     u32x4 k;           // 32 codes: row n, dims 32 g ..
-    uint32_t v[4];     // 8 codes: token 4g+j, dims 8n ..
+    u32x4 v;           // 32 codes: row lane / 4, dims 32 (lane % 4) ..
     uint32_t sc;       // scale word lane % 32 of the tile (zero on masked rows)
     int nvalid;        // rows of the tile inside the partition
     int nlow;          // rows below this one are before the window
@@ -213,18 +256,14 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     bad_block |= !ok;
     phys = ok ? phys : 0;
     const size_t row0 = ((size_t)phys * p.num_kv_heads + kvh) * BS + ttok % BS;
-    const char* kt = kbase + row0 * ROWB;
-    const char* vt = vbase + row0 * ROWB;
+    const char* const kt = kbase + row0 * ROWB;  // the tile's rows (wave-uniform)
+    const char* const vt = vbase + row0 * ROWB;
 
+    const int r = lane >> 2;
     raw.k = u32x4{0, 0, 0, 0};
-    if (!PARTIAL || (n >= nlow && n < nvalid)) raw.k = load16_stream(kt + n * ROWB + g * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * g + j;
-      const bool valid = !PARTIAL || (r >= nlow && r < nvalid);
-      raw.v[j] = valid ? __builtin_nontemporal_load((const uint32_t*)(vt + (size_t)r * ROWB + 4 * n))
-                       : 0u;
-    }
+    raw.v = u32x4{0, 0, 0, 0};
+    if (!PARTIAL || (n >= nlow && n < nvalid)) raw.k = load16_stream(kt + koff);
+    if (!PARTIAL || (r >= nlow && r < nvalid)) raw.v = load16_stream(vt + voff);
     // rows outside [nlow, nvalid) get zero scales: their B is 0
     raw.sc = (!PARTIAL || (sr >= nlow && sr < nvalid)) ? ssrc[row0 * (KG / 2)] : 0u;
     return raw;
@@ -240,6 +279,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     // n / 4 as fp16 pairs
     uint32_t* const st = s_sc[wave];
     st[lane] = raw.sc;
+    i4_value_store(s_v[wave], lane, raw.v);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -260,22 +300,13 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
       vs[1] = __builtin_amdgcn_perm(vsw[6], vsw[4], sel);
     }
 
-    // ---- value A operands: dim 8n+e of tokens 4g..4g+3 (shared by the sets)
+    // ---- value A operands: dims 16e + n of tokens 4g..4g+3 (shared by the sets)
     u32x2 va[VE];
     {
-      // odd dims (odd e) as 16 x code: high nibbles masked in place
-      uint32_t lo[4], hi[4];
+      u32x2 vw[2];
+      i4_value_read(s_v[wave], g, n, vw);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lo[j] = raw.v[j] & kNibbles;
-        hi[j] = raw.v[j] & (kNibbles << 4);
-      }
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const uint32_t* src = (e & 1) ? hi : lo;
-        va[e] = u32x2{__builtin_amdgcn_perm(src[1], src[0], i4_sel(e >> 1)),
-                      __builtin_amdgcn_perm(src[3], src[2], i4_sel(e >> 1))};
-      }
+      for (int c = 0; c < KG; ++c) i4_value_operands(vw, c, va[2 * c], va[2 * c + 1]);
     }
 
     // ---- K: the score MFMAs' A operands straight from registers
@@ -378,17 +409,17 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     corr[cs] += __shfl_xor(corr[cs], 32);
   }
   float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][D]
-  if ((n >> 2) == g) {  // column group n / 4 is the group of this lane's rows
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) {
-      const int hh = 4 * cs + (n & 3);
+  for (int cs = 0; cs < CS; ++cs) {
+    const int hh = 4 * cs + (n & 3);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const float f = (e & 1) ? kTwo24 / 16.0f : kTwo24;  // odd e: 16 x code
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s_acc[hh * D + 32 * g + 8 * i + e] = fmaf(o[cs][e][i], f, -8.0f * corr[cs]);
-      }
+    for (int e = 0; e < VE; ++e) {
+      if (e / 2 != (n >> 2)) continue;  // MFMA e holds column group n / 4's dims
+      const float f = (e & 1) ? kTwo24 / 16.0f : kTwo24;  // odd e: 16 x code
+      const float b = -8.0f * corr[cs];
+      *(f32x4*)(s_acc + hh * D + 16 * e + 4 * g) =
+          f32x4{fmaf(o[cs][e][0], f, b), fmaf(o[cs][e][1], f, b), fmaf(o[cs][e][2], f, b),
+                fmaf(o[cs][e][3], f, b)};
     }
   }
   if (g == 0 && n < 4) {
@@ -451,10 +482,6 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   constexpr int KG = D / kInt4Group;      // scale groups per row = score MFMAs
   constexpr int VE = D / 16;              // value MFMAs (two per group)
   constexpr int K_LPR = ROWB / 16;        // lanes per row in a V load
-  // The 32-byte halves of V row r trade places when bits 1 and 2 of r
-  // differ: the rows one transposing read touches (4g + k % 4 over the
-  // lanes of a pass) then fall on distinct banks.
-  auto vhalf = [](int r) { return ((r >> 1) ^ (r >> 2)) & 1; };
   constexpr int ACC_STRIDE = D + 4;       // floats per head row of the merge buffer
   constexpr int TPI = 2;                  // tiles fetched per loop iteration
   constexpr int SC_WORDS = TT * KG / 2;   // words of one tile's key (or value) scales
@@ -607,14 +634,9 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
 #pragma unroll
       for (int c = 0; c < KG; ++c) ka[c] = i4_widen(x[c]);
     }
-    // ---- V tile -> LDS as raw codes, 16-byte chunk q of row r at
-    // q ^ 2 vhalf(r); the scales beside it
-    {
-      const int r = lane / K_LPR;
-      const int q = lane % K_LPR;
-      vtile[r * K_LPR + (q ^ (2 * vhalf(r)))] = raw.v;
-      stile[lane] = raw.sc;
-    }
+    // ---- V tile -> LDS as raw codes; the scales beside it
+    i4_value_store(vtile, lane, raw.v);
+    stile[lane] = raw.sc;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -674,22 +696,10 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
       for (int c = 0; c < KG; ++c) corr[c] *= alpha;
     }
 
-    // ---- values: B_c = p * value scale of group c, fp16; A = V^T read
-    // transposed: within each 16-lane group, lane b receives as its nibble k
-    // nibble b of the 8 bytes that lane k points at.  In read h lane (g, k)
-    // points at token row 4g + k / 4, dims 64h + 16(k % 4) .. +16, so nibble
-    // k of the result is dim 64h + 16(k % 4) + n of token 4g + k / 4: byte b
-    // of word w holds token 4g + 2w + b / 2, its low nibble for MFMA
-    // 4h + 2(b % 2), its high one for the next.
+    // ---- values: B_c = p * value scale of group c, fp16; A = V^T from the
+    // transposing reads
     u32x2 vw[2];
-    {
-      const int vrow = 4 * g + (n >> 2);
-      const char* vt = (const char*)vtile + vrow * ROWB + 8 * (n & 3);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        vw[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-                    (__attribute__((address_space(3))) i32x2*)(vt + 32 * (h ^ vhalf(vrow)))));
-    }
+    i4_value_read(vtile, g, n, vw);
 #pragma unroll
     for (int c = 0; c < KG; ++c) {
       // p * scale as one mixed-precision FMA (fp16 scale, fp32 product)
@@ -699,13 +709,8 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
       };
       const u32x2 pb = {Mfma<Fmt::F16>::pack(wt(0), wt(1)), Mfma<Fmt::F16>::pack(wt(2), wt(3))};
       corr[c] = Mfma<Fmt::F16>::sum2(pb[1], Mfma<Fmt::F16>::sum2(pb[0], corr[c]));
-      // MFMA 2c from the low nibbles, 2c + 1 from the high ones (16 x code),
-      // bytes c % 2 and c % 2 + 2 of each word: tokens (4g, 4g+1) from word
-      // 0, (4g+2, 4g+3) from word 1, each under a zero high byte
-      const uint32_t x0 = vw[c >> 1][0], x1 = vw[c >> 1][1];
-      const uint32_t sel = 0x0C000C00u | ((uint32_t)((c & 1) + 2) << 16) | (uint32_t)(c & 1);
-      const u32x2 a0 = {__builtin_amdgcn_perm(0u, x0 & kNibbles, sel), __builtin_amdgcn_perm(0u, x1 & kNibbles, sel)};
-      const u32x2 a1 = {__builtin_amdgcn_perm(0u, x0 & ~kNibbles, sel), __builtin_amdgcn_perm(0u, x1 & ~kNibbles, sel)};
+      u32x2 a0, a1;
+      i4_value_operands(vw, c, a0, a1);
       o[2 * c] = Mfma<Fmt::F16>::pv(a0, pb, o[2 * c]);
       o[2 * c + 1] = Mfma<Fmt::F16>::pv(a1, pb, o[2 * c + 1]);
     }
