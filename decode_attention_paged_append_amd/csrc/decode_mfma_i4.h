@@ -190,8 +190,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
       float t = 0.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) t += f16_lo(qb[cs][c][w]) + f16_hi(qb[cs][c][w]);
-      t += __shfl_xor(t, 16);
-      t += __shfl_xor(t, 32);
+      t = rows_sum(t);
       qbias[cs][c] = -8.0f * kTwoM24 * t;
     }
   }
@@ -339,8 +338,7 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
         if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) z[i] = -__builtin_inff();
       }
       float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = rows_max(mt);
       const float mn = fmaxf(m[cs], mt);
       const bool moved = mn > m[cs];
       const float alpha = fast_exp2(m[cs] - mn);
@@ -403,10 +401,8 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   // waves through LDS
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs) {
-    lsum[cs] += __shfl_xor(lsum[cs], 16);
-    lsum[cs] += __shfl_xor(lsum[cs], 32);
-    corr[cs] += __shfl_xor(corr[cs], 16);
-    corr[cs] += __shfl_xor(corr[cs], 32);
+    lsum[cs] = rows_sum(lsum[cs]);
+    corr[cs] = rows_sum(corr[cs]);
   }
   float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][D]
 #pragma unroll
@@ -541,8 +537,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     float t = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) t += f16_lo(qb[c][w]) + f16_hi(qb[c][w]);
-    t += __shfl_xor(t, 16);
-    t += __shfl_xor(t, 32);
+    t = rows_sum(t);
     qbias[c] = -8.0f * kTwoM24 * t;
   }
 
@@ -675,8 +670,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
       if (PARTIAL && (4 * g + i >= nvalid || 4 * g + i < nlow)) z[i] = -__builtin_inff();
     }
     float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = rows_max(mt);
     const float mn = fmaxf(m, mt);
     const bool moved = mn > m;
     const float alpha = fast_exp2(m - mn);
@@ -746,12 +740,10 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
 
   // ---- merge: the lanes' shares of l and of the column sums, then the
   // waves through LDS (head rows padded by 4 floats: conflict-free stores)
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = rows_sum(lsum);
 #pragma unroll
   for (int c = 0; c < KG; ++c) {
-    corr[c] += __shfl_xor(corr[c], 16);
-    corr[c] += __shfl_xor(corr[c], 32);
+    corr[c] = rows_sum(corr[c]);
   }
   __syncthreads();  // every wave is done with its tile region
   float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][ACC_STRIDE]
