@@ -15,10 +15,13 @@
 // A tile is 16 consecutive positions of one block; each wave of the
 // workgroup takes every NW-th tile of the partition.  Lane l = 16g + n.
 //
-//  * K arrives through fully coalesced 16-byte loads (rows of the block are
-//    contiguous), goes to a per-wave LDS tile whose 16-byte chunks are XOR-
-//    swizzled by row, and is read back in the MFMA A layout (lane l: row n,
-//    8 consecutive dims of k-group g) without bank conflicts.
+//  * K reaches the MFMA A layout (lane l: row n) with no trip through LDS.
+//    Each 16-byte wave-load covers whole 128-byte lines: 16 rows of 64 bytes,
+//    or 8 rows of a 128-byte span, lane l taking row l % 8 of its load and
+//    chunk l / 8.  In the second case two loads cover rows 0..7 and 8..15,
+//    and one DPP exchange (row_ror:8 under bank masks) trades lane bit 3 with
+//    the load index, leaving lane l all chunks of row n it needs: those at
+//    bytes kbyte(g, c) below, whose dims the query operand follows.
 //  * S^T comes out with lane l holding tokens 4g..4g+3 of head n: exactly the
 //    B operand P^T of the value product, so the softmax weights never move.
 //  * V needs no LDS: lane l loads tokens 4g..4g+3 of its own dims n*D/16..;
@@ -114,17 +117,22 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
   constexpr int TT = 16;                        // positions per tile
   constexpr int ROWB = D * EB;                  // cache bytes per row
   constexpr int K_LOADS = TT * ROWB / 1024;     // 1 KiB wave-loads per K tile
-  constexpr int K_LPR = ROWB / 16;              // lanes per row in a K load
-  constexpr int K_RPL = kWave / K_LPR;          // rows per K load
-  constexpr int CHUNKS = D / 8;                 // 16-byte chunks per fp16 row in LDS
-  auto kslot = [](int x) { return CHUNKS == 16 ? x ^ ((x >> 3) & 1) : x; };
+  // byte of row n where lane (g, n)'s 8 dims of score MFMA c start, after
+  // the loads and the exchange
+  auto kbyte = [](int g, int c) {
+    if constexpr (ROWB == 64) return 16 * g + 8 * c;                      // 8-bit, D 64
+    else if constexpr (EB == 1) return 32 * g + 8 * c;                    // 8-bit, D 128
+    else if constexpr (ROWB == 128) return 32 * g + 16 * c;               // 16-bit, D 64
+    else return 128 * (c >> 1) + 32 * g + 16 * (c & 1);                   // 16-bit, D 128
+  };
   constexpr int VW = ROWB / 16;                 // V bytes per lane per row (16, 8 or 4)
   constexpr int VE = D / 16;                    // dims per lane = value MFMAs per tile
   constexpr int QKS = D / 32;                   // 16x16x32 MFMAs per score tile
   constexpr int TPI = 2;                        // tiles fetched per loop iteration
   static_assert(BS % TT == 0, "a tile lies inside one block");
   static_assert(GC >= 1 && GC <= 16, "at most 16 heads per workgroup");
-  static_assert(K_LOADS >= 1 && K_RPL * K_LOADS == TT, "K tile = whole wave-loads");
+  static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "K rows of 64, 128 or 256 bytes");
+  static_assert(K_LOADS * (EB == 1 ? 2 : 1) == QKS, "one or two score MFMAs per K load");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -166,13 +174,13 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
     append_new_token<F, D, BS, NW * kWave>(p, table, s, kvh, ctx - 1);
 
   // B operand of the score product: Q^T, lane (g, n) holds head n's dims
-  // 32c + 8g .. +8 (zero for padding heads).
+  // kbyte(g, c) / EB .. +8 (zero for padding heads).
   u32x4 qb[QKS];
 #pragma unroll
   for (int c = 0; c < QKS; ++c) {
     qb[c] = u32x4{0, 0, 0, 0};
     if (n < GC)
-      qb[c] = *(const u32x4*)((const char*)p.q + ((out_row0 + n) * D + 32 * c + 8 * g) * 2);
+      qb[c] = *(const u32x4*)((const char*)p.q + ((out_row0 + n) * D + kbyte(g, c) / EB) * 2);
   }
   // int8: start of the score accumulation, -128 * 2^-24 * sum of head n's q
   float qbias = 0.0f;
@@ -193,13 +201,10 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
   for (int e = 0; e < VE; ++e) o[e] = f32x4{0, 0, 0, 0};
   bool bad_block = false;
 
-  // LDS: the per-wave K tiles during the loop, the wave partials after it.
-  constexpr int KTILE_BYTES = TT * D * 2;
-  constexpr int ACC_BYTES = GC * D * 4;
-  constexpr int REGION = KTILE_BYTES > ACC_BYTES ? KTILE_BYTES : ACC_BYTES;
+  // LDS: the wave partials of the merge.
+  constexpr int REGION = GC * D * 4;
   __shared__ __attribute__((aligned(16))) char s_mem[NW * REGION];
   __shared__ float s_ml[NW][GC][2];
-  u32x4* const ktile = (u32x4*)(s_mem + wave * REGION);
 
   const char* __restrict__ kbase = (const char*)p.k_cache;
   const char* __restrict__ vbase = (const char*)p.v_cache;
@@ -239,14 +244,17 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
     const char* kt = kbase + row0 * ROWB;
     const char* vt = vbase + row0 * ROWB;
 
-    // ---- loads: K (coalesced), V (token 4g+j, dims of lane n), int8 scales
+    // ---- loads: K (whole lines), V (token 4g+j, dims of lane n), int8 scales
     u32x4* const kraw = raw.k;
 #pragma unroll
     for (int j = 0; j < K_LOADS; ++j) {
-      const int r = j * K_RPL + lane / K_LPR;
+      // 64-byte rows: row n, chunk g; else row 8 (j % 2) + lane % 8, chunk
+      // 8 (j / 2) + lane / 8
+      const int r = ROWB == 64 ? n : 8 * (j & 1) + (lane & 7);
+      const int off = ROWB == 64 ? n * ROWB + 16 * g
+                                 : r * ROWB + 128 * (j >> 1) + 16 * (lane >> 3);
       kraw[j] = u32x4{0, 0, 0, 0};
-      if (!PARTIAL || (r >= nlow && r < nvalid))
-        kraw[j] = load16_stream(kt + j * 1024 + lane * 16);
+      if (!PARTIAL || (r >= nlow && r < nvalid)) kraw[j] = load16_stream(kt + off);
     }
     uint32_t (*const vraw)[VW / 4] = raw.v;
 #pragma unroll
@@ -296,36 +304,36 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
     // scale of token 4g+i as the f16 operand of a v_fma_mix
     auto scale_of = [](const uint32_t* w, int i) { return (i & 1) ? f16_hi(w[i >> 1]) : f16_lo(w[i >> 1]); };
 
-    // ---- K tile -> LDS (fp16/bf16 halves), chunk c of row r at
-    // kslot(c ^ (r % CHUNKS)).  The XOR keeps the A-layout reads (16 rows,
-    // one chunk each) conflict-free; kslot (at 16 chunks a row: bit 0 flipped
-    // in the upper half) also spreads the 8 lanes of one row that write its
-    // even (or odd) chunks, as the int8 and fp8 widenings do, over all banks.
-    // Measured before it: 3.2 bank-conflict cycles per LDS instruction on the
-    // int8 kernel, 0.28 on fp16.
+    // ---- K: lanes with bit 3 set swap their load 2i with the other lanes'
+    // load 2i + 1 (row_ror:8 reaches lane ^ 8): lane (g, n) then holds row n
+    u32x4 kx[K_LOADS];
 #pragma unroll
-    for (int j = 0; j < K_LOADS; ++j) {
-      const int r = j * K_RPL + lane / K_LPR;
-      if constexpr (kQuant) {
-        const int c0 = 2 * (lane % K_LPR);
-        const u32x2 a = codes4_to_f16<F>(kraw[j][0]), b = codes4_to_f16<F>(kraw[j][1]);
-        const u32x2 c = codes4_to_f16<F>(kraw[j][2]), d = codes4_to_f16<F>(kraw[j][3]);
-        ktile[r * CHUNKS + kslot(c0 ^ (r % CHUNKS))] = u32x4{a[0], a[1], b[0], b[1]};
-        ktile[r * CHUNKS + kslot((c0 + 1) ^ (r % CHUNKS))] = u32x4{c[0], c[1], d[0], d[1]};
-      } else {
-        const int c0 = lane % K_LPR;
-        ktile[r * CHUNKS + kslot(c0 ^ (r % CHUNKS))] = kraw[j];
+    for (int j = 0; j < K_LOADS; ++j) kx[j] = kraw[j];
+    if constexpr (ROWB != 64) {
+#pragma unroll
+      for (int j = 0; j < K_LOADS; j += 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x0 = kraw[j][w], x1 = kraw[j + 1][w];
+          kx[j][w] = __builtin_amdgcn_update_dpp(x0, x1, 0x128, 0xF, 0xC, false);
+          kx[j + 1][w] = __builtin_amdgcn_update_dpp(x1, x0, 0x128, 0xF, 0x3, false);
+        }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- scores: S^T = K . Q^T, lane (g, n): tokens 4g+i of head n
     f32x4 sacc = {qbias, qbias, qbias, qbias};
 #pragma unroll
     for (int c = 0; c < QKS; ++c) {
-      const u32x4 a = ktile[n * CHUNKS + kslot((4 * c + g) ^ (n % CHUNKS))];
+      u32x4 a;
+      if constexpr (EB == 1) {
+        // codes 8(c % 2) .. +8 of register c / 2, widened in order
+        const u32x2 lo = codes4_to_f16<F>(kx[c >> 1][2 * (c & 1)]);
+        const u32x2 hi = codes4_to_f16<F>(kx[c >> 1][2 * (c & 1) + 1]);
+        a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        a = kx[c];
+      }
       sacc = MM::qk(a, qb[c], sacc);
     }
     constexpr float zs = kBias ? kSub : 1.0f;
@@ -444,7 +452,6 @@ __device__ __forceinline__ void decode_mfma_item(const DecodeParams& p, const Wg
   // ---- merge: sum the lanes' shares of l, then the waves through LDS
   lsum = rows_sum(lsum);
   if constexpr (kBias) corr = rows_sum(corr);
-  __syncthreads();  // every wave is done with its K tile region
   float* const s_acc = (float*)(s_mem + wave * REGION);  // [GC][D]
   if (n < GC) {
 #pragma unroll
