@@ -572,7 +572,15 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   // The tile's scales arrive as one word per lane (lanes 0..31 the key
   // scales, 32..63 the value scales, each [row][group] in order) and are
   // spread through LDS: fetched whole by every lane, they took two thirds
-  // of the registers of a tile in flight.
+  // of the registers of a tile in flight.  Key words land as they arrive;
+  // value halves are re-laid [row / 4][group][row % 4], so one lane's two
+  // 16-byte reads give each group's scales of its four tokens as fp16 pairs.
+  const int sw = lane & (SC_WORDS - 1);  // this lane's scale word
+  const int sr = sw / (KG / 2);          // and its row
+  const uint32_t* const ssrc = (const uint32_t*)(lane < SC_WORDS ? p.k_scale : p.v_scale) + sw;
+  const int sh0 = lane < SC_WORDS ? 2 * lane
+                                  : 2 * SC_WORDS + (sr >> 2) * 16 + 2 * (sw & 1) * 4 + (sr & 3);
+  const int sh1 = lane < SC_WORDS ? 2 * lane + 1 : sh0 + 4;  // the word's second group
   struct Raw {
     u32x4 k;           // 32 codes: row n, dims 32 g ..
     u32x4 v;           // 32 codes: row lane / 4, dims 32 (lane % 4) ..
@@ -609,10 +617,7 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     if (!PARTIAL || (n >= nlow && n < nvalid)) raw.k = load16_stream(kt + koff);
     if (!PARTIAL || (r >= nlow && r < nvalid)) raw.v = load16_stream(vt + voff);
     // rows outside [nlow, nvalid) get zero scales: their B is 0
-    const int sw = lane & (SC_WORDS - 1);
-    const int sr = sw / (KG / 2);
-    const uint32_t* ssrc = (const uint32_t*)(lane < SC_WORDS ? p.k_scale : p.v_scale);
-    raw.sc = (!PARTIAL || (sr >= nlow && sr < nvalid)) ? ssrc[row0 * (KG / 2) + sw] : 0u;
+    raw.sc = (!PARTIAL || (sr >= nlow && sr < nvalid)) ? ssrc[row0 * (KG / 2)] : 0u;
     return raw;
   };
 
@@ -631,12 +636,15 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     }
     // ---- V tile -> LDS as raw codes; the scales beside it
     i4_value_store(vtile, lane, raw.v);
-    stile[lane] = raw.sc;
+    ((uint16_t*)stile)[sh0] = (uint16_t)raw.sc;
+    ((uint16_t*)stile)[sh1] = (uint16_t)(raw.sc >> 16);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // scales of tokens 4g .. 4g+3 x KG groups (one address per 16 lanes)
+    // scales of tokens 4g .. 4g+3 x KG groups (one address per 16 lanes):
+    // key words [token][group pair], value pairs vs[2c + j] = group c of
+    // tokens 4g + 2j, 4g + 2j + 1
     uint32_t ks[8], vs[8];
     {
       const u32x4* s4 = (const u32x4*)stile;
@@ -694,14 +702,13 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     // transposing reads
     u32x2 vw[2];
     i4_value_read(vtile, g, n, vw);
+    // the weights rounded to fp16 once, times each group's scale pairs
+    // (v_pk_mul_f16): B_c carries two roundings
+    const uint32_t pp0 = Mfma<Fmt::F16>::pack(pw[0], pw[1]), pp1 = Mfma<Fmt::F16>::pack(pw[2], pw[3]);
 #pragma unroll
     for (int c = 0; c < KG; ++c) {
-      // p * scale as one mixed-precision FMA (fp16 scale, fp32 product)
-      auto wt = [&](int i) {
-        const uint32_t w = vs[(i * KG + c) >> 1];
-        return fmaf(pw[i], (c & 1) ? f16_hi(w) : f16_lo(w), 0.0f);
-      };
-      const u32x2 pb = {Mfma<Fmt::F16>::pack(wt(0), wt(1)), Mfma<Fmt::F16>::pack(wt(2), wt(3))};
+      const u32x2 pb = {__builtin_bit_cast(uint32_t, as_h2(pp0) * as_h2(vs[2 * c])),
+                        __builtin_bit_cast(uint32_t, as_h2(pp1) * as_h2(vs[2 * c + 1]))};
       corr[c] = Mfma<Fmt::F16>::sum2(pb[1], Mfma<Fmt::F16>::sum2(pb[0], corr[c]));
       u32x2 a0, a1;
       i4_value_operands(vw, c, a0, a1);
