@@ -6,16 +6,19 @@
 
 namespace pa {
 
-// Launch shapes.  Long chunks: 256 query rows per workgroup, as 8 waves x 2
-// row groups (head_dim 128; two waves per SIMD fit in the registers) or 4
-// waves x 4 row groups (head_dim 64).  Short chunks: 4 waves x 1 row group.
+// Launch shapes.  Long chunks at head_dim 128: 8 waves x 3 row groups (384
+// query rows per workgroup; two waves per SIMD fit in the 256 registers), so
+// each K/V fragment read from LDS serves three row groups; from 256 to 767
+// rows 8 waves x 2 row groups, which leaves less of a last tile idle.  At
+// head_dim 64: 4 waves x 4 row groups.  Short chunks: 4 waves x 1 row group.
 struct PrefillShape {
   int nr, nw;
   int rows() const { return nr * nw * 16; }
 };
 inline PrefillShape prefill_shape(int head_dim, int64_t rows) {
   if (rows < 256) return {1, 4};
-  return head_dim == 128 ? PrefillShape{2, 8} : PrefillShape{4, 4};
+  if (head_dim != 128) return {4, 4};
+  return rows < 768 ? PrefillShape{2, 8} : PrefillShape{3, 8};
 }
 
 template <Fmt F, int D, int BS, int NR, int NW>
@@ -46,8 +49,9 @@ static hipError_t launch_prefill_fmt(const PrefillParams& p, int head_dim, int b
     return shape.nr == 4 ? launch_prefill_bs<F, 64, 4, 4>(p, bs, row_tiles, num_seqs, stream)
                          : launch_prefill_bs<F, 64, 1, 4>(p, bs, row_tiles, num_seqs, stream);
   if (head_dim == 128)
-    return shape.nr == 2 ? launch_prefill_bs<F, 128, 2, 8>(p, bs, row_tiles, num_seqs, stream)
-                         : launch_prefill_bs<F, 128, 1, 4>(p, bs, row_tiles, num_seqs, stream);
+    return shape.nr == 3   ? launch_prefill_bs<F, 128, 3, 8>(p, bs, row_tiles, num_seqs, stream)
+           : shape.nr == 2 ? launch_prefill_bs<F, 128, 2, 8>(p, bs, row_tiles, num_seqs, stream)
+                           : launch_prefill_bs<F, 128, 1, 4>(p, bs, row_tiles, num_seqs, stream);
   return hipErrorInvalidValue;
 }
 
