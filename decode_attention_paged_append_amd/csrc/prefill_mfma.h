@@ -66,6 +66,12 @@ void prefill_mfma_kernel(const PrefillParams p) {
   constexpr int TILE_CHUNKS = TT * CH;         // 16-byte chunks per K (or V) tile
   constexpr int PER_THREAD = (TILE_CHUNKS + NW * kWave - 1) / (NW * kWave);
   constexpr bool EVEN = PER_THREAD * NW * kWave == TILE_CHUNKS;  // else the last pass is partial
+  // V chunk c of row r sits at c ^ vswz(r).  A transposing read of value
+  // MFMA e touches chunks 2e, 2e+1 of rows 4g .. 4g+3 (and 16 + those): at 16
+  // chunks a row, XOR-ing 2(r & 7) gives each of 8 rows its own 32-byte pair
+  // of banks (chunk ^ (r & 7) left two rows on each pair: 2-way conflicts,
+  // 1.2 conflict cycles per LDS instruction); at 8 chunks, r & 7.
+  auto vswz = [](int r) { return CH == 16 ? 2 * (r & 7) : (r & 7); };
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -186,7 +192,7 @@ void prefill_mfma_kernel(const PrefillParams p) {
       const int c = idx - row * CH;
       if (!EVEN && idx >= TILE_CHUNKS) continue;
       if (s < ntiles) s_k[s & 1][row * CH + (c ^ (row % CH))] = st.k[j];
-      if (s >= 1) s_v[(s - 1) & 1][row * CH + (c ^ (row & 7))] = st.v[j];
+      if (s >= 1) s_v[(s - 1) & 1][row * CH + (c ^ vswz(row))] = st.v[j];
     }
   };
 
@@ -284,15 +290,14 @@ void prefill_mfma_kernel(const PrefillParams p) {
     // .. +3, so lane (g, n) receives dim 16e + n of tokens 4g .. 4g+3: the A
     // operand V^T of value MFMA e (row n = dim 16e + n), with a second read
     // for tokens 16 + 4g .. (the k-slots 4..7 of the lane's weights).  V's
-    // 16-byte chunks sit XOR-swizzled by row & 7 (measured on MI355X: 1 %
-    // ahead of row % 16 at head_dim 128, and 4-6 % ahead of row-major rows
-    // read whole and regrouped with v_perm).
+    // 16-byte chunks sit XOR-swizzled by vswz(row); reading row-major rows
+    // whole and regrouping them with v_perm was 4-6 % slower.
     const int k = n >> 2, q = n & 3;
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       const int chunk = 2 * e + (q >> 1);
       auto read = [&](const int row) {
-        const int off = row * D + (chunk ^ (row & 7)) * 8 + (q & 1) * 4;
+        const int off = row * D + (chunk ^ vswz(row)) * 8 + (q & 1) * 4;
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(vt + off));
       };
