@@ -129,11 +129,13 @@ void prefill_mfma_kernel(const PrefillParams p) {
   const int wave_qmin = base + wave_first_tok;
   const int wave_qmax = base + wave_last_tok;
 
-  float m[NR], lsum[NR];
+  float m[NR], lsum[NR], thr[NR];  // thr: the lazy-rescale threshold on raw scores
   f32x4 o[NR][VE];
+  const float inv_scale_log2 = 1.0f / p.scale_log2;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     m[r] = kMaxInit;
+    thr[r] = (kMaxInit + kLazyRescale) * inv_scale_log2;
     lsum[r] = 0.0f;
 #pragma unroll
     for (int e = 0; e < VE; ++e) o[r][e] = f32x4{0, 0, 0, 0};
@@ -230,34 +232,38 @@ void prefill_mfma_kernel(const PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         float sv[2][4];
-        float mt = -__builtin_inff();
+        bool need = false;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             sv[h][i] = sacc[h][r][i];
             if (DIAG && t0 + 16 * h + 4 * g + i > qpos[r]) sv[h][i] = -__builtin_inff();
+            need |= sv[h][i] > thr[r];
           }
-          mt = fmaxf(mt, fmaxf(fmaxf(sv[h][0], sv[h][1]), fmaxf(sv[h][2], sv[h][3])));
         }
         // The reference max m of a row moves only when one of its scores
         // exceeds it by more than kLazyRescale.  The result is the same for
         // any reference (it cancels in the normalisation); weights stay
         // <= 2^kLazyRescale, far inside the operand formats' range; and on
         // almost every tile neither the row-wide max (two cross-lane steps)
-        // nor the accumulator rescale is needed.
+        // nor the accumulator rescale is needed.  The test compares the raw
+        // scores with thr = (m + kLazyRescale) / scale_log2: compares, unlike
+        // a max, take the matrix cores' results as they are.
         float mn = m[r];
-        float alpha = 1.0f;
-        const bool need = mt * p.scale_log2 > m[r] + kLazyRescale;
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-          mt = fmaxf(mt, __shfl_xor(mt, 16));
-          mt = fmaxf(mt, __shfl_xor(mt, 32));
-          mt *= p.scale_log2;
+          float mt = -__builtin_inff();
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            mt = fmaxf(mt, fmaxf(fmaxf(sv[h][0], sv[h][1]), fmaxf(sv[h][2], sv[h][3])));
+          mt = rows_max(mt) * p.scale_log2;
           if (mt > m[r] + kLazyRescale) mn = mt;  // same decision on the row's 4 lanes
-          alpha = fast_exp2(m[r] - mn);
+          const float alpha = fast_exp2(m[r] - mn);
 #pragma unroll
           for (int e = 0; e < VE; ++e) o[r][e] *= alpha;
+          lsum[r] *= alpha;
           m[r] = mn;
+          thr[r] = (mn + kLazyRescale) * inv_scale_log2;
         }
         float pw[2][4];
 #pragma unroll
@@ -268,7 +274,7 @@ void prefill_mfma_kernel(const PrefillParams p) {
         pb[r] = u32x4{MM::pack(pw[0][0], pw[0][1]), MM::pack(pw[0][2], pw[0][3]),
                       MM::pack(pw[1][0], pw[1][1]), MM::pack(pw[1][2], pw[1][3])};
         // the row sum of the rounded weights, the ones the value product uses
-        float ps = lsum[r] * alpha;
+        float ps = lsum[r];
 #pragma unroll
         for (int w = 0; w < 4; ++w) ps = MM::sum2(pb[r][w], ps);
         lsum[r] = ps;
