@@ -248,8 +248,9 @@ void prefill_mfma_kernel(const PrefillParams p) {
         // <= 2^kLazyRescale, far inside the operand formats' range; and on
         // almost every tile neither the row-wide max (two cross-lane steps)
         // nor the accumulator rescale is needed.  The test compares the raw
-        // scores with thr = (m + kLazyRescale) / scale_log2: compares, unlike
-        // a max, take the matrix cores' results as they are.
+        // scores with thr = (m + kLazyRescale) / scale_log2 (scale_log2 > 0:
+        // the library rejects other scales): compares, unlike a max, take the
+        // matrix cores' results as they are.
         float mn = m[r];
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
           float mt = -__builtin_inff();
