@@ -236,7 +236,23 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     int nlow;          // rows below this one are before the window
   };
 
-  auto fetch = [&](const int t, auto partial_tag) {
+  // The cache block of tile t (wave-uniform), from the 64 ids held one per
+  // lane; reading an id waits for every load before it, so a loop step reads
+  // all its tiles' ids before loading any of their rows.
+  auto block_of = [&](const int t) {
+    const int rel = (tok0 + t * TT) / BS - blk0;
+    if (rel >= ids_base + kWave) {
+      ids_base = rel & ~(kWave - 1);
+      const int bi = ids_base + lane;
+      ids = bi < nblk ? table[blk0 + bi] : 0;
+    }
+    const int phys = __builtin_amdgcn_readlane(ids, rel - ids_base);
+    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    bad_block |= !ok;
+    return ok ? phys : 0;
+  };
+
+  auto fetch = [&](const int t, const int phys, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     Raw raw;
     const int ttok = tok0 + t * TT;
@@ -244,16 +260,6 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
     const int nlow = start - ttok;
     raw.nvalid = nvalid;
     raw.nlow = nlow;
-    const int rel = ttok / BS - blk0;
-    if (rel >= ids_base + kWave) {
-      ids_base = rel & ~(kWave - 1);
-      const int bi = ids_base + lane;
-      ids = bi < nblk ? table[blk0 + bi] : 0;
-    }
-    int phys = __builtin_amdgcn_readlane(ids, rel - ids_base);
-    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
-    bad_block |= !ok;
-    phys = ok ? phys : 0;
     const size_t row0 = ((size_t)phys * p.num_kv_heads + kvh) * BS + ttok % BS;
     const char* const kt = kbase + row0 * ROWB;  // the tile's rows (wave-uniform)
     const char* const vt = vbase + row0 * ROWB;
@@ -371,15 +377,17 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   const int nfull = (tok_end - tok0) / TT;
   int t = t_first + wave;
   if (low_cut && wave == 0) {
-    const Raw a = fetch(t, std::true_type{});
+    const Raw a = fetch(t, block_of(t), std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
     consume(a, std::true_type{});
     t += NW;
   }
   if constexpr (TPI == 2) {
     for (; t + NW < nfull; t += 2 * NW) {
-      const Raw a = fetch(t, std::false_type{});
-      const Raw b = fetch(t + NW, std::false_type{});
+      const int ba = block_of(t);
+      const int bb = block_of(t + NW);
+      const Raw a = fetch(t, ba, std::false_type{});
+      const Raw b = fetch(t + NW, bb, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       consume(a, std::false_type{});
       consume(b, std::false_type{});
@@ -387,11 +395,11 @@ void decode_mfma_i4_kernel(const DecodeParams p) {
   }
   for (; t < ntiles; t += NW) {
     if (t < nfull) {
-      const Raw a = fetch(t, std::false_type{});
+      const Raw a = fetch(t, block_of(t), std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       consume(a, std::false_type{});
     } else {
-      const Raw a = fetch(t, std::true_type{});
+      const Raw a = fetch(t, block_of(t), std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
       consume(a, std::true_type{});
     }
@@ -589,7 +597,23 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     int nlow;          // rows below this one are before the window
   };
 
-  auto fetch = [&](const int t, auto partial_tag) {
+  // The cache block of tile t (wave-uniform), from the 64 ids held one per
+  // lane; reading an id waits for every load before it, so a loop step reads
+  // all its tiles' ids before loading any of their rows.
+  auto block_of = [&](const int t) {
+    const int rel = (tok0 + t * TT) / BS - blk0;
+    if (rel >= ids_base + kWave) {
+      ids_base = rel & ~(kWave - 1);
+      const int bi = ids_base + lane;
+      ids = bi < nblk ? table[blk0 + bi] : 0;
+    }
+    const int phys = __builtin_amdgcn_readlane(ids, rel - ids_base);
+    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    bad_block |= !ok;
+    return ok ? phys : 0;
+  };
+
+  auto fetch = [&](const int t, const int phys, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     Raw raw;
     const int ttok = tok0 + t * TT;
@@ -597,16 +621,6 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
     const int nlow = start - ttok;
     raw.nvalid = nvalid;
     raw.nlow = nlow;
-    const int rel = ttok / BS - blk0;
-    if (rel >= ids_base + kWave) {
-      ids_base = rel & ~(kWave - 1);
-      const int bi = ids_base + lane;
-      ids = bi < nblk ? table[blk0 + bi] : 0;
-    }
-    int phys = __builtin_amdgcn_readlane(ids, rel - ids_base);
-    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
-    bad_block |= !ok;
-    phys = ok ? phys : 0;
     const size_t row0 = ((size_t)phys * p.num_kv_heads + kvh) * BS + ttok % BS;
     const char* const kt = kbase + row0 * ROWB;  // the tile's rows (wave-uniform)
     const char* const vt = vbase + row0 * ROWB;
@@ -720,26 +734,29 @@ void decode_mfma_i4h_kernel(const DecodeParams p) {
   const int nfull = (tok_end - tok0) / TT;
   int t = t_first + wave;
   if (low_cut && wave == 0) {
-    const Raw a = fetch(t, std::true_type{});
+    const Raw a = fetch(t, block_of(t), std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
     consume(a, std::true_type{});
     t += NW;
   }
   for (; t + (TPI - 1) * NW < nfull; t += TPI * NW) {
+    int bl[TPI];
+#pragma unroll
+    for (int i = 0; i < TPI; ++i) bl[i] = block_of(t + i * NW);
     Raw r[TPI];
 #pragma unroll
-    for (int i = 0; i < TPI; ++i) r[i] = fetch(t + i * NW, std::false_type{});
+    for (int i = 0; i < TPI; ++i) r[i] = fetch(t + i * NW, bl[i], std::false_type{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < TPI; ++i) consume(r[i], std::false_type{});
   }
   for (; t < ntiles; t += NW) {
     if (t < nfull) {
-      const Raw a = fetch(t, std::false_type{});
+      const Raw a = fetch(t, block_of(t), std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       consume(a, std::false_type{});
     } else {
-      const Raw a = fetch(t, std::true_type{});
+      const Raw a = fetch(t, block_of(t), std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
       consume(a, std::true_type{});
     }
