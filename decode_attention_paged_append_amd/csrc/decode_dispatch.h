@@ -6,12 +6,27 @@
 
 namespace pa {
 
+// LDS reserved (unused) at launch to hold a CU to fewer resident workgroups.
+// The plan gives the int8 vector-ALU kernel at one head per workgroup and
+// head_dim 128 one round of workgroups, four per CU, but its registers (93
+// VGPRs) let five reside, and launches came out either at 87.5 or at 90.5
+// us on Llama-2-7B int8 (16 x 4096), as if the dispatcher at times put five
+// on some CUs and three on others.  Reserving LDS so that only four fit, the
+// launch took 87.4-87.6 us in three alternations on MI355X (uncapped: 87.5
+// once, 90.5-90.6 twice).  The 16-bit instances were level under the same
+// cap and keep their occupancy.
+template <Fmt F, int D, int GC>
+constexpr unsigned occupancy_lds() {
+  return F == Fmt::I8 && GC == 1 && D == 128 ? 32768u : 0u;
+}
+
 template <Fmt F, int D, int BS, int GC>
 static hipError_t launch_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_parts, (unsigned)(p.num_kv_heads * p.head_chunks),
                   (unsigned)num_seqs);
+  constexpr unsigned lds = occupancy_lds<F, D, GC>();
   hipLaunchKernelGGL((decode_partition_kernel<F, D, BS, GC, kDecodeWaves>), grid,
-                     dim3(kDecodeWaves * kWave), 0, stream, p);
+                     dim3(kDecodeWaves * kWave), lds, stream, p);
   return hipGetLastError();
 }
 
